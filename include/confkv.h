@@ -1,0 +1,199 @@
+/*
+ * confkv.h — C ABI of the MI355X (gfx950) decode-step library for
+ * confidence-gated KV-cache eviction (CONF-KV) and its KVpop fixed-budget
+ * variant.
+ *
+ * One call, confkv_step, runs one decode step for every layer and batch row:
+ *   1. a vocab-wide reduction of the logits gives the confidence
+ *        c = w_e (1 - H / log V) + w_m sigmoid(z(1) - z(2)) + w_p p_max
+ *      and c against tau picks the step's base budget per batch row
+ *      ("Conf-KV" post on rcap.io, method paragraph and decoding-loop
+ *      pseudocode; CONF-KV abstract on chatpaper.ai);
+ *   2. decode attention of each query head over its KV head's retained rows,
+ *      the recent window in FP16 and older rows INT8, dequantized in the
+ *      kernel (CONF-KV abstract: blockwise softmax attention with mixed
+ *      FP16/INT8 storage; Conf-KV post: the fused INT8 dequantization);
+ *   3. the EMA of each row's attention mass and the score
+ *        alpha * ema + (1 - alpha) * recency            (Conf-KV post);
+ *   4. per KV head, eviction of the lowest-scoring rows down to the budget,
+ *      sink and protected-window rows exempt          (Conf-KV post);
+ *   5. in-place compaction of the survivors and INT8 storage of the row that
+ *      leaves the FP16 window                          (Conf-KV post).
+ * With policy KVPOP, steps 1 and 3 are replaced by the fixed budget
+ * B = s + w + k over static per-token priorities ("Resumen Técnico: KVpop",
+ * gist.science, §2.1 and §2.4), the priority of a row arriving when it leaves
+ * the protected window (§2.3, delayed scoring).
+ *
+ * Conventions
+ * -----------
+ * - Every tensor pointer is a caller-owned DEVICE pointer, row-major, with the
+ *   shape in brackets. fp16 values are passed as their uint16_t bit patterns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *   only enqueue work on it, except where a function says it synchronizes.
+ * - Segment index: seg = (l * batch + b) * num_kv_heads + h. Query heads
+ *   h*G .. h*G+G-1 (G = num_q_heads / num_kv_heads) share KV head h.
+ * - Ownership: the caller allocates the device state buffer (size from
+ *   confkv_state_bytes) and all inputs/outputs, and keeps inputs alive until
+ *   the stream has passed the call. The library allocates only a host-side
+ *   handle (and HIP events while profiling is on); it never allocates device
+ *   memory.
+ * - Errors: argument and shape checks run on the host before anything is
+ *   enqueued and return CONFKV_EINVAL / CONFKV_ECAPACITY with the state
+ *   unchanged. Faults found by the kernels (non-finite logits or scores, a
+ *   segment outgrowing its capacity) set a sticky device error word that
+ *   confkv_status (and every synchronizing call) reports. After any error
+ *   the handle accepts only confkv_status, confkv_destroy, confkv_strerror.
+ *   Nothing throws across this ABI. A handle is not thread-safe.
+ */
+#ifndef CONFKV_H
+#define CONFKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONFKV_ABI_VERSION 1
+
+enum {
+  CONFKV_OK = 0,
+  CONFKV_EINVAL = -1,      /* bad argument, shape or config value            */
+  CONFKV_ECAPACITY = -2,   /* capacity or state buffer too small             */
+  CONFKV_EHIP = -3,        /* a HIP runtime call failed                      */
+  CONFKV_ENONFINITE = -4,  /* NaN/Inf in logits or in a ranking score        */
+  CONFKV_ESTATE = -5       /* handle destroyed or poisoned by an earlier error */
+};
+
+enum { CONFKV_POLICY_CONF = 0, CONFKV_POLICY_KVPOP = 1 };
+
+typedef struct confkv_handle confkv_handle;
+
+typedef struct confkv_config {
+  int32_t abi_version;     /* CONFKV_ABI_VERSION                                   */
+  int32_t num_layers;      /* L >= 1                                               */
+  int32_t batch;           /* B >= 1                                               */
+  int32_t num_q_heads;     /* Hq, a multiple of num_kv_heads; G in {1,2,4,5,8}     */
+  int32_t num_kv_heads;    /* Hkv >= 1                                             */
+  int32_t head_dim;        /* d in {64, 128}                                       */
+  int32_t vocab;           /* V >= 2 (CONF); ignored for KVPOP                     */
+  int32_t capacity;        /* rows older than the FP16 window that one segment can
+                              hold; >= max(prefill_len, largest budget + 1,
+                              num_sink + protect_last + 1)                        */
+  int32_t policy;          /* CONFKV_POLICY_CONF | CONFKV_POLICY_KVPOP             */
+  int32_t n_low, n_high;   /* the two base budgets (rows per segment)              */
+  int32_t protect_last;    /* P: the last P positions are never evicted (KVPOP: w) */
+  int32_t fp16_window;     /* W: rows with pos > t - W stay FP16 (KVPOP: = w)      */
+  int32_t num_sink;        /* s: positions < s are never evicted                   */
+  float tau;               /* confidence threshold                                 */
+  float alpha;             /* score = alpha * ema + (1 - alpha) * recency          */
+  float ema_beta;          /* ema <- beta * ema + (1 - beta) * mass                */
+  float w_entropy, w_margin, w_pmax;  /* 0.4, 0.3, 0.3                             */
+  int32_t gate_literal;    /* 0: c >= tau -> min(n_low, n_high) (the pages' prose);
+                              1: c >= tau -> n_high (the pseudocode as printed)   */
+  int32_t pyramid;         /* 1: layer l gets floor(base*(3(L-1)-2l)/(2(L-1)))     */
+  int32_t kvpop_k;         /* k of B = s + w + k (KVPOP)                           */
+  int32_t old_int8;        /* 1: rows leaving the FP16 window are stored INT8
+                              (per-token, per-head fp32 absmax scale, K and V
+                              separately); 0: they stay FP16                      */
+  float softmax_scale;     /* 0 -> 1/sqrt(d)                                       */
+  int32_t record_scores;   /* 1: keep the last step's per-row positions, ranking
+                              values and LSEs for confkv_read_last_step            */
+} confkv_config;
+
+/* Host-only check of a configuration with a given prefill length. Returns
+ * CONFKV_OK, CONFKV_EINVAL or CONFKV_ECAPACITY. Touches no GPU. */
+int confkv_validate(const confkv_config* cfg, int32_t prefill_len);
+
+/* Bytes of device state the configuration needs, or 0 if it is invalid.
+ * Host-only; touches no GPU. */
+size_t confkv_state_bytes(const confkv_config* cfg);
+
+/* Rows per segment in the buffers of confkv_read_cache/confkv_read_last_step:
+ * capacity + fp16 window slots. Host-only. 0 if cfg is invalid. */
+int32_t confkv_rows_max(const confkv_config* cfg);
+
+/* Carve `state` (>= confkv_state_bytes, 256-byte aligned) and ingest an
+ * optional prefill: prefill_k / prefill_v [L][B][Hkv][prefill_len][d] fp16 (both
+ * NULL iff prefill_len == 0; KVPOP takes no prefill). Prefill rows get
+ * positions 0..prefill_len-1 and EMA 0; those with pos <= prefill_len-1-W are
+ * stored INT8 (if old_int8); nothing is attended or evicted here. The next
+ * confkv_step decodes position prefill_len. Enqueues on `stream`; on success
+ * *out receives a new handle. */
+int confkv_init(const confkv_config* cfg, void* state, size_t state_bytes, void* stream,
+                const uint16_t* prefill_k, const uint16_t* prefill_v, int32_t prefill_len,
+                confkv_handle** out);
+
+/* One decode step at position t (prefill_len + number of earlier steps):
+ *   logits    [B][V]        fp32   CONF: required; KVPOP: must be NULL
+ *   q         [L][B][Hq][d] fp16   this step's queries
+ *   k_new     [L][B][Hkv][d] fp16  this step's key row (appended, pos = t)
+ *   v_new     [L][B][Hkv][d] fp16  this step's value row
+ *   prio_new  [L][B][Hkv]   fp32   KVPOP: priority of the row at position t-w,
+ *                                  which leaves the protected window now
+ *                                  (ignored where t-w < s); CONF: NULL
+ *   out       [L][B][Hq][d] fp16   attention output (written)
+ *   conf_out  [B] fp32, budget_out [B] int32: optional (NULL) copies of the
+ *             confidence and the base budget of each batch row (CONF only;
+ *             the per-layer budget applies the pyramid to the base).
+ * Only enqueues work; no host synchronization. */
+int confkv_step(confkv_handle* h, void* stream, const float* logits, const uint16_t* q,
+                const uint16_t* k_new, const uint16_t* v_new, const float* prio_new, uint16_t* out,
+                float* conf_out, int32_t* budget_out);
+
+/* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
+ * ascending position order. Per segment i, rows 0..len[i]-1 of each
+ * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max
+ * = confkv_rows_max); later rows are left untouched. Any output except len may
+ * be NULL. FP16 rows appear in k16/v16 and have zero k8/v8/scales; INT8 rows
+ * appear in k8/v8 + k_scale/v_scale and have zero k16/v16. ema is 0 for KVPOP
+ * and prio is 0 for CONF (and for rows still inside the window). Synchronizes
+ * `stream` and returns the sticky error status. */
+int confkv_read_cache(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count, int32_t* len,
+                      int32_t* pos, float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8,
+                      int8_t* v8, float* k_scale, float* v_scale, uint8_t* is_int8);
+
+/* Requires record_scores. For segments [seg_first, seg_first+seg_count) copy
+ * what the last step saw before evicting:
+ *   meta  [count][4] int32: staged rows, live rows, per-layer budget, evicted
+ *   pos   [count][rows_max] int32: position of each staged row (-1: empty slot)
+ *   score [count][rows_max] fp32: the ranking value (CONF: alpha*ema+(1-alpha)*rec
+ *         as stored in fp32; KVPOP: the priority) of each staged row
+ *   lse   [count][G] fp32: log-sum-exp of each query head's scores
+ * Any pointer may be NULL. Synchronizes `stream`. */
+int confkv_read_last_step(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count,
+                          int32_t* meta, int32_t* pos, float* score, float* lse);
+
+/* Totals over all segments since init (or the last reset), written to the
+ * HOST array totals[4]: KV bytes read by attention (K+V rows and INT8 scales),
+ * rows attended, rows moved by compaction or age-out, rows evicted.
+ * Synchronizes `stream`. */
+int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, int32_t reset);
+
+/* Profiling of the step's kernels with HIP events on the step's stream.
+ * confkv_profile(h, 1) starts recording an event pair around each launch of
+ * the fused attend+evict kernel and of the logits reducer;
+ * confkv_profile_read synchronizes and writes HOST values: total milliseconds
+ * and launch counts of each, then (if reset) clears them. */
+int confkv_profile(confkv_handle* h, int32_t enable);
+int confkv_profile_read(confkv_handle* h, double* fused_ms, int64_t* fused_launches, double* reduce_ms,
+                        int64_t* reduce_launches, int32_t reset);
+
+/* Position the next confkv_step decodes. -1 for a NULL handle. */
+int64_t confkv_position(const confkv_handle* h);
+
+/* Synchronize the last stream used and return the sticky device error word
+ * as a status code (CONFKV_OK if none). */
+int confkv_status(confkv_handle* h);
+
+/* Free the handle (not the state buffer). Safe on NULL. */
+int confkv_destroy(confkv_handle* h);
+
+/* Static string for a status code. */
+const char* confkv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONFKV_H */

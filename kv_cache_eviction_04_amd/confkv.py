@@ -1,0 +1,230 @@
+"""ctypes binding of libconfkv.so (the C ABI in include/confkv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their data pointers and torch's current HIP stream are handed
+to the library. Every stage of the decode step runs in the library's HIP
+kernels; there is no fallback. Loading fails loudly if the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconfkv.so")
+
+OK, EINVAL, ECAPACITY, EHIP, ENONFINITE, ESTATE = 0, -1, -2, -3, -4, -5
+POLICY_CONF, POLICY_KVPOP = 0, 1
+ABI_VERSION = 1
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", c_int32), ("num_layers", c_int32), ("batch", c_int32), ("num_q_heads", c_int32),
+        ("num_kv_heads", c_int32), ("head_dim", c_int32), ("vocab", c_int32), ("capacity", c_int32),
+        ("policy", c_int32), ("n_low", c_int32), ("n_high", c_int32), ("protect_last", c_int32),
+        ("fp16_window", c_int32), ("num_sink", c_int32), ("tau", c_float), ("alpha", c_float),
+        ("ema_beta", c_float), ("w_entropy", c_float), ("w_margin", c_float), ("w_pmax", c_float),
+        ("gate_literal", c_int32), ("pyramid", c_int32), ("kvpop_k", c_int32), ("old_int8", c_int32),
+        ("softmax_scale", c_float), ("record_scores", c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libconfkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_eviction_04_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    sig = {
+        "confkv_validate": (c_int, [POINTER(Config), c_int32]),
+        "confkv_state_bytes": (c_size_t, [POINTER(Config)]),
+        "confkv_rows_max": (c_int32, [POINTER(Config)]),
+        "confkv_init": (c_int, [POINTER(Config), P, c_size_t, P, P, P, c_int32, POINTER(P)]),
+        "confkv_step": (c_int, [P, P, P, P, P, P, P, P, P, P]),
+        "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
+        "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
+        "confkv_stats": (c_int, [P, P, POINTER(c_uint64), c_int32]),
+        "confkv_profile": (c_int, [P, c_int32]),
+        "confkv_profile_read": (c_int, [P, POINTER(c_double), POINTER(c_int64), POINTER(c_double),
+                                        POINTER(c_int64), c_int32]),
+        "confkv_position": (c_int64, [P]),
+        "confkv_status": (c_int, [P]),
+        "confkv_destroy": (c_int, [P]),
+        "confkv_strerror": (ctypes.c_char_p, [c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
+            "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
+            "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
+
+
+class ConfKVError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {lib().confkv_strerror(code).decode()} ({code})")
+
+
+def _check(code: int, what: str):
+    if code != OK:
+        raise ConfKVError(code, what)
+
+
+def make_config(w: dict, capacity: int | None = None, record: bool = False) -> Config:
+    """C config from a workload dict (the keys of ``synth.WORKLOADS``)."""
+    from .synth import capacity as default_capacity
+    c = Config()
+    c.abi_version = ABI_VERSION
+    for name in ("num_layers", "batch", "num_q_heads", "num_kv_heads", "head_dim", "n_low", "n_high",
+                 "protect_last", "fp16_window", "num_sink", "kvpop_k"):
+        setattr(c, name, int(w.get(name, 0)))
+    c.vocab = int(w.get("vocab") or 0)
+    c.policy = POLICY_KVPOP if w.get("policy") == "kvpop" else POLICY_CONF
+    for name in ("tau", "alpha", "ema_beta", "w_entropy", "w_margin", "w_pmax", "softmax_scale"):
+        setattr(c, name, float(w.get(name, 0.0)))
+    c.gate_literal = int(bool(w.get("gate_literal", False)))
+    c.pyramid = int(bool(w.get("pyramid", False)))
+    c.old_int8 = int(bool(w.get("old_int8", True)))
+    c.capacity = int(capacity if capacity is not None else default_capacity(w))
+    c.record_scores = int(bool(record))
+    return c
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _expect(t, shape, dtype, device, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+class Cache:
+    """One model's KV cache under the eviction policy, resident on one GPU."""
+
+    def __init__(self, w: dict, prefill_k=None, prefill_v=None, capacity=None, record=False, device=None):
+        self.w = dict(w)
+        dev = torch.device(device if device is not None else "cuda")
+        self.device = torch.device(dev.type, 0) if dev.index is None else dev
+        self.cfg = make_config(w, capacity, record)
+        L = lib()
+        P0 = 0 if prefill_k is None else int(prefill_k.shape[3])
+        _check(L.confkv_validate(ctypes.byref(self.cfg), P0), "config")
+        self.state_bytes = L.confkv_state_bytes(ctypes.byref(self.cfg))
+        self.rows_max = L.confkv_rows_max(ctypes.byref(self.cfg))
+        c = self.cfg
+        self.G = c.num_q_heads // c.num_kv_heads
+        self.S = c.num_layers * c.batch * c.num_kv_heads
+        if P0:
+            shp = (c.num_layers, c.batch, c.num_kv_heads, P0, c.head_dim)
+            _expect(prefill_k, shp, torch.float16, self.device, "prefill_k")
+            _expect(prefill_v, shp, torch.float16, self.device, "prefill_v")
+        self.state = torch.empty(self.state_bytes, dtype=torch.uint8, device=self.device)
+        h = c_void_p()
+        _check(L.confkv_init(ctypes.byref(self.cfg), _ptr(self.state), self.state_bytes, self._stream(),
+                             _ptr(prefill_k), _ptr(prefill_v), P0, ctypes.byref(h)), "confkv_init")
+        self.h = h
+
+    def _stream(self):
+        return c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    @property
+    def position(self) -> int:
+        return int(lib().confkv_position(self.h))
+
+    def step(self, logits, q, k, v, prio=None, out=None, conf_out=None, budget_out=None):
+        c, dev = self.cfg, self.device
+        L, B, Hq, H, d = c.num_layers, c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        if c.policy == POLICY_CONF:
+            _expect(logits, (B, c.vocab), torch.float32, dev, "logits")
+        elif logits is not None:
+            raise ValueError("KVpop takes no logits")
+        _expect(q, (L, B, Hq, d), torch.float16, dev, "q")
+        _expect(k, (L, B, H, d), torch.float16, dev, "k")
+        _expect(v, (L, B, H, d), torch.float16, dev, "v")
+        if c.policy == POLICY_KVPOP:
+            _expect(prio, (L, B, H), torch.float32, dev, "prio")
+        if out is None:
+            out = torch.empty((L, B, Hq, d), dtype=torch.float16, device=dev)
+        _expect(out, (L, B, Hq, d), torch.float16, dev, "out")
+        if conf_out is not None:
+            _expect(conf_out, (B,), torch.float32, dev, "conf_out")
+        if budget_out is not None:
+            _expect(budget_out, (B,), torch.int32, dev, "budget_out")
+        _check(lib().confkv_step(self.h, self._stream(), _ptr(logits), _ptr(q), _ptr(k), _ptr(v), _ptr(prio),
+                                 _ptr(out), _ptr(conf_out), _ptr(budget_out)), "confkv_step")
+        return out
+
+    def read_cache(self, seg_first=0, seg_count=None):
+        """Logical contents (ascending position) of a segment range, as torch
+        tensors on the device; rows >= len[i] are zero."""
+        n = self.S - seg_first if seg_count is None else seg_count
+        R, d, dev = self.rows_max, self.cfg.head_dim, self.device
+        z = lambda *s, dt: torch.zeros(s, dtype=dt, device=dev)  # noqa: E731
+        o = dict(len=z(n, dt=torch.int32), pos=z(n, R, dt=torch.int32), ema=z(n, R, dt=torch.float32),
+                 prio=z(n, R, dt=torch.float32), k16=z(n, R, d, dt=torch.float16), v16=z(n, R, d, dt=torch.float16),
+                 k8=z(n, R, d, dt=torch.int8), v8=z(n, R, d, dt=torch.int8), k_scale=z(n, R, dt=torch.float32),
+                 v_scale=z(n, R, dt=torch.float32), is_int8=z(n, R, dt=torch.uint8))
+        _check(lib().confkv_read_cache(self.h, self._stream(), seg_first, n, *[_ptr(o[k]) for k in (
+            "len", "pos", "ema", "prio", "k16", "v16", "k8", "v8", "k_scale", "v_scale", "is_int8")]),
+            "confkv_read_cache")
+        return o
+
+    def read_last_step(self, seg_first=0, seg_count=None):
+        n = self.S - seg_first if seg_count is None else seg_count
+        R, dev = self.rows_max, self.device
+        o = dict(meta=torch.zeros((n, 4), dtype=torch.int32, device=dev),
+                 pos=torch.full((n, R), -1, dtype=torch.int32, device=dev),
+                 score=torch.zeros((n, R), dtype=torch.float32, device=dev),
+                 lse=torch.zeros((n, self.G), dtype=torch.float32, device=dev))
+        _check(lib().confkv_read_last_step(self.h, self._stream(), seg_first, n, _ptr(o["meta"]), _ptr(o["pos"]),
+                                           _ptr(o["score"]), _ptr(o["lse"])), "confkv_read_last_step")
+        return o
+
+    def stats(self, reset=False):
+        arr = (c_uint64 * 4)()
+        _check(lib().confkv_stats(self.h, self._stream(), arr, int(reset)), "confkv_stats")
+        return dict(kv_bytes=int(arr[0]), rows_attended=int(arr[1]), rows_moved=int(arr[2]), rows_evicted=int(arr[3]))
+
+    def profile(self, enable=True):
+        _check(lib().confkv_profile(self.h, int(enable)), "confkv_profile")
+
+    def profile_read(self, reset=True):
+        fm, rm = c_double(), c_double()
+        fn, rn = c_int64(), c_int64()
+        _check(lib().confkv_profile_read(self.h, ctypes.byref(fm), ctypes.byref(fn), ctypes.byref(rm),
+                                         ctypes.byref(rn), int(reset)), "confkv_profile_read")
+        return dict(fused_ms=fm.value, fused_launches=fn.value, reduce_ms=rm.value, reduce_launches=rn.value)
+
+    def status(self) -> int:
+        return int(lib().confkv_status(self.h))
+
+    def close(self):
+        if getattr(self, "h", None) is not None:
+            lib().confkv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,451 @@
+// Host side of the C ABI declared in include/confkv.h: configuration checks,
+// carving of the caller's state buffer, and the per-step launch sequence.
+// Nothing here computes a step; every stage runs in kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "confkv.h"
+#include "layout.h"
+
+#define CONFKV_API extern "C" __attribute__((visibility("default")))
+
+using namespace confkv;
+
+namespace {
+
+constexpr uint32_t kMagic = 0xC0F4B1E5u;
+constexpr uint32_t kDead = 0xDEADDEADu;
+constexpr int kMaxProfilePairs = 1 << 15;
+
+struct EventPool {
+  std::vector<hipEvent_t> ev;  // pairs: start, stop
+  size_t used = 0;             // pairs recorded since the last read
+  double ms = 0.0;
+  int64_t n = 0;
+};
+
+}  // namespace
+
+struct confkv_handle {
+  uint32_t magic;
+  confkv_config cfg;
+  Layout lay;
+  Params par;
+  void* state;
+  size_t state_bytes;
+  int64_t t;           // position decoded by the next step
+  int64_t rows_bound;  // upper bound on rows any segment retains before the next step
+  int64_t keep_max;    // no segment keeps more rows than this after an eviction
+  int poisoned;
+  hipStream_t last_stream;
+  int prof;
+  EventPool pf, pr;    // fused kernel, logits reducer
+};
+
+namespace {
+
+int group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 5 || g == 8; }
+
+int64_t window_of(const confkv_config* c) {
+  return c->policy == CONFKV_POLICY_KVPOP ? c->protect_last : c->fp16_window;
+}
+
+// Largest per-layer budget the configuration can produce.
+int64_t budget_max(const confkv_config* c) {
+  if (c->policy == CONFKV_POLICY_KVPOP) return (int64_t)c->num_sink + c->protect_last + c->kvpop_k;
+  const int64_t top = std::max(c->n_low, c->n_high);
+  return (c->pyramid && c->num_layers > 1) ? (3 * top) / 2 : top;
+}
+
+int64_t keep_bound(const confkv_config* c) {
+  return std::max<int64_t>(budget_max(c), (int64_t)c->num_sink + c->protect_last);
+}
+
+bool finite_all(std::initializer_list<float> v) {
+  for (float x : v)
+    if (!isfinite(x)) return false;
+  return true;
+}
+
+int check_cfg(const confkv_config* c, int32_t P0) {
+  if (!c) return CONFKV_EINVAL;
+  if (c->abi_version != CONFKV_ABI_VERSION) return CONFKV_EINVAL;
+  if (c->num_layers < 1 || c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1) return CONFKV_EINVAL;
+  if (c->num_q_heads % c->num_kv_heads) return CONFKV_EINVAL;
+  if (!group_ok(c->num_q_heads / c->num_kv_heads)) return CONFKV_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return CONFKV_EINVAL;
+  if (c->policy != CONFKV_POLICY_CONF && c->policy != CONFKV_POLICY_KVPOP) return CONFKV_EINVAL;
+  if (c->protect_last < 0 || c->fp16_window < 0 || c->num_sink < 0 || P0 < 0) return CONFKV_EINVAL;
+  if (c->old_int8 != 0 && c->old_int8 != 1) return CONFKV_EINVAL;
+  if (!finite_all({c->softmax_scale}) || c->softmax_scale < 0.0f) return CONFKV_EINVAL;
+  if (c->policy == CONFKV_POLICY_CONF) {
+    if (c->vocab < 2 || c->n_low < 0 || c->n_high < 0) return CONFKV_EINVAL;
+    if (!finite_all({c->tau, c->alpha, c->ema_beta, c->w_entropy, c->w_margin, c->w_pmax})) return CONFKV_EINVAL;
+  } else {
+    if (c->kvpop_k < 0 || P0 != 0) return CONFKV_EINVAL;
+  }
+  const int64_t W = window_of(c);
+  if (W > (1 << 16)) return CONFKV_EINVAL;
+  if (c->capacity < 1) return CONFKV_ECAPACITY;
+  const int64_t need = std::max<int64_t>({(int64_t)P0, keep_bound(c) + 1, 1});
+  if ((int64_t)c->capacity < need) return CONFKV_ECAPACITY;
+  // index arithmetic of the kernels stays in range
+  const int64_t S = (int64_t)c->num_layers * c->batch * c->num_kv_heads;
+  if (S > (1 << 30) || (int64_t)c->capacity > (1 << 30)) return CONFKV_EINVAL;
+  if (S * ((int64_t)c->capacity + W + 1) * c->head_dim * 2 > (int64_t)1 << 50) return CONFKV_ECAPACITY;
+  return CONFKV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Carve the state; with base == nullptr only the size is computed.
+size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
+  Layout lay;
+  memset(&lay, 0, sizeof(lay));
+  lay.L = c->num_layers;
+  lay.B = c->batch;
+  lay.Hq = c->num_q_heads;
+  lay.Hkv = c->num_kv_heads;
+  lay.G = c->num_q_heads / c->num_kv_heads;
+  lay.D = c->head_dim;
+  lay.V = c->policy == CONFKV_POLICY_CONF ? c->vocab : 0;
+  lay.S = c->num_layers * c->batch * c->num_kv_heads;
+  lay.cap = c->capacity;
+  lay.W = (int32_t)window_of(c);
+  lay.Wr = lay.W + 1;
+  lay.rows_max = lay.cap + lay.Wr;
+  lay.planes = std::max(lay.G, 4);
+  lay.chunks = lay.V > 0 ? (lay.V + kChunk - 1) / kChunk : 0;
+  lay.old_bytes = c->old_int8 ? 1 : 2;
+  const size_t S = (size_t)lay.S, D = (size_t)lay.D, Wr = (size_t)lay.Wr, cap = (size_t)lay.cap;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    const size_t o = align256(off);
+    off = o + std::max<size_t>(bytes, 1);
+    return base ? base + o : nullptr;
+  };
+  lay.ring_k = (uint16_t*)take(S * Wr * D * 2);
+  lay.ring_v = (uint16_t*)take(S * Wr * D * 2);
+  lay.ring_pos = (int32_t*)take(S * Wr * 4);
+  lay.ring_ema = (float*)take(S * Wr * 4);
+  lay.ring_prio = (float*)take(S * Wr * 4);
+  lay.old_k = take(S * cap * D * lay.old_bytes);
+  lay.old_v = take(S * cap * D * lay.old_bytes);
+  lay.old_ks = (float*)take(S * cap * 4);
+  lay.old_vs = (float*)take(S * cap * 4);
+  lay.old_pos = (int32_t*)take(S * cap * 4);
+  lay.old_ema = (float*)take(S * cap * 4);
+  lay.old_prio = (float*)take(S * cap * 4);
+  lay.seg_nold = (int32_t*)take(S * 4);
+  lay.seg_stats = (uint64_t*)take(S * kStatFields * 8);
+  const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();
+  lay.stage = hbm_stage ? (float*)take(S * lay.planes * (size_t)lay.rows_max * 4) : nullptr;
+  lay.partials = (ConfPartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(ConfPartial));
+  lay.row_counter = (uint32_t*)take((size_t)lay.B * 4);
+  lay.row_conf = (float*)take((size_t)lay.B * 4);
+  lay.row_base = (int32_t*)take((size_t)lay.B * 4);
+  lay.err = (uint32_t*)take(4);
+  lay.stats_total = (uint64_t*)take(kStatFields * 8);
+  if (c->record_scores) {
+    lay.rec_meta = (int32_t*)take(S * 16);
+    lay.rec_pos = (int32_t*)take(S * lay.rows_max * 4);
+    lay.rec_score = (float*)take(S * lay.rows_max * 4);
+    lay.rec_lse = (float*)take(S * lay.G * 4);
+  }
+  if (L) *L = lay;
+  return align256(off);
+}
+
+Params make_params(const confkv_config* c) {
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.tau = c->tau;
+  p.alpha = c->alpha;
+  p.beta = c->ema_beta;
+  p.w_e = c->w_entropy;
+  p.w_m = c->w_margin;
+  p.w_p = c->w_pmax;
+  p.sm_scale = c->softmax_scale > 0.0f ? c->softmax_scale : (float)(1.0 / sqrt((double)c->head_dim));
+  p.n_low = c->n_low;
+  p.n_high = c->n_high;
+  p.P = c->protect_last;
+  p.s = c->num_sink;
+  p.kvpop_k = c->kvpop_k;
+  p.policy = c->policy;
+  p.gate_literal = c->gate_literal ? 1 : 0;
+  p.pyramid = c->pyramid ? 1 : 0;
+  p.old_int8 = c->old_int8;
+  p.record = c->record_scores ? 1 : 0;
+  return p;
+}
+
+// Handles handed out and not yet destroyed; a destroyed or foreign pointer is
+// never dereferenced.
+std::mutex g_mu;
+std::unordered_set<const confkv_handle*> g_live;
+
+bool live(const confkv_handle* h) {
+  if (!h) return false;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_live.count(h) != 0;
+}
+
+int record_event(confkv_handle* h, EventPool& pool, hipStream_t s, bool start) {
+  if (!h->prof) return 0;
+  const size_t idx = 2 * pool.used + (start ? 0 : 1);
+  if (pool.used >= (size_t)kMaxProfilePairs) return 0;
+  while (pool.ev.size() <= idx) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    pool.ev.push_back(e);
+  }
+  if (hipEventRecord(pool.ev[idx], s) != hipSuccess) return -1;
+  if (!start) ++pool.used;
+  return 0;
+}
+
+int collect(EventPool& pool) {
+  for (size_t i = 0; i < pool.used; ++i) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(pool.ev[2 * i + 1]) != hipSuccess) return -1;
+    if (hipEventElapsedTime(&ms, pool.ev[2 * i], pool.ev[2 * i + 1]) != hipSuccess) return -1;
+    pool.ms += ms;
+    pool.n += 1;
+  }
+  pool.used = 0;
+  return 0;
+}
+
+int device_status(confkv_handle* h) {
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  uint32_t err = 0;
+  if (hipMemcpy(&err, h->lay.err, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  if (!err) return CONFKV_OK;
+  h->poisoned = 1;
+  if (err & kErrNonFinite) return CONFKV_ENONFINITE;
+  if (err & kErrCapacity) return CONFKV_ECAPACITY;
+  return CONFKV_EHIP;
+}
+
+}  // namespace
+
+CONFKV_API int confkv_validate(const confkv_config* cfg, int32_t prefill_len) { return check_cfg(cfg, prefill_len); }
+
+CONFKV_API size_t confkv_state_bytes(const confkv_config* cfg) {
+  if (check_cfg(cfg, 0) != CONFKV_OK) return 0;
+  return carve(cfg, nullptr, nullptr);
+}
+
+CONFKV_API int32_t confkv_rows_max(const confkv_config* cfg) {
+  if (check_cfg(cfg, 0) != CONFKV_OK) return 0;
+  return cfg->capacity + (int32_t)window_of(cfg) + 1;
+}
+
+CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_bytes, void* stream,
+                           const uint16_t* prefill_k, const uint16_t* prefill_v, int32_t prefill_len,
+                           confkv_handle** out) {
+  if (!out) return CONFKV_EINVAL;
+  *out = nullptr;
+  const int rc = check_cfg(cfg, prefill_len);
+  if (rc != CONFKV_OK) return rc;
+  if (!state || ((uintptr_t)state & 255)) return CONFKV_EINVAL;
+  if (state_bytes < carve(cfg, nullptr, nullptr)) return CONFKV_ECAPACITY;
+  if (prefill_len > 0 && (!prefill_k || !prefill_v)) return CONFKV_EINVAL;
+  if (prefill_len == 0 && (prefill_k || prefill_v)) return CONFKV_EINVAL;
+  confkv_handle* h = new (std::nothrow) confkv_handle();
+  if (!h) return CONFKV_EHIP;
+  h->magic = kMagic;
+  h->cfg = *cfg;
+  carve(cfg, (uint8_t*)state, &h->lay);
+  h->par = make_params(cfg);
+  h->state = state;
+  h->state_bytes = state_bytes;
+  h->t = prefill_len;
+  h->rows_bound = prefill_len;
+  h->keep_max = keep_bound(cfg);
+  h->poisoned = 0;
+  h->last_stream = (hipStream_t)stream;
+  h->prof = 0;
+  if (launch_init(h->lay, h->par, prefill_k, prefill_v, prefill_len, stream) != 0) {
+    h->magic = kDead;
+    delete h;
+    return CONFKV_EHIP;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(h);
+  }
+  *out = h;
+  return CONFKV_OK;
+}
+
+CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, const uint16_t* q,
+                           const uint16_t* k_new, const uint16_t* v_new, const float* prio_new, uint16_t* out,
+                           float* conf_out, int32_t* budget_out) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  if (!q || !k_new || !v_new || !out) return CONFKV_EINVAL;
+  const bool conf = h->cfg.policy == CONFKV_POLICY_CONF;
+  if (conf && (!logits || prio_new)) return CONFKV_EINVAL;
+  if (!conf && (logits || !prio_new || conf_out || budget_out)) return CONFKV_EINVAL;
+  if (h->t >= (int64_t)INT32_MAX - 1) return CONFKV_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  const Layout& lay = h->lay;
+  if (conf) {
+    if (record_event(h, h->pr, s, true)) goto hip_fail;
+    if (launch_conf_reduce(lay, h->par, logits, conf_out, budget_out, stream) != 0) goto hip_fail;
+    if (record_event(h, h->pr, s, false)) goto hip_fail;
+  }
+  {
+    StepArgs a;
+    a.t = (int32_t)h->t;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.prio_new = prio_new;
+    a.out = out;
+    const int64_t rows = std::min<int64_t>(h->rows_bound, lay.cap) + lay.Wr;
+    const int64_t lds_rows = (rows + 3) & ~(int64_t)3;
+    const int64_t lds_bytes = lds_rows * lay.planes * 4;
+    const bool use_lds = lds_bytes <= fused_max_dynamic_lds();
+    a.lds_rows = use_lds ? (int32_t)lds_rows : 0;
+    if (!use_lds && !lay.stage) return CONFKV_EINVAL;  // cannot happen: carve sized the staging
+    if (record_event(h, h->pf, s, true)) goto hip_fail;
+    if (launch_fused_step(lay, h->par, a, use_lds, use_lds ? (int)lds_bytes : 0, stream) != 0) goto hip_fail;
+    if (record_event(h, h->pf, s, false)) goto hip_fail;
+  }
+  h->t += 1;
+  h->rows_bound = std::min(h->rows_bound + 1, h->keep_max);
+  return CONFKV_OK;
+hip_fail:
+  h->poisoned = 1;
+  return CONFKV_EHIP;
+}
+
+CONFKV_API int confkv_read_cache(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count, int32_t* len,
+                                 int32_t* pos, float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8,
+                                 int8_t* v8, float* k_scale, float* v_scale, uint8_t* is_int8) {
+  if (!live(h) || h->poisoned) return CONFKV_ESTATE;
+  if (!len || seg_first < 0 || seg_count < 1 || seg_first + (int64_t)seg_count > h->lay.S) return CONFKV_EINVAL;
+  h->last_stream = (hipStream_t)stream;
+  if (launch_read_cache(h->lay, seg_first, seg_count, len, pos, ema, prio, k16, v16, k8, v8, k_scale, v_scale,
+                        is_int8, h->cfg.old_int8, stream) != 0) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  return device_status(h);
+}
+
+CONFKV_API int confkv_read_last_step(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count,
+                                     int32_t* meta, int32_t* pos, float* score, float* lse) {
+  if (!live(h) || h->poisoned) return CONFKV_ESTATE;
+  if (!h->cfg.record_scores) return CONFKV_EINVAL;
+  if (seg_first < 0 || seg_count < 1 || seg_first + (int64_t)seg_count > h->lay.S) return CONFKV_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  const Layout& L = h->lay;
+  const size_t rm = (size_t)L.rows_max;
+  bool ok = true;
+  if (meta)
+    ok &= hipMemcpyAsync(meta, L.rec_meta + (size_t)seg_first * 4, (size_t)seg_count * 16, hipMemcpyDeviceToDevice,
+                         s) == hipSuccess;
+  if (pos)
+    ok &= hipMemcpyAsync(pos, L.rec_pos + (size_t)seg_first * rm, (size_t)seg_count * rm * 4,
+                         hipMemcpyDeviceToDevice, s) == hipSuccess;
+  if (score)
+    ok &= hipMemcpyAsync(score, L.rec_score + (size_t)seg_first * rm, (size_t)seg_count * rm * 4,
+                         hipMemcpyDeviceToDevice, s) == hipSuccess;
+  if (lse)
+    ok &= hipMemcpyAsync(lse, L.rec_lse + (size_t)seg_first * L.G, (size_t)seg_count * L.G * 4,
+                         hipMemcpyDeviceToDevice, s) == hipSuccess;
+  if (!ok) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  return device_status(h);
+}
+
+CONFKV_API int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, int32_t reset) {
+  if (!live(h) || h->poisoned) return CONFKV_ESTATE;
+  if (!totals) return CONFKV_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  if (launch_stats_total(h->lay, reset, stream) != 0 ||
+      hipMemcpyAsync(totals, h->lay.stats_total, kStatFields * 8, hipMemcpyDeviceToHost, s) != hipSuccess) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  return device_status(h);
+}
+
+CONFKV_API int confkv_profile(confkv_handle* h, int32_t enable) {
+  if (!live(h)) return CONFKV_ESTATE;
+  h->prof = enable ? 1 : 0;
+  return CONFKV_OK;
+}
+
+CONFKV_API int confkv_profile_read(confkv_handle* h, double* fused_ms, int64_t* fused_launches, double* reduce_ms,
+                                   int64_t* reduce_launches, int32_t reset) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (collect(h->pf) || collect(h->pr)) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  if (fused_ms) *fused_ms = h->pf.ms;
+  if (fused_launches) *fused_launches = h->pf.n;
+  if (reduce_ms) *reduce_ms = h->pr.ms;
+  if (reduce_launches) *reduce_launches = h->pr.n;
+  if (reset) {
+    h->pf.ms = h->pr.ms = 0.0;
+    h->pf.n = h->pr.n = 0;
+  }
+  return CONFKV_OK;
+}
+
+CONFKV_API int64_t confkv_position(const confkv_handle* h) { return live(h) ? h->t : -1; }
+
+CONFKV_API int confkv_status(confkv_handle* h) {
+  if (!live(h)) return CONFKV_ESTATE;
+  return device_status(h);
+}
+
+CONFKV_API int confkv_destroy(confkv_handle* h) {
+  if (!h) return CONFKV_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_live.erase(h)) return CONFKV_ESTATE;
+  }
+  for (hipEvent_t e : h->pf.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->pr.ev) (void)hipEventDestroy(e);
+  h->magic = kDead;
+  delete h;
+  return CONFKV_OK;
+}
+
+CONFKV_API const char* confkv_strerror(int code) {
+  switch (code) {
+    case CONFKV_OK: return "ok";
+    case CONFKV_EINVAL: return "invalid argument, shape or configuration";
+    case CONFKV_ECAPACITY: return "capacity or state buffer too small";
+    case CONFKV_EHIP: return "HIP runtime error";
+    case CONFKV_ENONFINITE: return "non-finite logits or ranking score";
+    case CONFKV_ESTATE: return "handle destroyed or poisoned by an earlier error";
+    default: return "unknown status code";
+  }
+}

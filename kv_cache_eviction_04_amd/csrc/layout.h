@@ -1,0 +1,99 @@
+// Device-state layout and kernel parameter blocks shared by the host ABI
+// (api.hip) and the kernels (kernels.hip). Internal: not part of the C ABI.
+//
+// Per segment seg = (l*B + b)*Hkv + h the state holds two regions:
+//   ring  — the FP16 window: Wr = W + 1 slots, a row at position p lives in
+//           slot p mod Wr; ring_pos = -1 marks an empty or evicted slot. At
+//           step t the live slots hold positions in [t-W, t].
+//   old   — rows older than the window, densely packed in [0, n_old) in no
+//           particular order: INT8 codes + fp32 absmax scales (old_int8) or
+//           FP16. Every old position is below every ring position.
+// All arrays are segment-major structure-of-arrays; each array base is
+// 256-byte aligned and every K/V row starts on a 64-byte boundary.
+#pragma once
+#include <stdint.h>
+
+namespace confkv {
+
+constexpr int kThreads = 256;          // fused-step workgroup
+constexpr int kChunk = 4096;           // logits per reducer workgroup (256 x 16)
+constexpr int kStatFields = 4;         // kv bytes, rows attended, rows moved, rows evicted
+constexpr uint32_t kErrNonFinite = 1u, kErrCapacity = 2u, kErrInternal = 4u;
+
+struct ConfPartial {                   // one logits chunk: m = top1
+  double S;                            // sum exp(z - m)
+  double T;                            // sum exp(z - m) * (z - m)
+  float m, top2;
+  uint32_t nonfinite, pad;
+};
+
+struct Layout {
+  int32_t L, B, Hq, Hkv, G, D, V;
+  int32_t S;          // segments
+  int32_t cap;        // old rows per segment
+  int32_t W;          // FP16 window (rows with pos > t - W stay in the ring)
+  int32_t Wr;         // ring slots = W + 1
+  int32_t rows_max;   // cap + Wr: staged rows per segment upper bound
+  int32_t planes;     // staging planes per segment = max(G, 4)
+  int32_t chunks;     // logits chunks per batch row
+  int32_t old_bytes;  // bytes per element of an old row (1 int8, 2 fp16)
+  // ring
+  uint16_t* ring_k;   // [S][Wr][D]
+  uint16_t* ring_v;
+  int32_t* ring_pos;  // [S][Wr]
+  float* ring_ema;    // [S][Wr]
+  float* ring_prio;   // [S][Wr]
+  // old
+  uint8_t* old_k;     // [S][cap][D * old_bytes]
+  uint8_t* old_v;
+  float* old_ks;      // [S][cap] (old_int8)
+  float* old_vs;
+  int32_t* old_pos;   // [S][cap]
+  float* old_ema;     // [S][cap]
+  float* old_prio;    // [S][cap]
+  int32_t* seg_nold;  // [S]
+  uint64_t* seg_stats;  // [S][kStatFields]
+  float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
+  // confidence reducer
+  ConfPartial* partials;  // [B][chunks]
+  uint32_t* row_counter;  // [B]
+  float* row_conf;        // [B]
+  int32_t* row_base;      // [B]
+  uint32_t* err;          // [1]
+  uint64_t* stats_total;  // [kStatFields]
+  // last-step record (record_scores)
+  int32_t* rec_meta;  // [S][4]
+  int32_t* rec_pos;   // [S][rows_max]
+  float* rec_score;   // [S][rows_max]
+  float* rec_lse;     // [S][G]
+};
+
+struct Params {
+  float tau, alpha, beta, w_e, w_m, w_p, sm_scale;
+  int32_t n_low, n_high, P, s, kvpop_k, policy, gate_literal, pyramid, old_int8, record;
+};
+
+struct StepArgs {
+  int32_t t;                 // position decoded this step
+  int32_t lds_rows;          // staged-row capacity of the LDS planes (LDS variant)
+  const uint16_t* q;         // [L][B][Hq][D]
+  const uint16_t* k_new;     // [L][B][Hkv][D]
+  const uint16_t* v_new;
+  const float* prio_new;     // [L][B][Hkv] or null
+  uint16_t* out;             // [L][B][Hq][D]
+};
+
+// Launchers (kernels.hip). All enqueue on `stream` and return the launch status.
+int launch_init(const Layout& lay, const Params& par, const uint16_t* pk, const uint16_t* pv, int32_t P0,
+                void* stream);
+int launch_conf_reduce(const Layout& lay, const Params& par, const float* logits, float* conf_out,
+                       int32_t* budget_out, void* stream);
+int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
+                      void* stream);
+int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, int32_t* len, int32_t* pos,
+                      float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8, int8_t* v8,
+                      float* ks, float* vs, uint8_t* is8, int32_t old_int8, void* stream);
+int launch_stats_total(const Layout& lay, int32_t reset, void* stream);
+int fused_max_dynamic_lds();
+
+}  // namespace confkv
