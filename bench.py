@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused evict+attend decode step on one MI355X.
+
+Default workload: the Llama-3-8B shape at a 32K context (32 layers, 32 query /
+8 KV heads, head_dim 128, vocab 128256, batch 16, 32768-token synthetic
+prefill, budgets 1024 / 2048, protected window 128, FP16 window 256). After
+the first decode step (which attends over the whole prefill and evicts down
+to the budget; timed and reported separately) and `--warmup` steps, exactly
+`--steps` steady decode steps are timed. Each step is the whole hot path: the
+logits reducer (confidence and budget) and the fused attend+evict kernel.
+Inputs for the timed steps are generated and resident in HBM beforehand.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode steps/s + KV GB/s (fraction of HBM peak) for fused evict+attend step"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, st, steps, S):
+    """Bytes the method must move per launch of the fused kernel (averaged over
+    the timed steps): KV rows read, per-row state, query/output/new-row
+    traffic, and rows moved by compaction or age-out."""
+    L, B, Hq, d = w["num_layers"], w["batch"], w["num_q_heads"], w["head_dim"]
+    kv = st["kv_bytes"] / steps
+    per_row_state = 8 if w["policy"] == "kvpop" else 12      # pos + (prio) | pos + ema read + ema write
+    state = st["rows_attended"] / steps * per_row_state
+    io = 2 * (L * B * Hq * d * 2) + S * (2 * d * 2) + S * (4 * d)
+    old_row = (2 * d + 8) if w["old_int8"] else 4 * d
+    moved = st["rows_moved"] / steps * 2 * old_row
+    return kv, kv + state + io + moved
+
+
+def cpu_baseline(w, gpu, seed, first_input_step, budget_s):
+    """Time the CPU oracle (as it stands) on a bounded, exact sample of the same
+    workload: a subset of segments continued from the GPU's current state."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_eviction_04_amd import synth
+    from oracle import cache as OC
+    from oracle import confidence as OCONF
+
+    L, B, H = w["num_layers"], w["batch"], w["num_kv_heads"]
+    rows = sorted({0, B - 1})
+    layers = sorted({0, L // 2, L - 1})
+    segs = [(l * B + b) * H + h for l in layers for b in rows for h in range(H)]
+    cfg = OC.Config.from_dict(w)
+    oc = OC.OracleCache(cfg, segs)
+    for s in segs:
+        ro = {k: v.cpu().numpy() for k, v in gpu.read_cache(s, 1).items()}
+        seg = OC.Segment(w["head_dim"])
+        n = int(ro["len"][0])
+        seg.pos = ro["pos"][0, :n].astype(np.int64)
+        seg.is8 = ro["is_int8"][0, :n].astype(bool)
+        seg.k16, seg.v16 = ro["k16"][0, :n].copy(), ro["v16"][0, :n].copy()
+        seg.k8, seg.v8 = ro["k8"][0, :n].copy(), ro["v8"][0, :n].copy()
+        seg.ks, seg.vs = ro["k_scale"][0, :n].copy(), ro["v_scale"][0, :n].copy()
+        seg.ema = ro["ema"][0, :n].astype(np.float64)
+        seg.prio = ro["prio"][0, :n].copy()
+        oc.segs[s] = seg
+    oc.t = gpu.position
+    dev = torch.device("cuda", 0)
+    t_seg = t_conf = 0.0
+    n_steps = 0
+    with threadpool_limits(limits=1):
+        while t_seg + t_conf < budget_s:
+            x = synth.step_inputs(w, seed, first_input_step + n_steps, dev)
+            xs = {k: (None if v is None else v.cpu().numpy()) for k, v in x.items()}
+            base = None
+            if cfg.policy == "conf":
+                t0 = time.perf_counter()
+                base = {}
+                for b in rows:
+                    c = OCONF.confidence(xs["logits"][b], cfg.w_entropy, cfg.w_margin, cfg.w_pmax)
+                    base[b] = OCONF.gate(c, cfg.tau, cfg.n_low, cfg.n_high, cfg.gate_literal)
+                t_conf += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oc.step(logits=xs["logits"] if cfg.policy == "conf" else None, q=xs["q"], k_new=xs["k"],
+                    v_new=xs["v"], prio=xs["prio"], base_override=base)
+            t_seg += time.perf_counter() - t0
+            n_steps += 1
+    S = L * B * H
+    # oc.step computes the confidence of its rows itself; t_conf times that same work on its own, so
+    # the segment part is (t_seg - t_conf) and the confidence part scales with the batch rows.
+    per_step = ((t_seg - t_conf) / n_steps) * (S / len(segs)) + (t_conf / n_steps) * (B / len(rows))
+    return {
+        "value": 1.0 / per_step,
+        "unit": "steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{n_steps} steady steps of {len(segs)} of {S} segments (batch rows {rows}, layers {layers}, "
+                   f"all {H} KV heads) continued from the GPU state, plus confidence for {len(rows)} of {B} rows; "
+                   f"per-step time extrapolated x{S}/{len(segs)} (segments) and x{B}/{len(rows)} (rows); "
+                   f"float64 NumPy, one thread"),
+        "seconds": t_seg + t_conf,
+        "steps_timed": n_steps,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference kernel for HBM counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs the decode step on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_eviction_04_amd import confkv, synth
+
+    dev = torch.device("cuda", 0)
+    w = synth.workload(args.workload)
+    L, B, Hq, H, d = w["num_layers"], w["batch"], w["num_q_heads"], w["num_kv_heads"], w["head_dim"]
+    S = L * B * H
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
+
+    log(f"workload {args.workload}: L{L} B{B} Hq{Hq} Hkv{H} d{d} prefill {w['prefill']}")
+    t0 = time.perf_counter()
+    pk = pv = None
+    if w["prefill"]:
+        pk, pv = synth.prefill(w, args.seed, dev)
+    gpu = confkv.Cache(w, pk, pv, device=dev)
+    torch.cuda.synchronize()
+    del pk, pv
+    torch.cuda.empty_cache()
+    log(f"init done in {time.perf_counter() - t0:.1f}s, state {gpu.state_bytes / 2**30:.2f} GiB")
+
+    step_i = 0
+    out = torch.empty((L, B, Hq, d), dtype=torch.float16, device=dev)
+
+    def run_step(x):
+        gpu.step(x["logits"], x["q"], x["k"], x["v"], x["prio"], out=out)
+
+    # first decode step: attends over the whole prefill, then evicts to the budget
+    x = synth.step_inputs(w, args.seed, step_i, dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_step(x)
+    e1.record()
+    torch.cuda.synchronize()
+    first_ms = e0.elapsed_time(e1)
+    step_i += 1
+    first_stats = gpu.stats(reset=True)
+    log(f"first step {first_ms:.3f} ms, KV read {first_stats['kv_bytes'] / 1e9:.2f} GB")
+
+    fill = 0
+    if w["policy"] == "kvpop":  # reach the steady state: sinks + window + k rows
+        fill = w["num_sink"] + w["protect_last"] + w["kvpop_k"]
+    for i in range(fill + args.warmup):
+        run_step(synth.step_inputs(w, args.seed, step_i, dev))
+        step_i += 1
+    inputs = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    gpu.stats(reset=True)
+    gpu.profile(True)
+    gpu.profile_read(reset=True)
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for x in inputs:
+        run_step(x)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_i += args.steps
+    gpu.profile(False)
+    prof = gpu.profile_read(reset=True)
+    st = gpu.stats(reset=True)
+    rc = gpu.status()
+    if rc != confkv.OK:
+        log(f"device status {rc}")
+        sys.exit(1)
+
+    ms_per_step = wall * 1e3 / args.steps
+    steps_per_s = args.steps / wall
+    kv_per_step, alg_per_launch = algorithmic_bytes(w, st, args.steps, S)
+    kv_gbps = kv_per_step / (ms_per_step * 1e-3) / 1e9
+    fused_avg_ms = prof["fused_ms"] / max(prof["fused_launches"], 1)
+    reduce_avg_ms = prof["reduce_ms"] / max(prof["reduce_launches"], 1)
+    achieved = alg_per_launch / (fused_avg_ms * 1e-3) / 1e9
+    log(f"{steps_per_s:.1f} steps/s ({ms_per_step:.4f} ms/step), KV {kv_gbps:.0f} GB/s; fused kernel "
+        f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic; reducer {reduce_avg_ms * 1e3:.1f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.4g} steps/s ({cpu['seconds']:.1f}s of CPU work)")
+
+    res = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": d,
+            "vocab": w["vocab"], "prefill": w["prefill"], "policy": w["policy"],
+            "n_low": w["n_low"], "n_high": w["n_high"], "protect_last": w["protect_last"],
+            "fp16_window": w["fp16_window"], "num_sink": w["num_sink"], "kvpop_k": w["kvpop_k"],
+            "pyramid": w["pyramid"], "kv_storage": "fp16 window + int8 older rows" if w["old_int8"] else "fp16",
+            "seed": args.seed,
+        },
+        "kv_gb_per_s": kv_gbps,
+        "kv_frac_of_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
+        "kv_bytes_per_step": kv_per_step,
+        "tokens_per_s": steps_per_s * B,
+        "first_step_ms": first_ms,
+        "first_step_kv_bytes": first_stats["kv_bytes"],
+        "reducer_us": reduce_avg_ms * 1e3,
+        "rows_evicted_per_step": st["rows_evicted"] / args.steps,
+        "rows_moved_per_step": st["rows_moved"] / args.steps,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "fused_step_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "bytes_per_launch": alg_per_launch,
+            "avg_launch_us": fused_avg_ms * 1e3,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -262,28 +262,46 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
     s_last = (prev == (uint32_t)(lay.chunks - 1));
   }
   __syncthreads();
-  if (!s_last || tid != 0) return;
+  if (!s_last || wave != 0) return;
   __threadfence();
 
-  const volatile ConfPartial* parts = lay.partials + (size_t)b * lay.chunks;
-  double Mx = -INFINITY;
+  // Last chunk of row b: wave 0 merges the partials, one chunk per lane.
+  const ConfPartial* parts = lay.partials + (size_t)b * lay.chunks;
   float a1 = -INFINITY, a2 = -INFINITY;
+  double pm = -INFINITY, pS = 0.0, pT = 0.0;
   uint32_t badall = 0;
-  for (int c = 0; c < lay.chunks; ++c) {
-    const float pm = parts[c].m, p2 = parts[c].top2;
-    badall |= parts[c].nonfinite;
-    Mx = fmax(Mx, (double)pm);
-    top2_merge(a1, a2, pm, p2);
+  for (int c0 = 0; c0 < lay.chunks; c0 += 64) {
+    const int c = c0 + lane;
+    if (c < lay.chunks) {
+      const ConfPartial P = parts[c];
+      badall |= P.nonfinite;
+      top2_merge(a1, a2, P.m, P.top2);
+      // fold chunk c into this lane's running (m, S, T)
+      const double m2 = (double)P.m;
+      if (m2 > -INFINITY) {
+        const double mx = fmax(pm, m2);
+        const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(m2 - mx);
+        pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (P.T + (m2 - mx) * P.S);
+        pS = f1 * pS + f2 * P.S;
+        pm = mx;
+      }
+    }
   }
-  double Sx = 0.0, Tx = 0.0;
-  for (int c = 0; c < lay.chunks; ++c) {
-    const double pm = (double)parts[c].m;
-    if (pm == -INFINITY) continue;
-    const double f = exp(pm - Mx);
-    const double pS = parts[c].S, pT = parts[c].T;
-    Sx += pS * f;
-    Tx += f * (pT + (pm - Mx) * pS);
+  for (int o = 32; o > 0; o >>= 1) {
+    const float o1 = __shfl_xor(a1, o, 64), o2 = __shfl_xor(a2, o, 64);
+    top2_merge(a1, a2, o1, o2);
+    badall |= __shfl_xor(badall, o, 64);
+    const double qm = __shfl_xor(pm, o, 64), qS = __shfl_xor(pS, o, 64), qT = __shfl_xor(pT, o, 64);
+    if (qm > -INFINITY) {
+      const double mx = fmax(pm, qm);
+      const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(qm - mx);
+      pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (qT + (qm - mx) * qS);
+      pS = f1 * pS + f2 * qS;
+      pm = mx;
+    }
   }
+  if (lane != 0) return;
+  const double Sx = pS, Tx = pT;
   const double H = log(Sx) - Tx / Sx;
   const double Hn = H / log((double)V);
   const double margin = (double)a1 - (double)a2;
@@ -359,11 +377,12 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
 }
 
 template <int D, int G, bool kLds>
-__global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params par, StepArgs a) {
+__global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fused_step_kernel(Layout lay, Params par, StepArgs a) {
   constexpr int LPR = D / 16;          // lanes per row
   constexpr int RPB = kThreads / LPR;  // rows per block iteration
   constexpr int PL = G > 4 ? G : 4;    // staging planes
-  constexpr int U = 2;                 // rows per lane in flight
+  constexpr int U8 = 8;                // INT8 rows per lane in flight (16 B each)
+  constexpr int U16 = 4;               // FP16 rows per lane in flight (32 B each)
   static_assert(LPR == 4 || LPR == 8, "head_dim 64 or 128");
 
   __shared__ float red_f[4][G];
@@ -451,11 +470,11 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
   for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
 
   if (par.old_int8) {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U) {
-      uint4 kk[U];
-      float sc[U];
+    for (int i0 = rg; i0 < n_old; i0 += RPB * U8) {
+      uint4 kk[U8];
+      float sc[U8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U8; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           kk[u] = *reinterpret_cast<const uint4*>(okp + (size_t)i * D + c * 16);
@@ -463,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U8; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           h2 kh[8];
@@ -485,10 +504,10 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
   } else {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U) {
-      uint4 k0[U], k1[U];
+    for (int i0 = rg; i0 < n_old; i0 += RPB * U16) {
+      uint4 k0[U16], k1[U16];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U16; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           const uint4* p = reinterpret_cast<const uint4*>(okp + ((size_t)i * D + c * 16) * 2);
@@ -497,7 +516,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U16; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           const h2 kh[8] = {as_h2(k0[u].x), as_h2(k0[u].y), as_h2(k0[u].z), as_h2(k0[u].w),
@@ -515,11 +534,11 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
   }
-  for (int r0 = rg; r0 < Wr; r0 += RPB * U) {
-    uint4 k0[U], k1[U];
-    bool live[U];
+  for (int r0 = rg; r0 < Wr; r0 += RPB * U16) {
+    uint4 k0[U16], k1[U16];
+    bool live[U16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U16; ++u) {
       const int r = r0 + u * RPB;
       live[u] = false;
       if (r < Wr) {
@@ -532,7 +551,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U16; ++u) {
       const int r = r0 + u * RPB;
       if (r < Wr) {
         if (live[u]) {
@@ -602,11 +621,11 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
     for (int e = 0; e < 16; ++e) acc[g][e] = 0.0f;
   }
   if (par.old_int8) {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U) {
-      uint4 vv[U];
-      float sc[U];
+    for (int i0 = rg; i0 < n_old; i0 += RPB * U8) {
+      uint4 vv[U8];
+      float sc[U8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U8; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           vv[u] = *reinterpret_cast<const uint4*>(ovp + (size_t)i * D + c * 16);
@@ -614,7 +633,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U8; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           const uint32_t w4[4] = {vv[u].x ^ 0x80808080u, vv[u].y ^ 0x80808080u, vv[u].z ^ 0x80808080u,
@@ -633,10 +652,10 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
   } else {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U) {
-      uint4 v0[U], v1[U];
+    for (int i0 = rg; i0 < n_old; i0 += RPB * U16) {
+      uint4 v0[U16], v1[U16];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U16; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           const uint4* p = reinterpret_cast<const uint4*>(ovp + ((size_t)i * D + c * 16) * 2);
@@ -645,7 +664,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U16; ++u) {
         const int i = i0 + u * RPB;
         if (i < n_old) {
           const uint32_t w8[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
@@ -665,11 +684,11 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
   }
-  for (int r0 = rg; r0 < Wr; r0 += RPB * U) {
-    uint4 v0[U], v1[U];
-    bool live[U];
+  for (int r0 = rg; r0 < Wr; r0 += RPB * U16) {
+    uint4 v0[U16], v1[U16];
+    bool live[U16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U16; ++u) {
       const int r = r0 + u * RPB;
       live[u] = false;
       if (r < Wr) {
@@ -682,7 +701,7 @@ __global__ void __launch_bounds__(kThreads) fused_step_kernel(Layout lay, Params
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U16; ++u) {
       const int r = r0 + u * RPB;
       if (r < Wr && live[u]) {
         const uint32_t w8[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
