@@ -122,11 +122,13 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   lay.cap = c->capacity;
   lay.W = (int32_t)window_of(c);
   lay.Wr = lay.W + 1;
-  lay.rows_max = lay.cap + lay.Wr;
+  lay.cap32 = (lay.cap + 31) & ~31;
+  lay.Wr32 = (lay.Wr + 31) & ~31;
+  lay.rows_max = lay.cap32 + lay.Wr32;
   lay.planes = std::max(lay.G, 4);
   lay.chunks = lay.V > 0 ? (lay.V + kChunk - 1) / kChunk : 0;
   lay.old_bytes = c->old_int8 ? 1 : 2;
-  const size_t S = (size_t)lay.S, D = (size_t)lay.D, Wr = (size_t)lay.Wr, cap = (size_t)lay.cap;
+  const size_t S = (size_t)lay.S, D = (size_t)lay.D, Wr = (size_t)lay.Wr32, cap = (size_t)lay.cap32;
   size_t off = 0;
   auto take = [&](size_t bytes) -> uint8_t* {
     const size_t o = align256(off);
@@ -253,7 +255,9 @@ CONFKV_API size_t confkv_state_bytes(const confkv_config* cfg) {
 
 CONFKV_API int32_t confkv_rows_max(const confkv_config* cfg) {
   if (check_cfg(cfg, 0) != CONFKV_OK) return 0;
-  return cfg->capacity + (int32_t)window_of(cfg) + 1;
+  Layout lay;
+  carve(cfg, nullptr, &lay);
+  return lay.rows_max;
 }
 
 CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_bytes, void* stream,
@@ -281,7 +285,8 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   h->poisoned = 0;
   h->last_stream = (hipStream_t)stream;
   h->prof = 0;
-  if (launch_init(h->lay, h->par, prefill_k, prefill_v, prefill_len, stream) != 0) {
+  if (launch_init(h->lay, h->par, state, carve(cfg, nullptr, nullptr), prefill_k, prefill_v, prefill_len, stream) !=
+      0) {
     h->magic = kDead;
     delete h;
     return CONFKV_EHIP;
@@ -320,8 +325,8 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
     a.v_new = v_new;
     a.prio_new = prio_new;
     a.out = out;
-    const int64_t rows = std::min<int64_t>(h->rows_bound, lay.cap) + lay.Wr;
-    const int64_t lds_rows = (rows + 3) & ~(int64_t)3;
+    const int64_t old32 = (std::min<int64_t>(h->rows_bound, lay.cap) + 31) & ~(int64_t)31;
+    const int64_t lds_rows = old32 + lay.Wr32;
     const int64_t lds_bytes = lds_rows * lay.planes * 4;
     const bool use_lds = lds_bytes <= fused_max_dynamic_lds();
     a.lds_rows = use_lds ? (int32_t)lds_rows : 0;

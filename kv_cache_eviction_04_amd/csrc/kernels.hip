@@ -6,9 +6,10 @@
 //                       chunk; the last chunk of a batch row to finish merges
 //                       them into the confidence c and the base budget.
 //   fused_step_kernel   one workgroup per segment (layer, batch row, KV head):
-//                       append -> QK pass -> max -> exp/sum -> PV pass -> out
-//                       -> mass/EMA/score/key -> select -> compact -> age-out.
-//   init / ingest       carve the state and store the prefill.
+//                       append -> QK on MFMA -> max -> exp/sum -> PV on MFMA
+//                       -> out -> mass/EMA/score/key -> select -> compact ->
+//                       age-out.
+//   init / ingest       zero the state and store the prefill.
 //   read_cache          logical (ascending position) read-out for checking.
 //
 // Sources: "Conf-KV" post (rcap.io), method paragraph and decoding-loop
@@ -23,27 +24,40 @@
 namespace confkv {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ half8 as_h8(uint4 u) { return __builtin_bit_cast(half8, u); }
 __device__ __forceinline__ float half_lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[0]; }
 __device__ __forceinline__ float half_hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[1]; }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- V tiles
+// Element offset of (row, col) in a segment's transposed V storage (see
+// layout.h): rows in tiles of 32, each tile 32*D elements.
+__device__ __forceinline__ size_t vt8(int row, int col, int D) {
+  const int r = row & 31, q = r >> 3, e = r & 7, cb = col >> 4, j = col & 15;
+  return (size_t)(row >> 5) * 32 * D + 1024 * (cb >> 1) + 16 * (16 * q + j) + 8 * (cb & 1) + e;
+}
+__device__ __forceinline__ size_t vt16(int row, int col, int D) {
+  const int r = row & 31, q = r >> 3, e = r & 7, cb = col >> 4, j = col & 15;
+  return (size_t)(row >> 5) * 32 * D + 512 * cb + 8 * (16 * q + j) + e;
+}
 
 // ---------------------------------------------------------------- lane groups
-// A row of d elements is spread over LPR = d/16 consecutive lanes, 16 elements
-// (16 bytes of INT8 or 32 bytes of FP16) each. Reductions inside a group use
-// DPP: quad_perm swaps (xor 1, xor 2) and, for 8-lane groups, the half-row
-// mirror (lane i <-> 7-i), which pairs the two quads.
+// Row-wise work (quantization, moves) spreads a row of d elements over
+// LPR = d/16 consecutive lanes, 16 elements each. Group reductions use DPP:
+// quad_perm swaps (xor 1, xor 2) and, for 8-lane groups, the half-row mirror
+// (lane i <-> 7-i), which pairs the two quads.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  if constexpr (LPR == 8) v += dpp<0x141>(v);
-  return v;
 }
 template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
@@ -61,6 +75,16 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
   const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   lo = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
   hi = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+}
+// 16 codes -> codes 0..7 and 8..15 as fp16 MFMA operands.
+__device__ __forceinline__ void i8x16_to_h8(uint4 w, half8& a, half8& b) {
+  h2 t0, t1, t2, t3, t4, t5, t6, t7;
+  i8x4_to_h2(w.x, t0, t1);
+  i8x4_to_h2(w.y, t2, t3);
+  i8x4_to_h2(w.z, t4, t5);
+  i8x4_to_h2(w.w, t6, t7);
+  a = half8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+  b = half8{t4[0], t4[1], t5[0], t5[1], t6[0], t6[1], t7[0], t7[1]};
 }
 
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -134,24 +158,17 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* re
 // clamped to [-127, 127]; amax == 0 gives scale 0 and zero codes. Both
 // quotients are formed in binary64 and rounded once to binary32, which is the
 // correctly rounded binary32 quotient (53 >= 2*24 + 2), independent of the
-// compiler's float-division mode.
+// compiler's float-division mode. Returns the group's scale; codes[e] holds
+// the code of element e.
 template <int LPR>
-__device__ __forceinline__ void quantize16(const uint16_t* src, uint8_t* dst_codes, float* dst_scale, bool lead) {
-  const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(src)[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[2 * j] = half_lo(w[j]);
-    x[2 * j + 1] = half_hi(w[j]);
-  }
+__device__ __forceinline__ float quantize16(const float (&x)[16], int8_t (&codes)[16]) {
   float am = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(x[e]));
   am = group_max<LPR>(am);
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
   float scale = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) codes[e] = 0;
   if (am > 0.0f) {
     scale = (float)((double)am / 127.0);
     const double sd = (double)scale;
@@ -159,11 +176,26 @@ __device__ __forceinline__ void quantize16(const uint16_t* src, uint8_t* dst_cod
     for (int e = 0; e < 16; ++e) {
       float r = rintf((float)((double)x[e] / sd));
       r = fminf(fmaxf(r, -127.0f), 127.0f);
-      packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (e & 3));
+      codes[e] = (int8_t)(int)r;
     }
   }
-  *reinterpret_cast<uint4*>(dst_codes) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  if (lead) *dst_scale = scale;
+  return scale;
+}
+__device__ __forceinline__ void load16h(const uint16_t* src, float (&x)[16]) {
+  const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = half_lo(w[j]);
+    x[2 * j + 1] = half_hi(w[j]);
+  }
+}
+__device__ __forceinline__ uint4 pack16(const int8_t (&c)[16]) {
+  uint32_t p[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) p[e >> 2] |= ((uint32_t)(uint8_t)c[e]) << (8 * (e & 3));
+  return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
 // ======================================================= logits -> confidence
@@ -178,6 +210,14 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
   a2 = fmaxf(lo, fmaxf(a2, b2));
   a1 = hi;
 }
+__device__ __forceinline__ void mst_merge(double& pm, double& pS, double& pT, double qm, double qS, double qT) {
+  if (qm == -INFINITY) return;
+  const double mx = fmax(pm, qm);
+  const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(qm - mx);
+  pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (qT + (qm - mx) * qS);
+  pS = f1 * pS + f2 * qS;
+  pm = mx;
+}
 
 __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par, const float* logits, float* conf_out,
                                                           int32_t* budget_out) {
@@ -190,27 +230,20 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
   const float* z = logits + (size_t)b * V;
   const int begin = ci * kChunk, end = min(V, begin + kChunk);
 
+  // all 16 loads first (index clamped into the chunk), then the arithmetic
   float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = z[min(begin + tid + 256 * j, end - 1)];
   float t1 = -INFINITY, t2 = -INFINITY;
   uint32_t bad = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int idx = begin + tid + 256 * j;
-    x[j] = -INFINITY;
-    if (idx < end) {
-      const float v = z[idx];
-      if (!isfinite(v)) {
-        bad = 1;
-      } else {
-        x[j] = v;
-        if (v > t1) {
-          t2 = t1;
-          t1 = v;
-        } else if (v > t2) {
-          t2 = v;
-        }
-      }
-    }
+    const bool in = begin + tid + 256 * j < end;
+    const bool fin = isfinite(x[j]);
+    bad |= (in && !fin) ? 1u : 0u;
+    x[j] = (in && fin) ? x[j] : -INFINITY;
+    t2 = fmaxf(t2, fminf(t1, x[j]));
+    t1 = fmaxf(t1, x[j]);
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float o1 = __shfl_xor(t1, o, 64), o2 = __shfl_xor(t2, o, 64);
@@ -231,12 +264,10 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
   if (M > -INFINITY) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      if (x[j] > -INFINITY) {
-        const float dz = x[j] - M;
-        const float e = expf(dz);
-        S += (double)e;
-        T += (double)e * (double)dz;
-      }
+      const float dz = x[j] - M;
+      const float e = x[j] > -INFINITY ? expf(dz) : 0.0f;
+      S += (double)e;
+      T += e > 0.0f ? (double)e * (double)dz : 0.0;
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -276,15 +307,7 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
       const ConfPartial P = parts[c];
       badall |= P.nonfinite;
       top2_merge(a1, a2, P.m, P.top2);
-      // fold chunk c into this lane's running (m, S, T)
-      const double m2 = (double)P.m;
-      if (m2 > -INFINITY) {
-        const double mx = fmax(pm, m2);
-        const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(m2 - mx);
-        pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (P.T + (m2 - mx) * P.S);
-        pS = f1 * pS + f2 * P.S;
-        pm = mx;
-      }
+      mst_merge(pm, pS, pT, (double)P.m, P.S, P.T);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -292,13 +315,7 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
     top2_merge(a1, a2, o1, o2);
     badall |= __shfl_xor(badall, o, 64);
     const double qm = __shfl_xor(pm, o, 64), qS = __shfl_xor(pS, o, 64), qT = __shfl_xor(pT, o, 64);
-    if (qm > -INFINITY) {
-      const double mx = fmax(pm, qm);
-      const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(qm - mx);
-      pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (qT + (qm - mx) * qS);
-      pS = f1 * pS + f2 * qS;
-      pm = mx;
-    }
+    mst_merge(pm, pS, pT, qm, qS, qT);
   }
   if (lane != 0) return;
   const double Sx = pS, Tx = pT;
@@ -332,8 +349,11 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
 template <bool kLds>
 struct Stage {
   float* p;
-  int rs;  // row stride of a plane
+  int rs;  // row stride of a plane (a multiple of 32)
   __device__ __forceinline__ float& at(int plane, int i) const { return p[plane * rs + i]; }
+  __device__ __forceinline__ const float4& at4(int plane, int i) const {
+    return *reinterpret_cast<const float4*>(p + plane * rs + i);
+  }
   __device__ __forceinline__ uint64_t key(int i) const {
     return ((uint64_t)__builtin_bit_cast(uint32_t, p[rs + i]) << 32) | __builtin_bit_cast(uint32_t, p[i]);
   }
@@ -345,21 +365,22 @@ struct Stage {
 };
 
 // The e-th smallest key (e >= 1) over keys [0, rows): an 8-bit-digit radix
-// select from the most significant digit down.
+// select from the most significant digit down. Each wave counts into its own
+// histogram to spread the LDS atomics.
 template <bool kLds>
-__device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, uint32_t* hist, uint32_t* red,
+__device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, uint32_t* hist4, uint32_t* red,
                                  int32_t* sh) {
   uint64_t prefix = 0, mask = 0;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int w = 0; w < 4; ++w) hist4[w * 256 + tid] = 0;
     __syncthreads();
     for (int i = tid; i < rows; i += kThreads) {
       const uint64_t k = st.key(i);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      if ((k & mask) == prefix) atomicAdd(&hist4[wave * 256 + ((k >> shift) & 255u)], 1u);
     }
     __syncthreads();
-    const uint32_t cnt = hist[tid];
+    const uint32_t cnt = hist4[tid] + hist4[256 + tid] + hist4[512 + tid] + hist4[768 + tid];
     uint32_t total;
     const uint32_t excl = block_excl_scan_u32(cnt, red, &total);
     if (excl < e && e <= excl + cnt) {
@@ -376,39 +397,48 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
   return prefix;
 }
 
+// One workgroup per segment. Stage-row index space: old rows [0, n_old32)
+// (rows >= n_old are padding), ring slots [n_old32, n_old32 + Wr32).
 template <int D, int G, bool kLds>
-__global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fused_step_kernel(Layout lay, Params par, StepArgs a) {
-  constexpr int LPR = D / 16;          // lanes per row
-  constexpr int RPB = kThreads / LPR;  // rows per block iteration
+__global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Params par, StepArgs a) {
+  constexpr int LPR = D / 16;          // lanes per row for row-wise work
+  constexpr int RPB = kThreads / LPR;  // rows per block iteration for row-wise work
+  constexpr int KS = D / 32;           // MFMA k-steps over d
+  constexpr int NCB = D / 16;          // 16-column blocks of d
   constexpr int PL = G > 4 ? G : 4;    // staging planes
-  constexpr int U8 = 8;                // INT8 rows per lane in flight (16 B each)
-  constexpr int U16 = 4;               // FP16 rows per lane in flight (32 B each)
+  constexpr int NP8 = 4;               // 16-row INT8 K tiles in flight per wave
+  constexpr int NP16 = 2;              // 16-row FP16 K tiles in flight per wave
+  constexpr int NV8 = 2;               // 32-row INT8 V tiles in flight per wave
+  constexpr int NV16 = 1;              // 32-row FP16 V tiles in flight per wave
+  constexpr int KB = 4;                // rows per thread in flight in the key phase
   static_assert(LPR == 4 || LPR == 8, "head_dim 64 or 128");
+  static_assert(G <= 16, "a GQA group fits one MFMA tile");
 
   __shared__ float red_f[4][G];
   __shared__ uint32_t red_u[4];
   __shared__ uint64_t red_k[4];
   __shared__ float obuf[G * D];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist4[4 * 256];
   __shared__ int32_t sh[4];
+  __shared__ int32_t sh_out_live;
   extern __shared__ float dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rg = tid / LPR;
+  const int lq = lane >> 4, lj = lane & 15;  // MFMA lane coordinates
   const int seg = blockIdx.x;
-  const int h = seg % lay.Hkv, b = (seg / lay.Hkv) % lay.B, l = seg / (lay.Hkv * lay.B);
-  (void)h;
-  const int t = a.t, Wr = lay.Wr, ob = lay.old_bytes;
+  const int b = (seg / lay.Hkv) % lay.B, l = seg / (lay.Hkv * lay.B);
+  const int t = a.t, Wr = lay.Wr, Wr32 = lay.Wr32, ob = lay.old_bytes;
   const bool kvpop = par.policy == 1;
 
-  uint16_t* rk = lay.ring_k + (size_t)seg * Wr * D;
-  uint16_t* rv = lay.ring_v + (size_t)seg * Wr * D;
-  int32_t* rpos = lay.ring_pos + (size_t)seg * Wr;
-  float* rema = lay.ring_ema + (size_t)seg * Wr;
-  float* rprio = lay.ring_prio + (size_t)seg * Wr;
-  const size_t obase = (size_t)seg * lay.cap;
+  uint16_t* rk = lay.ring_k + (size_t)seg * Wr32 * D;
+  uint16_t* rvt = lay.ring_v + (size_t)seg * Wr32 * D;
+  int32_t* rpos = lay.ring_pos + (size_t)seg * Wr32;
+  float* rema = lay.ring_ema + (size_t)seg * Wr32;
+  float* rprio = lay.ring_prio + (size_t)seg * Wr32;
+  const size_t obase = (size_t)seg * lay.cap32;
   uint8_t* okp = lay.old_k + obase * D * ob;
-  uint8_t* ovp = lay.old_v + obase * D * ob;
+  uint8_t* ovt = lay.old_v + obase * D * ob;
   float* oks = lay.old_ks + obase;
   float* ovs = lay.old_vs + obase;
   int32_t* opos = lay.old_pos + obase;
@@ -416,7 +446,8 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
   float* oprio = lay.old_prio + obase;
 
   const int n_old = lay.seg_nold[seg];
-  const int rows = n_old + Wr;
+  const int n_old32 = (n_old + 31) & ~31;
+  const int rows = n_old32 + Wr32;
   Stage<kLds> st;
   if constexpr (kLds) {
     st.p = dyn_lds;
@@ -430,16 +461,29 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
     st.rs = lay.rows_max;
   }
 
+  // ---- q as MFMA A operands (row g = lane%16; zero rows g >= G). INT8 K tiles
+  // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
+  half8 qa8[KS], qa16[KS];
+  {
+    const uint16_t* qrow = a.q + ((size_t)seg * G + (lj < G ? lj : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
+      const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
+      qa8[kk] = lj < G ? as_h8(u8) : half8{};
+      qa16[kk] = lj < G ? as_h8(u16) : half8{};
+    }
+  }
+
   // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
   // previous row (pos t - Wr) left the window at the end of the last step.
   const int slot_new = t % Wr;
   {
-    const uint4* kn = reinterpret_cast<const uint4*>(a.k_new + (size_t)seg * D);
-    const uint4* vn = reinterpret_cast<const uint4*>(a.v_new + (size_t)seg * D);
+    const uint16_t* kn = a.k_new + (size_t)seg * D;
+    const uint16_t* vn = a.v_new + (size_t)seg * D;
     if (tid < D / 8)
-      reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn[tid];
-    else if (tid < D / 4)
-      reinterpret_cast<uint4*>(rv + (size_t)slot_new * D)[tid - D / 8] = vn[tid - D / 8];
+      reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = reinterpret_cast<const uint4*>(kn)[tid];
+    if (tid < D) rvt[vt16(slot_new, tid, D)] = vn[tid];
     if (tid == 0) {
       rpos[slot_new] = t;
       rema[slot_new] = 0.0f;
@@ -451,138 +495,162 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
         const int sl = pl % Wr;
         if (rpos[sl] == pl) rprio[sl] = a.prio_new[seg];
       }
+      sh_out_live = 0;
     }
   }
   __syncthreads();
 
-  // ---- QK pass: s_gi = (q_g . k_i) * scale_i * sm_scale, staged per row.
-  h2 qh[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)seg * G + g) * D + c * 16);
-    const uint4 x0 = qp[0], x1 = qp[1];
-    qh[g][0] = as_h2(x0.x); qh[g][1] = as_h2(x0.y); qh[g][2] = as_h2(x0.z); qh[g][3] = as_h2(x0.w);
-    qh[g][4] = as_h2(x1.x); qh[g][5] = as_h2(x1.y); qh[g][6] = as_h2(x1.z); qh[g][7] = as_h2(x1.w);
-  }
+  // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
+  // lane (lq, lj) receives S[4*lq + r][row lj].
   const float sm = par.sm_scale;
-  float mloc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
-
+  float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float sv_max = 0.0f;
+  const int nt_old = n_old32 >> 4;
   if (par.old_int8) {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U8) {
-      uint4 kk[U8];
-      float sc[U8];
+    for (int t0 = wave; t0 < nt_old; t0 += 4 * NP8) {
+      uint4 k0[NP8], k1[NP8];
+      float sk[NP8], sv[NP8];
 #pragma unroll
-      for (int u = 0; u < U8; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          kk[u] = *reinterpret_cast<const uint4*>(okp + (size_t)i * D + c * 16);
-          sc[u] = oks[i];
+      for (int u = 0; u < NP8; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_old) {
+          const int row = 16 * tt + lj;
+          const uint8_t* kr = okp + (size_t)row * D;
+          k0[u] = *reinterpret_cast<const uint4*>(kr + 16 * lq);
+          if constexpr (D == 128) k1[u] = *reinterpret_cast<const uint4*>(kr + 16 * (lq + 4));
+          sk[u] = oks[row];
+          sv[u] = ovs[row];
         }
       }
 #pragma unroll
-      for (int u = 0; u < U8; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          h2 kh[8];
-          i8x4_to_h2(kk[u].x, kh[0], kh[1]);
-          i8x4_to_h2(kk[u].y, kh[2], kh[3]);
-          i8x4_to_h2(kk[u].z, kh[4], kh[5]);
-          i8x4_to_h2(kk[u].w, kh[6], kh[7]);
-          const float f = sc[u] * sm;
+      for (int u = 0; u < NP8; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_old) {
+          half8 b0, b1;
+          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+          i8x16_to_h8(k0[u], b0, b1);
+          acc = mfma16(qa8[0], b0, acc);
+          acc = mfma16(qa8[1], b1, acc);
+          if constexpr (D == 128) {
+            half8 b2, b3;
+            i8x16_to_h8(k1[u], b2, b3);
+            acc = mfma16(qa8[2], b2, acc);
+            acc = mfma16(qa8[3], b3, acc);
+          }
+          const int row = 16 * tt + lj;
+          const bool valid = row < n_old;
+          if (valid) sv_max = fmaxf(sv_max, sv[u]);
+          const float f = sk[u] * sm;
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_fdot2(kh[j], qh[g][j], acc, false);
-            const float s = group_sum<LPR>(acc) * f;
-            if (c == 0) st.at(g, i) = s;
-            mloc[g] = fmaxf(mloc[g], s);
+          for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            if (g < G) {
+              const float s = valid ? acc[r] * f : -INFINITY;
+              st.at(g, row) = s;
+              mloc[r] = fmaxf(mloc[r], s);
+            }
           }
         }
       }
     }
   } else {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U16) {
-      uint4 k0[U16], k1[U16];
+    for (int t0 = wave; t0 < nt_old; t0 += 4 * NP16) {
+      uint4 kc[NP16][KS];
 #pragma unroll
-      for (int u = 0; u < U16; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          const uint4* p = reinterpret_cast<const uint4*>(okp + ((size_t)i * D + c * 16) * 2);
-          k0[u] = p[0];
-          k1[u] = p[1];
+      for (int u = 0; u < NP16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_old) {
+          const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)(16 * tt + lj) * D;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) kc[u][kk] = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
         }
       }
 #pragma unroll
-      for (int u = 0; u < U16; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          const h2 kh[8] = {as_h2(k0[u].x), as_h2(k0[u].y), as_h2(k0[u].z), as_h2(k0[u].w),
-                            as_h2(k1[u].x), as_h2(k1[u].y), as_h2(k1[u].z), as_h2(k1[u].w)};
+      for (int u = 0; u < NP16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_old) {
+          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float acc = 0.0f;
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(kc[u][kk]), acc);
+          const int row = 16 * tt + lj;
+          const bool valid = row < n_old;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_fdot2(kh[j], qh[g][j], acc, false);
-            const float s = group_sum<LPR>(acc) * sm;
-            if (c == 0) st.at(g, i) = s;
-            mloc[g] = fmaxf(mloc[g], s);
+          for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            if (g < G) {
+              const float s = valid ? acc[r] * sm : -INFINITY;
+              st.at(g, row) = s;
+              mloc[r] = fmaxf(mloc[r], s);
+            }
           }
         }
       }
     }
   }
-  for (int r0 = rg; r0 < Wr; r0 += RPB * U16) {
-    uint4 k0[U16], k1[U16];
-    bool live[U16];
+  {
+    const int nt_ring = Wr32 >> 4;
+    for (int t0 = wave; t0 < nt_ring; t0 += 4 * NP16) {
+      uint4 kc[NP16][KS];
+      int32_t pr[NP16];
 #pragma unroll
-    for (int u = 0; u < U16; ++u) {
-      const int r = r0 + u * RPB;
-      live[u] = false;
-      if (r < Wr) {
-        live[u] = rpos[r] >= 0;
-        if (live[u]) {
-          const uint4* p = reinterpret_cast<const uint4*>(rk + (size_t)r * D + c * 16);
-          k0[u] = p[0];
-          k1[u] = p[1];
+      for (int u = 0; u < NP16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_ring) {
+          const int r = 16 * tt + lj;
+          const uint16_t* kr = rk + (size_t)r * D;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) kc[u][kk] = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
+          pr[u] = rpos[r];
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U16; ++u) {
-      const int r = r0 + u * RPB;
-      if (r < Wr) {
-        if (live[u]) {
-          const h2 kh[8] = {as_h2(k0[u].x), as_h2(k0[u].y), as_h2(k0[u].z), as_h2(k0[u].w),
-                            as_h2(k1[u].x), as_h2(k1[u].y), as_h2(k1[u].z), as_h2(k1[u].w)};
+      for (int u = 0; u < NP16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nt_ring) {
+          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float acc = 0.0f;
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(kc[u][kk]), acc);
+          const int r = 16 * tt + lj;
+          const bool valid = r < Wr && pr[u] >= 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_fdot2(kh[j], qh[g][j], acc, false);
-            const float s = group_sum<LPR>(acc) * sm;
-            if (c == 0) st.at(g, n_old + r) = s;
-            mloc[g] = fmaxf(mloc[g], s);
+          for (int rr = 0; rr < 4; ++rr) {
+            const int g = 4 * lq + rr;
+            if (g < G) {
+              const float s = valid ? acc[rr] * sm : -INFINITY;
+              st.at(g, n_old32 + r) = s;
+              mloc[rr] = fmaxf(mloc[rr], s);
+            }
           }
-        } else if (c == 0) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) st.at(g, n_old + r) = -INFINITY;
         }
       }
     }
   }
+  // row maxima: reduce over the 16 lanes of each lane group, then over waves
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float v = wave_max(mloc[g]);
-    if (lane == 0) red_f[wave][g] = v;
+  for (int r = 0; r < 4; ++r) {
+    float v = mloc[r];
+    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int g = 4 * lq + r;
+    if (lj == 0 && g < G) red_f[wave][g] = v;
   }
+  sv_max = wave_max(sv_max);
+  if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
   __syncthreads();
   float M[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) M[g] = fmaxf(fmaxf(red_f[0][g], red_f[1][g]), fmaxf(red_f[2][g], red_f[3][g]));
+  float svm = 0.0f;
+  for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
   __syncthreads();
+  // PV weights are prescaled by a power of two that keeps p*sV*f below 2^14
+  // (fp16 range) while lifting small weights out of the fp16 subnormals.
+  int fexp = 10;
+  if (svm > 0.0f) {
+    int e2;
+    frexpf(svm, &e2);
+    fexp = min(10, max(-30, 14 - e2));
+  }
+  const float fscale = ldexpf(1.0f, fexp), finv = ldexpf(1.0f, -fexp);
 
   // ---- p_gi = exp(s_gi - M_g) in place; l_g = sum_i p_gi.
   float lsum[G];
@@ -609,182 +677,200 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
     inv_l[g] = 1.0f / Lsum[g];
   }
 
-  // ---- PV pass: acc_g += p_gi * v-hat_i. INT8 rows fold the V scale into
-  // the weight and use biased-unsigned codes (u = code + 128); the bias is
-  // removed once at the end: sum w (u - 128) = sum w u - 128 sum w.
-  float acc[G][16];
-  float bias[G];
+  // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
+  // with A = w as an fp16 hi + lo pair (about 22 significant bits) and B = V
+  // from the transposed tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj].
+  // INT8 tiles fold the V scale into w = p * sV * f.
+  floatx4 O[NCB];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    bias[g] = 0.0f;
+  for (int cb = 0; cb < NCB; ++cb) O[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto weights = [&](int srow, const float* sv8, half8& ahi, half8& alo) {
+    float w[8];
+    if (lj < G) {
+      const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
+      const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[g][e] = 0.0f;
-  }
+      for (int e = 0; e < 8; ++e) w[e] = pp[e] > 0.0f ? pp[e] * (sv8 ? sv8[e] * fscale : fscale) : 0.0f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 hi = (_Float16)w[e];
+      ahi[e] = hi;
+      alo[e] = (_Float16)(w[e] - (float)hi);
+    }
+  };
+  const int nv_old = n_old32 >> 5;
   if (par.old_int8) {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U8) {
-      uint4 vv[U8];
-      float sc[U8];
+    for (int t0 = wave; t0 < nv_old; t0 += 4 * NV8) {
+      uint4 vw[NV8][NCB / 2];
+      float4 s0[NV8], s1[NV8];
 #pragma unroll
-      for (int u = 0; u < U8; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          vv[u] = *reinterpret_cast<const uint4*>(ovp + (size_t)i * D + c * 16);
-          sc[u] = ovs[i];
+      for (int u = 0; u < NV8; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_old) {
+          const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
+#pragma unroll
+          for (int k = 0; k < NCB / 2; ++k) vw[u][k] = *reinterpret_cast<const uint4*>(tb + 1024 * k);
+          s0[u] = *reinterpret_cast<const float4*>(ovs + 32 * tt + 8 * lq);
+          s1[u] = *reinterpret_cast<const float4*>(ovs + 32 * tt + 8 * lq + 4);
         }
       }
 #pragma unroll
-      for (int u = 0; u < U8; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          const uint32_t w4[4] = {vv[u].x ^ 0x80808080u, vv[u].y ^ 0x80808080u, vv[u].z ^ 0x80808080u,
-                                  vv[u].w ^ 0x80808080u};
-          float f[16];
+      for (int u = 0; u < NV8; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_old) {
+          const float sv8[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+          half8 ahi, alo;
+          weights(32 * tt + 8 * lq, sv8, ahi, alo);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) f[e] = (float)((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float w = st.at(g, i) * sc[u];
-            bias[g] += w;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[g][e] = fmaf(w, f[e], acc[g][e]);
+          for (int k = 0; k < NCB / 2; ++k) {
+            half8 blo, bhi;
+            i8x16_to_h8(vw[u][k], blo, bhi);
+            O[2 * k] = mfma16(ahi, blo, O[2 * k]);
+            O[2 * k] = mfma16(alo, blo, O[2 * k]);
+            O[2 * k + 1] = mfma16(ahi, bhi, O[2 * k + 1]);
+            O[2 * k + 1] = mfma16(alo, bhi, O[2 * k + 1]);
           }
         }
       }
     }
   } else {
-    for (int i0 = rg; i0 < n_old; i0 += RPB * U16) {
-      uint4 v0[U16], v1[U16];
+    for (int t0 = wave; t0 < nv_old; t0 += 4 * NV16) {
+      uint4 vw[NV16][NCB];
 #pragma unroll
-      for (int u = 0; u < U16; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          const uint4* p = reinterpret_cast<const uint4*>(ovp + ((size_t)i * D + c * 16) * 2);
-          v0[u] = p[0];
-          v1[u] = p[1];
+      for (int u = 0; u < NV16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_old) {
+          const uint16_t* tb = reinterpret_cast<const uint16_t*>(ovt) + (size_t)tt * 32 * D + 8 * lane;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) vw[u][cb] = *reinterpret_cast<const uint4*>(tb + 512 * cb);
         }
       }
 #pragma unroll
-      for (int u = 0; u < U16; ++u) {
-        const int i = i0 + u * RPB;
-        if (i < n_old) {
-          const uint32_t w8[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
-          float f[16];
+      for (int u = 0; u < NV16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_old) {
+          half8 ahi, alo;
+          weights(32 * tt + 8 * lq, nullptr, ahi, alo);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            f[2 * j] = half_lo(w8[j]);
-            f[2 * j + 1] = half_hi(w8[j]);
-          }
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float w = st.at(g, i);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[g][e] = fmaf(w, f[e], acc[g][e]);
+          for (int cb = 0; cb < NCB; ++cb) {
+            O[cb] = mfma16(ahi, as_h8(vw[u][cb]), O[cb]);
+            O[cb] = mfma16(alo, as_h8(vw[u][cb]), O[cb]);
           }
         }
       }
     }
   }
-  for (int r0 = rg; r0 < Wr; r0 += RPB * U16) {
-    uint4 v0[U16], v1[U16];
-    bool live[U16];
+  {
+    const int nv_ring = Wr32 >> 5;
+    for (int t0 = wave; t0 < nv_ring; t0 += 4 * NV16) {
+      uint4 vw[NV16][NCB];
 #pragma unroll
-    for (int u = 0; u < U16; ++u) {
-      const int r = r0 + u * RPB;
-      live[u] = false;
-      if (r < Wr) {
-        live[u] = rpos[r] >= 0;
-        if (live[u]) {
-          const uint4* p = reinterpret_cast<const uint4*>(rv + (size_t)r * D + c * 16);
-          v0[u] = p[0];
-          v1[u] = p[1];
+      for (int u = 0; u < NV16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_ring) {
+          const uint16_t* tb = rvt + (size_t)tt * 32 * D + 8 * lane;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) vw[u][cb] = *reinterpret_cast<const uint4*>(tb + 512 * cb);
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U16; ++u) {
-      const int r = r0 + u * RPB;
-      if (r < Wr && live[u]) {
-        const uint32_t w8[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
-        float f[16];
+      for (int u = 0; u < NV16; ++u) {
+        const int tt = t0 + 4 * u;
+        if (tt < nv_ring) {
+          half8 ahi, alo;
+          weights(n_old32 + 32 * tt + 8 * lq, nullptr, ahi, alo);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          f[2 * j] = half_lo(w8[j]);
-          f[2 * j + 1] = half_hi(w8[j]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float w = st.at(g, n_old + r);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[g][e] = fmaf(w, f[e], acc[g][e]);
+          for (int cb = 0; cb < NCB; ++cb) {
+            O[cb] = mfma16(ahi, as_h8(vw[u][cb]), O[cb]);
+            O[cb] = mfma16(alo, as_h8(vw[u][cb]), O[cb]);
+          }
         }
       }
     }
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = fmaf(-128.0f, bias[g], acc[g][e]);
-      for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[g][e] = v;
-    }
-  }
-  // Lanes 0..LPR-1 of each wave hold the wave's sums; add the waves in order.
+  // add the four waves' partial outputs in order (deterministic), then scale
   for (int w = 0; w < 4; ++w) {
-    if (wave == w && lane < LPR) {
+    if (wave == w) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int idx = g * D + lane * 16 + e;
-          obuf[idx] = (w == 0 ? 0.0f : obuf[idx]) + acc[g][e];
+        for (int r = 0; r < 4; ++r) {
+          const int g = 4 * lq + r;
+          if (g < G) {
+            const int idx = g * D + 16 * cb + lj;
+            obuf[idx] = (w == 0 ? 0.0f : obuf[idx]) + O[cb][r];
+          }
         }
       }
     }
     __syncthreads();
   }
   for (int idx = tid; idx < G * D; idx += kThreads)
-    a.out[(size_t)seg * G * D + idx] = f2h(obuf[idx] * inv_l[idx / D]);
+    a.out[(size_t)seg * G * D + idx] = f2h(obuf[idx] * finv * inv_l[idx / D]);
 
   // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
   // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
   // Keys overwrite planes 0/1 of the row just read (same thread).
   uint32_t n_live = 0, n_elig = 0;
-  const float inv_t1 = 1.0f;  // (kept explicit below: IEEE division per row)
-  (void)inv_t1;
-  for (int i = tid; i < rows; i += kThreads) {
-    const bool in_old = i < n_old;
-    const int r = i - n_old;
-    const int32_t pos = in_old ? opos[i] : rpos[r];
-    uint64_t key = ~0ull;
-    float score = NAN;
-    if (pos >= 0) {
-      ++n_live;
-      if (!kvpop) {
-        float mass = 0.0f;
+  const int pos_out = t - lay.W;
+  for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
+    int32_t pos[KB];
+    float ev[KB];
 #pragma unroll
-        for (int g = 0; g < G; ++g) mass = fmaf(st.at(g, i), inv_l[g], mass);
-        mass *= (1.0f / (float)G);
-        float* ep = in_old ? (oema + i) : (rema + r);
-        const float e = par.beta * (*ep) + (1.0f - par.beta) * mass;
-        *ep = e;
-        const float rec = (float)(pos + 1) / (float)(t + 1);
-        score = par.alpha * e + (1.0f - par.alpha) * rec;
-      } else {
-        score = in_old ? oprio[i] : rprio[r];
-      }
-      const bool elig = pos >= par.s && pos <= t - par.P;
-      if (!isfinite(score)) {
-        atomicOr(lay.err, kErrNonFinite);
-      } else if (elig) {
-        key = rank_key(score, pos);
-        ++n_elig;
+    for (int u = 0; u < KB; ++u) {
+      const int i = i0 + kThreads * u;
+      pos[u] = -1;
+      ev[u] = 0.0f;
+      if (i < n_old) {
+        pos[u] = opos[i];
+        ev[u] = kvpop ? oprio[i] : oema[i];
+      } else if (i >= n_old32 && i < rows && i - n_old32 < Wr) {
+        pos[u] = rpos[i - n_old32];
+        ev[u] = kvpop ? rprio[i - n_old32] : rema[i - n_old32];
       }
     }
-    st.set_key(i, key);
-    if (par.record) {
-      lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
-      lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int i = i0 + kThreads * u;
+      if (i < rows) {
+        uint64_t key = ~0ull;
+        float score = NAN;
+        if (pos[u] >= 0) {
+          ++n_live;
+          if (!kvpop) {
+            float mass = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) mass = fmaf(st.at(g, i), inv_l[g], mass);
+            mass *= (1.0f / (float)G);
+            const float e = par.beta * ev[u] + (1.0f - par.beta) * mass;
+            if (i < n_old)
+              oema[i] = e;
+            else
+              rema[i - n_old32] = e;
+            const float rec = (float)(pos[u] + 1) / (float)(t + 1);
+            score = par.alpha * e + (1.0f - par.alpha) * rec;
+          } else {
+            score = ev[u];
+          }
+          const bool elig = pos[u] >= par.s && pos[u] <= t - par.P;
+          if (!isfinite(score)) {
+            atomicOr(lay.err, kErrNonFinite);
+          } else if (elig) {
+            key = rank_key(score, pos[u]);
+            ++n_elig;
+          }
+          if (pos[u] == pos_out && i >= n_old32) sh_out_live = 1;
+        }
+        st.set_key(i, key);
+        if (par.record) {
+          lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos[u];
+          lay.rec_score[(size_t)seg * lay.rows_max + i] = pos[u] >= 0 ? score : NAN;
+        }
+      }
     }
   }
   n_live = block_sum_u32(n_live, red_u);
@@ -805,15 +891,15 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
   uint64_t T = 0;  // victims: key <= T (no key is 0)
   if (e > 0 && e <= 8) {
     for (uint32_t r = 0; r < e; ++r) {
-      uint64_t m = ~0ull;
+      uint64_t mk = ~0ull;
       for (int i = tid; i < rows; i += kThreads) {
         const uint64_t k = st.key(i);
-        if (k > T && k < m) m = k;
+        if (k > T && k < mk) mk = k;
       }
-      T = block_min_u64(m, red_k);
+      T = block_min_u64(mk, red_k);
     }
   } else if (e > 8) {
-    T = radix_select(st, rows, e, hist, red_u, sh);
+    T = radix_select(st, rows, e, hist4, red_u, sh);
   }
 
   // ---- compaction of the old region: victims below the new count m become
@@ -848,12 +934,17 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
     for (int r = rg; r < (int)nh; r += RPB) {
       const int src = srcs[r], dst = holes[r];
       const size_t rb = (size_t)D * ob;
-      const int cb = 16 * ob;  // bytes per lane
-      for (int off = 0; off < cb; off += 16) {
-        *reinterpret_cast<uint4*>(okp + dst * rb + c * cb + off) =
-            *reinterpret_cast<const uint4*>(okp + src * rb + c * cb + off);
-        *reinterpret_cast<uint4*>(ovp + dst * rb + c * cb + off) =
-            *reinterpret_cast<const uint4*>(ovp + src * rb + c * cb + off);
+      const int cbytes = 16 * ob;  // bytes per lane
+      for (int off = 0; off < cbytes; off += 16)
+        *reinterpret_cast<uint4*>(okp + dst * rb + c * cbytes + off) =
+            *reinterpret_cast<const uint4*>(okp + src * rb + c * cbytes + off);
+      if (ob == 1) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) ovt[vt8(dst, 16 * c + jj, D)] = ovt[vt8(src, 16 * c + jj, D)];
+      } else {
+        uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) v16[vt16(dst, 16 * c + jj, D)] = v16[vt16(src, 16 * c + jj, D)];
       }
       if (c == 0) {
         opos[dst] = opos[src];
@@ -866,43 +957,59 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
   }
   if (e > 0)
     for (int r = tid; r < Wr; r += kThreads)
-      if (st.key(n_old + r) <= T) rpos[r] = -1;
+      if (st.key(n_old32 + r) <= T) rpos[r] = -1;
   __syncthreads();
 
   // ---- age-out: the row at t - W leaves the FP16 window; if it survived it
   // is appended to the old region, quantized when old rows are INT8.
   int n_old_new = m;
   bool aged = false;
-  const int pos_out = t - lay.W;
-  if (pos_out >= 0 && wave == 0) {
+  if (pos_out >= 0) {
     const int slot = pos_out % Wr;
-    const bool alive = rpos[slot] == pos_out;
+    const bool alive = sh_out_live && st.key(n_old32 + slot) > T;
     if (alive) {
       if (m >= lay.cap) {
-        if (lane == 0) atomicOr(lay.err, kErrCapacity);
+        if (tid == 0) atomicOr(lay.err, kErrCapacity);
       } else {
-        if (lane < 2 * LPR) {
+        if (wave == 0 && lane < 2 * LPR) {
           const bool isv = lane >= LPR;
           const int cc = lane % LPR;
-          const uint16_t* src = (isv ? rv : rk) + (size_t)slot * D + cc * 16;
-          uint8_t* dst = (isv ? ovp : okp) + (size_t)m * D * ob;
-          if (par.old_int8) {
-            quantize16<LPR>(src, dst + cc * 16, (isv ? ovs : oks) + m, cc == 0);
+          float x[16];
+          if (!isv) {
+            load16h(rk + (size_t)slot * D + cc * 16, x);
           } else {
-            const uint4* s4 = reinterpret_cast<const uint4*>(src);
-            uint4* d4 = reinterpret_cast<uint4*>(dst + cc * 32);
-            d4[0] = s4[0];
-            d4[1] = s4[1];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) x[jj] = h2f(rvt[vt16(slot, 16 * cc + jj, D)]);
+          }
+          if (par.old_int8) {
+            int8_t codes[16];
+            const float scale = quantize16<LPR>(x, codes);
+            if (!isv) {
+              *reinterpret_cast<uint4*>(okp + (size_t)m * D + cc * 16) = pack16(codes);
+              if (cc == 0) oks[m] = scale;
+            } else {
+#pragma unroll
+              for (int jj = 0; jj < 16; ++jj) ovt[vt8(m, 16 * cc + jj, D)] = (uint8_t)codes[jj];
+              if (cc == 0) ovs[m] = scale;
+            }
+          } else {
+            if (!isv) {
+              const uint4* s4 = reinterpret_cast<const uint4*>(rk + (size_t)slot * D + cc * 16);
+              uint4* d4 = reinterpret_cast<uint4*>(okp + ((size_t)m * D + cc * 16) * 2);
+              d4[0] = s4[0];
+              d4[1] = s4[1];
+            } else {
+              uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
+#pragma unroll
+              for (int jj = 0; jj < 16; ++jj) v16[vt16(m, 16 * cc + jj, D)] = f2h(x[jj]);
+            }
+            if (cc == 0) (isv ? ovs : oks)[m] = 0.0f;
           }
         }
-        if (lane == 0) {
+        if (tid == 0) {
           opos[m] = pos_out;
           oema[m] = rema[slot];
           oprio[m] = rprio[slot];
-          if (!par.old_int8) {
-            oks[m] = 0.0f;
-            ovs[m] = 0.0f;
-          }
           rpos[slot] = -1;
         }
         aged = true;
@@ -914,11 +1021,11 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
     lay.seg_nold[seg] = n_old_new;
     const uint64_t live_ring = (uint64_t)n_live - (uint64_t)n_old;
     const uint64_t old_row = par.old_int8 ? (uint64_t)(2 * D + 8) : (uint64_t)(4 * D);
-    uint64_t* sp = lay.seg_stats + (size_t)seg * kStatFields;
-    sp[0] += (uint64_t)n_old * old_row + live_ring * (uint64_t)(4 * D);
-    sp[1] += n_live;
-    sp[2] += moved + (aged ? 1u : 0u);
-    sp[3] += e;
+    unsigned long long* sp = reinterpret_cast<unsigned long long*>(lay.seg_stats + (size_t)seg * kStatFields);
+    atomicAdd(sp + 0, (unsigned long long)((uint64_t)n_old * old_row + live_ring * (uint64_t)(4 * D)));
+    atomicAdd(sp + 1, (unsigned long long)n_live);
+    atomicAdd(sp + 2, (unsigned long long)(moved + (aged ? 1u : 0u)));
+    atomicAdd(sp + 3, (unsigned long long)e);
     if (par.record) {
       int32_t* mp = lay.rec_meta + (size_t)seg * 4;
       mp[0] = rows;
@@ -932,73 +1039,100 @@ __global__ void __launch_bounds__(kThreads, (G <= 2 ? 4 : (G <= 4 ? 3 : 2))) fus
 }
 
 // ================================================================ init/ingest
-__global__ void init_meta_kernel(Layout lay, int32_t n_old_init) {
-  const int seg = blockIdx.x, tid = threadIdx.x;
-  for (int r = tid; r < lay.Wr; r += blockDim.x) {
-    lay.ring_pos[(size_t)seg * lay.Wr + r] = -1;
-    lay.ring_ema[(size_t)seg * lay.Wr + r] = 0.0f;
-    lay.ring_prio[(size_t)seg * lay.Wr + r] = 0.0f;
-  }
-  if (tid < kStatFields) lay.seg_stats[(size_t)seg * kStatFields + tid] = 0;
-  if (tid == 0) lay.seg_nold[seg] = n_old_init;
-  if (seg == 0) {
-    for (int i = tid; i < lay.B; i += blockDim.x) {
-      lay.row_counter[i] = 0;
-      lay.row_base[i] = 0;
-      lay.row_conf[i] = 0.0f;
-    }
-    if (tid == 0) *lay.err = 0;
-  }
+__global__ void zero_kernel(uint4* p, size_t n16) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) p[i] = z;
 }
 
-// Prefill row p of segment seg: pos <= P0-1-W goes to old row p (quantized when
-// old rows are INT8), the rest to ring slot p mod Wr.
+__global__ void init_meta_kernel(Layout lay, int32_t n_old_init) {
+  const int seg = blockIdx.x, tid = threadIdx.x;
+  for (int r = tid; r < lay.Wr32; r += blockDim.x) lay.ring_pos[(size_t)seg * lay.Wr32 + r] = -1;
+  if (tid == 0) lay.seg_nold[seg] = n_old_init;
+}
+
+// Prefill rows 32*blockIdx.x .. +31 of segment blockIdx.y. Rows with
+// pos <= P0-1-W go to old row pos (quantized when old rows are INT8), the rest
+// to ring slot pos mod Wr. Old V rows are assembled into their transposed tile
+// in LDS and written out in 16-byte chunks.
 template <int D>
 __global__ void __launch_bounds__(256) ingest_kernel(Layout lay, Params par, const uint16_t* pk, const uint16_t* pv,
                                                      int32_t P0) {
-  constexpr int LPR = D / 16, RPB = 256 / LPR;
-  const int seg = blockIdx.y, tid = threadIdx.x, c = tid % LPR;
-  const int p = blockIdx.x * RPB + tid / LPR;
-  if (p >= P0) return;  // whole lane groups leave together
+  constexpr int LPR = D / 16;
+  __shared__ uint16_t tile[32 * D];  // old V rows of this block, row-major (codes or halves)
+  const int seg = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x, c = tid % LPR, rr = tid / LPR;
   const int n_old_init = max(0, P0 - lay.W);
-  const uint16_t* ks = pk + ((size_t)seg * P0 + p) * D + c * 16;
-  const uint16_t* vs = pv + ((size_t)seg * P0 + p) * D + c * 16;
   const int ob = lay.old_bytes;
-  if (p < n_old_init) {
-    const size_t row = (size_t)seg * lay.cap + p;
-    uint8_t* dk = lay.old_k + row * D * ob;
-    uint8_t* dv = lay.old_v + row * D * ob;
-    if (par.old_int8) {
-      quantize16<LPR>(ks, dk + c * 16, lay.old_ks + row, c == 0);
-      quantize16<LPR>(vs, dv + c * 16, lay.old_vs + row, c == 0);
-    } else {
-      reinterpret_cast<uint4*>(dk + c * 32)[0] = reinterpret_cast<const uint4*>(ks)[0];
-      reinterpret_cast<uint4*>(dk + c * 32)[1] = reinterpret_cast<const uint4*>(ks)[1];
-      reinterpret_cast<uint4*>(dv + c * 32)[0] = reinterpret_cast<const uint4*>(vs)[0];
-      reinterpret_cast<uint4*>(dv + c * 32)[1] = reinterpret_cast<const uint4*>(vs)[1];
-      if (c == 0) {
-        lay.old_ks[row] = 0.0f;
-        lay.old_vs[row] = 0.0f;
+  const size_t obase = (size_t)seg * lay.cap32;
+  for (int i = tid; i < 32 * D; i += 256) tile[i] = 0;
+  __syncthreads();
+  const int p = 32 * blk + rr;
+  if (rr < 32 && p < P0) {  // whole lane groups share p
+    float xk[16], xv[16];
+    load16h(pk + ((size_t)seg * P0 + p) * D + c * 16, xk);
+    load16h(pv + ((size_t)seg * P0 + p) * D + c * 16, xv);
+    if (p < n_old_init) {
+      const size_t row = obase + p;
+      if (par.old_int8) {
+        int8_t ck[16], cv[16];
+        const float sk = quantize16<LPR>(xk, ck);
+        const float sv = quantize16<LPR>(xv, cv);
+        *reinterpret_cast<uint4*>(lay.old_k + row * D + c * 16) = pack16(ck);
+        uint8_t* t8 = reinterpret_cast<uint8_t*>(tile);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t8[rr * D + 16 * c + e] = (uint8_t)cv[e];
+        if (c == 0) {
+          lay.old_ks[row] = sk;
+          lay.old_vs[row] = sv;
+        }
+      } else {
+        uint16_t* dk = reinterpret_cast<uint16_t*>(lay.old_k) + row * D + c * 16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          dk[e] = f2h(xk[e]);
+          tile[rr * D + 16 * c + e] = f2h(xv[e]);
+        }
       }
+      if (c == 0) lay.old_pos[row] = p;
+    } else {
+      const int slot = p % lay.Wr;
+      uint16_t* dk = lay.ring_k + ((size_t)seg * lay.Wr32 + slot) * D + c * 16;
+      uint16_t* dv = lay.ring_v + (size_t)seg * lay.Wr32 * D;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dk[e] = f2h(xk[e]);
+        dv[vt16(slot, 16 * c + e, D)] = f2h(xv[e]);
+      }
+      if (c == 0) lay.ring_pos[(size_t)seg * lay.Wr32 + slot] = p;
     }
-    if (c == 0) {
-      lay.old_pos[row] = p;
-      lay.old_ema[row] = 0.0f;
-      lay.old_prio[row] = 0.0f;
-    }
-  } else {
-    const int slot = p % lay.Wr;
-    const size_t row = (size_t)seg * lay.Wr + slot;
-    uint4* dk = reinterpret_cast<uint4*>(lay.ring_k + row * D + c * 16);
-    uint4* dv = reinterpret_cast<uint4*>(lay.ring_v + row * D + c * 16);
-    dk[0] = reinterpret_cast<const uint4*>(ks)[0];
-    dk[1] = reinterpret_cast<const uint4*>(ks)[1];
-    dv[0] = reinterpret_cast<const uint4*>(vs)[0];
-    dv[1] = reinterpret_cast<const uint4*>(vs)[1];
-    if (c == 0) {
-      lay.ring_pos[row] = p;
-      lay.ring_ema[row] = 0.0f;
-      lay.ring_prio[row] = 0.0f;
+  }
+  __syncthreads();
+  if (32 * blk < n_old_init) {
+    if (ob == 1) {
+      // 16-byte chunk ch = 64*k + lane of the tile: columns 16*(2k) + j and
+      // 16*(2k+1) + j, rows 8q .. 8q+7 (lane = 16q + j)
+      const uint8_t* t8 = reinterpret_cast<const uint8_t*>(tile);
+      uint8_t* dst = lay.old_v + (obase + 32 * (size_t)blk) * D;
+      for (int ch = tid; ch < 2 * D; ch += 256) {
+        const int k = ch >> 6, ln = ch & 63, q = ln >> 4, j = ln & 15;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w[2 * h + (e >> 2)] |= (uint32_t)t8[(8 * q + e) * D + 16 * (2 * k + h) + j] << (8 * (e & 3));
+        reinterpret_cast<uint4*>(dst)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(lay.old_v) + (obase + 32 * (size_t)blk) * D;
+      for (int ch = tid; ch < 4 * D; ch += 256) {
+        const int cb = ch >> 6, ln = ch & 63, q = ln >> 4, j = ln & 15;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)tile[(8 * q + 2 * e) * D + 16 * cb + j] |
+                 ((uint32_t)tile[(8 * q + 2 * e + 1) * D + 16 * cb + j] << 16);
+        reinterpret_cast<uint4*>(dst)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 }
@@ -1013,10 +1147,10 @@ __global__ void __launch_bounds__(256) read_cache_kernel(Layout lay, int32_t seg
                                                          uint8_t* is8_o, int32_t old_int8) {
   const int si = blockIdx.y, seg = seg_first + si;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int D = lay.D, Wr = lay.Wr, ob = lay.old_bytes;
+  const int D = lay.D, Wr = lay.Wr;
   const int n_old = lay.seg_nold[seg];
-  const int32_t* opos = lay.old_pos + (size_t)seg * lay.cap;
-  const int32_t* rpos = lay.ring_pos + (size_t)seg * Wr;
+  const int32_t* opos = lay.old_pos + (size_t)seg * lay.cap32;
+  const int32_t* rpos = lay.ring_pos + (size_t)seg * lay.Wr32;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     int live = 0;
     for (int r = 0; r < Wr; ++r) live += rpos[r] >= 0;
@@ -1024,7 +1158,8 @@ __global__ void __launch_bounds__(256) read_cache_kernel(Layout lay, int32_t seg
   }
   if (i >= n_old + Wr) return;
   const bool in_old = i < n_old;
-  const int32_t pos = in_old ? opos[i] : rpos[i - n_old];
+  const int row = in_old ? i : i - n_old;
+  const int32_t pos = in_old ? opos[row] : rpos[row];
   if (pos < 0) return;
   int rank = 0;
   if (in_old) {
@@ -1037,30 +1172,30 @@ __global__ void __launch_bounds__(256) read_cache_kernel(Layout lay, int32_t seg
   const bool row8 = in_old && old_int8;
   if (pos_o) pos_o[orow] = pos;
   if (is8_o) is8_o[orow] = row8 ? 1 : 0;
-  const size_t src = in_old ? (size_t)seg * lay.cap + i : (size_t)seg * Wr + (i - n_old);
+  const size_t src = in_old ? (size_t)seg * lay.cap32 + row : (size_t)seg * lay.Wr32 + row;
   if (ema_o) ema_o[orow] = in_old ? lay.old_ema[src] : lay.ring_ema[src];
   if (prio_o) prio_o[orow] = in_old ? lay.old_prio[src] : lay.ring_prio[src];
   if (ks_o) ks_o[orow] = row8 ? lay.old_ks[src] : 0.0f;
   if (vs_o) vs_o[orow] = row8 ? lay.old_vs[src] : 0.0f;
+  const size_t vbase = (in_old ? (size_t)seg * lay.cap32 : (size_t)seg * lay.Wr32) * D;
   for (int e = 0; e < D; ++e) {
     uint16_t hk = 0, hv = 0;
     int8_t ck = 0, cv = 0;
     if (row8) {
       ck = (int8_t)lay.old_k[src * D + e];
-      cv = (int8_t)lay.old_v[src * D + e];
+      cv = (int8_t)lay.old_v[vbase + vt8(row, e, D)];
     } else if (in_old) {
       hk = reinterpret_cast<const uint16_t*>(lay.old_k)[src * D + e];
-      hv = reinterpret_cast<const uint16_t*>(lay.old_v)[src * D + e];
+      hv = reinterpret_cast<const uint16_t*>(lay.old_v)[vbase + vt16(row, e, D)];
     } else {
       hk = lay.ring_k[src * D + e];
-      hv = lay.ring_v[src * D + e];
+      hv = lay.ring_v[vbase + vt16(row, e, D)];
     }
     if (k16) k16[orow * D + e] = hk;
     if (v16) v16[orow * D + e] = hv;
     if (k8) k8[orow * D + e] = ck;
     if (v8) v8[orow * D + e] = cv;
   }
-  (void)ob;
 }
 
 __global__ void __launch_bounds__(256) stats_total_kernel(Layout lay, int32_t reset) {
@@ -1084,15 +1219,17 @@ __global__ void __launch_bounds__(256) stats_total_kernel(Layout lay, int32_t re
 // ================================================================ launchers
 static inline int ok_or_err() { return hipGetLastError() == hipSuccess ? 0 : -3; }
 
-int launch_init(const Layout& lay, const Params& par, const uint16_t* pk, const uint16_t* pv, int32_t P0,
-                void* stream) {
+int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
+                const uint16_t* pv, int32_t P0, void* stream) {
   hipStream_t s = (hipStream_t)stream;
+  const size_t n16 = state_bytes / 16;
+  hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<uint4*>(state), n16);
+  if (hipGetLastError() != hipSuccess) return -3;
   const int32_t n_old_init = P0 > lay.W ? P0 - lay.W : 0;
   hipLaunchKernelGGL(init_meta_kernel, dim3(lay.S), dim3(256), 0, s, lay, n_old_init);
   if (hipGetLastError() != hipSuccess) return -3;
   if (P0 > 0) {
-    const int rpb = 256 / (lay.D / 16);
-    const dim3 grid((P0 + rpb - 1) / rpb, lay.S);
+    const dim3 grid((P0 + 31) / 32, lay.S);
     if (lay.D == 64)
       hipLaunchKernelGGL(ingest_kernel<64>, grid, dim3(256), 0, s, lay, par, pk, pv, P0);
     else

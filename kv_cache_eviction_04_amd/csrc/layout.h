@@ -8,8 +8,17 @@
 //   old   — rows older than the window, densely packed in [0, n_old) in no
 //           particular order: INT8 codes + fp32 absmax scales (old_int8) or
 //           FP16. Every old position is below every ring position.
+// Row counts are padded to multiples of 32 (cap32, Wr32); padding rows stay
+// finite (zeroed at init) and are masked out of every computation.
+// K is stored row-major ([row][d]). V is stored in 32-row transposed tiles so
+// that one 16-byte load per lane is one MFMA B-operand slice (8 consecutive
+// rows of one column) and a wave's load covers 1 KiB of contiguous memory:
+// inside a tile, element (row r, column c), with q = r/8, e = r%8,
+// cb = c/16, j = c%16, lives at
+//   INT8: 1024*(cb/2) + 16*(16q + j) + 8*(cb%2) + e   bytes
+//   FP16:  512*cb     +  8*(16q + j) + e              halves
 // All arrays are segment-major structure-of-arrays; each array base is
-// 256-byte aligned and every K/V row starts on a 64-byte boundary.
+// 256-byte aligned.
 #pragma once
 #include <stdint.h>
 
@@ -33,24 +42,26 @@ struct Layout {
   int32_t cap;        // old rows per segment
   int32_t W;          // FP16 window (rows with pos > t - W stay in the ring)
   int32_t Wr;         // ring slots = W + 1
-  int32_t rows_max;   // cap + Wr: staged rows per segment upper bound
+  int32_t cap32;      // cap rounded up to 32
+  int32_t Wr32;       // Wr rounded up to 32
+  int32_t rows_max;   // cap32 + Wr32: staged rows per segment upper bound
   int32_t planes;     // staging planes per segment = max(G, 4)
   int32_t chunks;     // logits chunks per batch row
   int32_t old_bytes;  // bytes per element of an old row (1 int8, 2 fp16)
   // ring
-  uint16_t* ring_k;   // [S][Wr][D]
-  uint16_t* ring_v;
-  int32_t* ring_pos;  // [S][Wr]
-  float* ring_ema;    // [S][Wr]
-  float* ring_prio;   // [S][Wr]
+  uint16_t* ring_k;   // [S][Wr32][D] row-major
+  uint16_t* ring_v;   // [S][Wr32/32] transposed FP16 tiles
+  int32_t* ring_pos;  // [S][Wr32]
+  float* ring_ema;    // [S][Wr32]
+  float* ring_prio;   // [S][Wr32]
   // old
-  uint8_t* old_k;     // [S][cap][D * old_bytes]
-  uint8_t* old_v;
-  float* old_ks;      // [S][cap] (old_int8)
+  uint8_t* old_k;     // [S][cap32][D * old_bytes] row-major
+  uint8_t* old_v;     // [S][cap32/32] transposed tiles
+  float* old_ks;      // [S][cap32] (old_int8)
   float* old_vs;
-  int32_t* old_pos;   // [S][cap]
-  float* old_ema;     // [S][cap]
-  float* old_prio;    // [S][cap]
+  int32_t* old_pos;   // [S][cap32]
+  float* old_ema;     // [S][cap32]
+  float* old_prio;    // [S][cap32]
   int32_t* seg_nold;  // [S]
   uint64_t* seg_stats;  // [S][kStatFields]
   float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
@@ -84,8 +95,8 @@ struct StepArgs {
 };
 
 // Launchers (kernels.hip). All enqueue on `stream` and return the launch status.
-int launch_init(const Layout& lay, const Params& par, const uint16_t* pk, const uint16_t* pv, int32_t P0,
-                void* stream);
+int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
+                const uint16_t* pv, int32_t P0, void* stream);
 int launch_conf_reduce(const Layout& lay, const Params& par, const float* logits, float* conf_out,
                        int32_t* budget_out, void* stream);
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,

@@ -40,7 +40,8 @@ def test_workloads_validate(name):
     L = confkv.lib()
     assert L.confkv_validate(ctypes.byref(c), w["prefill"]) == confkv.OK
     assert L.confkv_state_bytes(ctypes.byref(c)) > 0
-    assert L.confkv_rows_max(ctypes.byref(c)) == c.capacity + (c.protect_last if c.policy else c.fp16_window) + 1
+    r32 = lambda x: (x + 31) // 32 * 32
+    assert L.confkv_rows_max(ctypes.byref(c)) == r32(c.capacity) + r32((c.protect_last if c.policy else c.fp16_window) + 1)
 
 
 @pytest.mark.parametrize("field,value,code", [
