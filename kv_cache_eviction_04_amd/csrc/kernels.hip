@@ -346,6 +346,105 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
 }
 
 // ================================================== fused attend+evict step
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+// Tuning constants of the fused kernel (defaults measured on MI355X).
+#ifndef CONFKV_NT
+#define CONFKV_NT 0        // K/V tile loads marked non-temporal
+#endif
+#ifndef CONFKV_PIPE
+#define CONFKV_PIPE 0      // 0: load a batch, then compute it; 1: two-stage pipeline
+#endif
+#ifndef CONFKV_QK8_NPB
+#define CONFKV_QK8_NPB 4   // INT8 K tiles per batch
+#endif
+#ifndef CONFKV_QK16_NPB
+#define CONFKV_QK16_NPB 2  // FP16 K tiles per batch
+#endif
+#ifndef CONFKV_PV8_NPB
+#define CONFKV_PV8_NPB 8   // INT8 V tiles per batch
+#endif
+#ifndef CONFKV_PV16_NPB
+#define CONFKV_PV16_NPB 4  // FP16 V tiles per batch
+#endif
+#ifndef CONFKV_KB
+#define CONFKV_KB 6        // key-phase rows per thread loaded ahead
+#endif
+#ifndef CONFKV_OCC
+#define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 4)
+#endif
+// Streaming loads of K/V tiles: read once per step, so marked non-temporal.
+__device__ __forceinline__ uint4 ldnt4(const void* p) {
+#if CONFKV_NT
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 ldnt2(const void* p) {
+#if CONFKV_NT
+  const u2v v = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(p));
+  return make_uint2(v[0], v[1]);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
+}
+
+// Tile loop over [t0, t1) (uniform across the wavefront). Batched: issue the
+// loads of NPB tiles, then compute them. Two-stage: while one batch is
+// computed, the loads of the next are in flight (twice the registers).
+template <int NPB, class Buf, class LoadF, class CompF>
+__device__ __forceinline__ void pipelined(int t0, int t1, LoadF&& load, CompF&& comp) {
+  if (t0 >= t1) return;
+#if !CONFKV_PIPE
+  for (int base = t0; base < t1; base += NPB) {
+    Buf A[NPB];
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + u < t1) load(base + u, A[u]);
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + u < t1) comp(base + u, A[u]);
+  }
+  return;
+#endif
+  Buf A[NPB], B[NPB];
+#pragma unroll
+  for (int u = 0; u < NPB; ++u)
+    if (t0 + u < t1) load(t0 + u, A[u]);
+  for (int base = t0; base < t1; base += 2 * NPB) {
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + NPB + u < t1) load(base + NPB + u, B[u]);
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + u < t1) comp(base + u, A[u]);
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + 2 * NPB + u < t1) load(base + 2 * NPB + u, A[u]);
+#pragma unroll
+    for (int u = 0; u < NPB; ++u)
+      if (base + NPB + u < t1) comp(base + NPB + u, B[u]);
+  }
+}
+struct QK8Buf {
+  uint4 k0, k1;
+  float sk, sv;
+};
+template <int KS>
+struct QK16Buf {
+  uint4 kc[KS];
+  int32_t pr;
+};
+struct PV8Buf {
+  uint4 v;
+};
+template <int CBW>
+struct PV16Buf {
+  uint4 v[CBW];
+};
+
 template <bool kLds>
 struct Stage {
   float* p;
@@ -365,22 +464,21 @@ struct Stage {
 };
 
 // The e-th smallest key (e >= 1) over keys [0, rows): an 8-bit-digit radix
-// select from the most significant digit down. Each wave counts into its own
-// histogram to spread the LDS atomics.
+// select from the most significant digit down.
 template <bool kLds>
-__device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, uint32_t* hist4, uint32_t* red,
+__device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, uint32_t* hist, uint32_t* red,
                                  int32_t* sh) {
   uint64_t prefix = 0, mask = 0;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int w = 0; w < 4; ++w) hist4[w * 256 + tid] = 0;
+    hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < rows; i += kThreads) {
       const uint64_t k = st.key(i);
-      if ((k & mask) == prefix) atomicAdd(&hist4[wave * 256 + ((k >> shift) & 255u)], 1u);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    const uint32_t cnt = hist4[tid] + hist4[256 + tid] + hist4[512 + tid] + hist4[768 + tid];
+    const uint32_t cnt = hist[tid];
     uint32_t total;
     const uint32_t excl = block_excl_scan_u32(cnt, red, &total);
     if (excl < e && e <= excl + cnt) {
@@ -400,26 +498,26 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
 // One workgroup per segment. Stage-row index space: old rows [0, n_old32)
 // (rows >= n_old are padding), ring slots [n_old32, n_old32 + Wr32).
 template <int D, int G, bool kLds>
-__global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Params par, StepArgs a) {
+__global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_step_kernel(Layout lay, Params par, StepArgs a) {
   constexpr int LPR = D / 16;          // lanes per row for row-wise work
   constexpr int RPB = kThreads / LPR;  // rows per block iteration for row-wise work
   constexpr int KS = D / 32;           // MFMA k-steps over d
   constexpr int NCB = D / 16;          // 16-column blocks of d
   constexpr int PL = G > 4 ? G : 4;    // staging planes
+  constexpr int CBW = NCB / 4;         // PV column blocks per wave (waves split d)
   constexpr int NP8 = 4;               // 16-row INT8 K tiles in flight per wave
   constexpr int NP16 = 2;              // 16-row FP16 K tiles in flight per wave
-  constexpr int NV8 = 2;               // 32-row INT8 V tiles in flight per wave
-  constexpr int NV16 = 1;              // 32-row FP16 V tiles in flight per wave
-  constexpr int KB = 4;                // rows per thread in flight in the key phase
+  constexpr int NV8 = 8;               // 32-row INT8 V tiles in flight per wave
+  constexpr int NV16 = 4;              // 32-row FP16 V tiles in flight per wave
+  constexpr int KB = CONFKV_KB;        // rows per thread in flight in the key phase
   static_assert(LPR == 4 || LPR == 8, "head_dim 64 or 128");
   static_assert(G <= 16, "a GQA group fits one MFMA tile");
 
-  __shared__ float red_f[4][G];
+  __shared__ float red_m[4][G], red_l[4][G];
   __shared__ uint32_t red_u[4];
   __shared__ uint64_t red_k[4];
-  __shared__ float obuf[G * D];
-  __shared__ uint32_t hist4[4 * 256];
-  __shared__ int32_t sh[4];
+  __shared__ uint32_t hist[256];
+  __shared__ int32_t sh[8];
   __shared__ int32_t sh_out_live;
   extern __shared__ float dyn_lds[];
 
@@ -463,21 +561,27 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
 
   // ---- q as MFMA A operands (row g = lane%16; zero rows g >= G). INT8 K tiles
   // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
+  const uint16_t* qrow = a.q + ((size_t)seg * G + (lj < G ? lj : 0)) * D;
   half8 qa8[KS], qa16[KS];
-  {
-    const uint16_t* qrow = a.q + ((size_t)seg * G + (lj < G ? lj : 0)) * D;
+  auto load_qa16 = [&]() {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
       const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-      qa8[kk] = lj < G ? as_h8(u8) : half8{};
       qa16[kk] = lj < G ? as_h8(u16) : half8{};
     }
+  };
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
+    qa8[kk] = lj < G ? as_h8(u8) : half8{};
   }
 
   // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
   // previous row (pos t - Wr) left the window at the end of the last step.
+  // The barrier that publishes it comes after the old-region QK, which does
+  // not read the ring.
   const int slot_new = t % Wr;
+  const int pos_out = t - lay.W;
   {
     const uint16_t* kn = a.k_new + (size_t)seg * D;
     const uint16_t* vn = a.v_new + (size_t)seg * D;
@@ -498,150 +602,160 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
       sh_out_live = 0;
     }
   }
-  __syncthreads();
 
   // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
-  // lane (lq, lj) receives S[4*lq + r][row lj].
+  // lane (lq, lj) receives S[4*lq + r][row lj]. Each wave takes a contiguous
+  // share of the tiles, stages s in LDS and keeps a running max per head.
   const float sm = par.sm_scale;
-  float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float sv_max = 0.0f;
   const int nt_old = n_old32 >> 4;
-  if (par.old_int8) {
-    for (int t0 = wave; t0 < nt_old; t0 += 4 * NP8) {
-      uint4 k0[NP8], k1[NP8];
-      float sk[NP8], sv[NP8];
-#pragma unroll
-      for (int u = 0; u < NP8; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_old) {
-          const int row = 16 * tt + lj;
-          const uint8_t* kr = okp + (size_t)row * D;
-          k0[u] = *reinterpret_cast<const uint4*>(kr + 16 * lq);
-          if constexpr (D == 128) k1[u] = *reinterpret_cast<const uint4*>(kr + 16 * (lq + 4));
-          sk[u] = oks[row];
-          sv[u] = ovs[row];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NP8; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_old) {
-          half8 b0, b1;
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-          i8x16_to_h8(k0[u], b0, b1);
-          acc = mfma16(qa8[0], b0, acc);
-          acc = mfma16(qa8[1], b1, acc);
-          if constexpr (D == 128) {
-            half8 b2, b3;
-            i8x16_to_h8(k1[u], b2, b3);
-            acc = mfma16(qa8[2], b2, acc);
-            acc = mfma16(qa8[3], b3, acc);
-          }
-          const int row = 16 * tt + lj;
-          const bool valid = row < n_old;
-          if (valid) sv_max = fmaxf(sv_max, sv[u]);
-          const float f = sk[u] * sm;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int g = 4 * lq + r;
-            if (g < G) {
-              const float s = valid ? acc[r] * f : -INFINITY;
-              st.at(g, row) = s;
-              mloc[r] = fmaxf(mloc[r], s);
+  {
+    const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
+    if (par.old_int8) {
+      pipelined<CONFKV_QK8_NPB, QK8Buf>(
+          ta, tb,
+          [&](int tt, QK8Buf& bf) {
+            const int row = 16 * tt + lj;
+            const uint8_t* kr = okp + (size_t)row * D;
+            bf.k0 = ldnt4(kr + 16 * lq);
+            if constexpr (D == 128) bf.k1 = ldnt4(kr + 16 * (lq + 4));
+            bf.sk = oks[row];
+            bf.sv = ovs[row];
+          },
+          [&](int tt, const QK8Buf& bf) {
+            half8 b0, b1;
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            i8x16_to_h8(bf.k0, b0, b1);
+            acc = mfma16(qa8[0], b0, acc);
+            acc = mfma16(qa8[1], b1, acc);
+            if constexpr (D == 128) {
+              half8 b2, b3;
+              i8x16_to_h8(bf.k1, b2, b3);
+              acc = mfma16(qa8[2], b2, acc);
+              acc = mfma16(qa8[3], b3, acc);
             }
-          }
-        }
-      }
-    }
-  } else {
-    for (int t0 = wave; t0 < nt_old; t0 += 4 * NP16) {
-      uint4 kc[NP16][KS];
+            const int row = 16 * tt + lj;
+            const bool valid = row < n_old;
+            if (valid) sv_max = fmaxf(sv_max, bf.sv);
+            const float f = bf.sk * sm;
 #pragma unroll
-      for (int u = 0; u < NP16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_old) {
-          const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)(16 * tt + lj) * D;
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) kc[u][kk] = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NP16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_old) {
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(kc[u][kk]), acc);
-          const int row = 16 * tt + lj;
-          const bool valid = row < n_old;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int g = 4 * lq + r;
-            if (g < G) {
-              const float s = valid ? acc[r] * sm : -INFINITY;
-              st.at(g, row) = s;
-              mloc[r] = fmaxf(mloc[r], s);
+            for (int r = 0; r < 4; ++r) {
+              const int g = 4 * lq + r;
+              if (g < G) {
+                const float sc = valid ? acc[r] * f : -INFINITY;
+                st.at(g, row) = sc;
+                mrun[r] = fmaxf(mrun[r], sc);
+              }
             }
-          }
-        }
-      }
+          });
+    } else {
+      load_qa16();
+      pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+          ta, tb,
+          [&](int tt, QK16Buf<KS>& bf) {
+            const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)(16 * tt + lj) * D;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+          },
+          [&](int tt, const QK16Buf<KS>& bf) {
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
+            const int row = 16 * tt + lj;
+            const bool valid = row < n_old;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int g = 4 * lq + r;
+              if (g < G) {
+                const float sc = valid ? acc[r] * sm : -INFINITY;
+                st.at(g, row) = sc;
+                mrun[r] = fmaxf(mrun[r], sc);
+              }
+            }
+          });
     }
   }
+  __syncthreads();  // the appended ring row is visible from here on
+  if (par.old_int8) load_qa16();
   {
-    const int nt_ring = Wr32 >> 4;
-    for (int t0 = wave; t0 < nt_ring; t0 += 4 * NP16) {
-      uint4 kc[NP16][KS];
-      int32_t pr[NP16];
-#pragma unroll
-      for (int u = 0; u < NP16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_ring) {
+    const int nt_ring = (Wr + 15) >> 4;  // tiles wholly past slot Wr-1 are skipped
+    const int ta = (wave * nt_ring) >> 2, tb = ((wave + 1) * nt_ring) >> 2;
+    pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+        ta, tb,
+        [&](int tt, QK16Buf<KS>& bf) {
           const int r = 16 * tt + lj;
           const uint16_t* kr = rk + (size_t)r * D;
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) kc[u][kk] = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
-          pr[u] = rpos[r];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NP16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nt_ring) {
+          for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+          bf.pr = rpos[r];
+        },
+        [&](int tt, const QK16Buf<KS>& bf) {
           floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(kc[u][kk]), acc);
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
           const int r = 16 * tt + lj;
-          const bool valid = r < Wr && pr[u] >= 0;
+          const bool valid = r < Wr && bf.pr >= 0;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int g = 4 * lq + rr;
             if (g < G) {
-              const float s = valid ? acc[rr] * sm : -INFINITY;
-              st.at(g, n_old32 + r) = s;
-              mloc[rr] = fmaxf(mloc[rr], s);
+              const float sc = valid ? acc[rr] * sm : -INFINITY;
+              st.at(g, n_old32 + r) = sc;
+              mrun[rr] = fmaxf(mrun[rr], sc);
             }
           }
-        }
-      }
-    }
+        });
+    // ring slots past the last QK tile
+    for (int r = tid + 16 * nt_ring; r < Wr32; r += kThreads)
+#pragma unroll
+      for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
   }
-  // row maxima: reduce over the 16 lanes of each lane group, then over waves
+  // per-head maxima: over the 16 lanes of each lane group, then per wave
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float v = mloc[r];
-    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    float m = mrun[r];
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     const int g = 4 * lq + r;
-    if (lj == 0 && g < G) red_f[wave][g] = v;
+    if (lj == 0 && g < G) red_m[wave][g] = m;
   }
   sv_max = wave_max(sv_max);
   if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
+
+  // prefetch of this thread's first rows for the weight and key passes
+  int32_t kpos[KB];
+  float kev[KB], ksv[KB];
+  auto load_rows = [&](int i0) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int i = i0 + kThreads * u;
+      int32_t p = -1;
+      float ev = 0.0f, sv = 0.0f;
+      if (i < n_old) {
+        p = opos[i];
+        ev = (kvpop ? oprio : oema)[i];
+        sv = ovs[i];
+      } else if (i >= n_old32 && i < rows && i - n_old32 < Wr) {
+        p = rpos[i - n_old32];
+        ev = (kvpop ? rprio : rema)[i - n_old32];
+      }
+      kpos[u] = p;
+      kev[u] = ev;
+      ksv[u] = sv;
+    }
+  };
+  load_rows(tid);
   __syncthreads();
   float M[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) M[g] = fmaxf(fmaxf(red_f[0][g], red_f[1][g]), fmaxf(red_f[2][g], red_f[3][g]));
+  for (int g = 0; g < G; ++g) {
+    float m = red_m[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, red_m[w][g]);
+    M[g] = m;
+  }
   float svm = 0.0f;
   for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
-  __syncthreads();
   // PV weights are prescaled by a power of two that keeps p*sV*f below 2^14
   // (fp16 range) while lifting small weights out of the fp16 subnormals.
   int fexp = 10;
@@ -652,223 +766,213 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
   }
   const float fscale = ldexpf(1.0f, fexp), finv = ldexpf(1.0f, -fexp);
 
-  // ---- p_gi = exp(s_gi - M_g) in place; l_g = sum_i p_gi.
-  float lsum[G];
+  // ---- weight pass, once per (row, head): p = exp(s - M_g), l_g = sum p, and
+  // the PV weight w = p * scale * f stored in place of s as an fp16 pair
+  // (hi | lo << 16) with hi + lo = w to about 22 bits. scale is the row's V
+  // scale for INT8 rows with a nonzero scale, else 1.
+  float lpart[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) lsum[g] = 0.0f;
-  for (int i = tid; i < rows; i += kThreads) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float p = __expf(st.at(g, i) - M[g]);
-      st.at(g, i) = p;
-      lsum[g] += p;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float v = wave_sum(lsum[g]);
-    if (lane == 0) red_f[wave][g] = v;
-  }
-  __syncthreads();
-  float inv_l[G], Lsum[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    Lsum[g] = red_f[0][g] + red_f[1][g] + red_f[2][g] + red_f[3][g];
-    inv_l[g] = 1.0f / Lsum[g];
-  }
-
-  // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
-  // with A = w as an fp16 hi + lo pair (about 22 significant bits) and B = V
-  // from the transposed tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj].
-  // INT8 tiles fold the V scale into w = p * sV * f.
-  floatx4 O[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) O[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto weights = [&](int srow, const float* sv8, half8& ahi, half8& alo) {
-    float w[8];
-    if (lj < G) {
-      const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
-      const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = pp[e] > 0.0f ? pp[e] * (sv8 ? sv8[e] * fscale : fscale) : 0.0f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const _Float16 hi = (_Float16)w[e];
-      ahi[e] = hi;
-      alo[e] = (_Float16)(w[e] - (float)hi);
-    }
-  };
-  const int nv_old = n_old32 >> 5;
-  if (par.old_int8) {
-    for (int t0 = wave; t0 < nv_old; t0 += 4 * NV8) {
-      uint4 vw[NV8][NCB / 2];
-      float4 s0[NV8], s1[NV8];
-#pragma unroll
-      for (int u = 0; u < NV8; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_old) {
-          const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
-#pragma unroll
-          for (int k = 0; k < NCB / 2; ++k) vw[u][k] = *reinterpret_cast<const uint4*>(tb + 1024 * k);
-          s0[u] = *reinterpret_cast<const float4*>(ovs + 32 * tt + 8 * lq);
-          s1[u] = *reinterpret_cast<const float4*>(ovs + 32 * tt + 8 * lq + 4);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NV8; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_old) {
-          const float sv8[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
-          half8 ahi, alo;
-          weights(32 * tt + 8 * lq, sv8, ahi, alo);
-#pragma unroll
-          for (int k = 0; k < NCB / 2; ++k) {
-            half8 blo, bhi;
-            i8x16_to_h8(vw[u][k], blo, bhi);
-            O[2 * k] = mfma16(ahi, blo, O[2 * k]);
-            O[2 * k] = mfma16(alo, blo, O[2 * k]);
-            O[2 * k + 1] = mfma16(ahi, bhi, O[2 * k + 1]);
-            O[2 * k + 1] = mfma16(alo, bhi, O[2 * k + 1]);
-          }
-        }
-      }
-    }
-  } else {
-    for (int t0 = wave; t0 < nv_old; t0 += 4 * NV16) {
-      uint4 vw[NV16][NCB];
-#pragma unroll
-      for (int u = 0; u < NV16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_old) {
-          const uint16_t* tb = reinterpret_cast<const uint16_t*>(ovt) + (size_t)tt * 32 * D + 8 * lane;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) vw[u][cb] = *reinterpret_cast<const uint4*>(tb + 512 * cb);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NV16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_old) {
-          half8 ahi, alo;
-          weights(32 * tt + 8 * lq, nullptr, ahi, alo);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            O[cb] = mfma16(ahi, as_h8(vw[u][cb]), O[cb]);
-            O[cb] = mfma16(alo, as_h8(vw[u][cb]), O[cb]);
-          }
-        }
-      }
-    }
-  }
-  {
-    const int nv_ring = Wr32 >> 5;
-    for (int t0 = wave; t0 < nv_ring; t0 += 4 * NV16) {
-      uint4 vw[NV16][NCB];
-#pragma unroll
-      for (int u = 0; u < NV16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_ring) {
-          const uint16_t* tb = rvt + (size_t)tt * 32 * D + 8 * lane;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) vw[u][cb] = *reinterpret_cast<const uint4*>(tb + 512 * cb);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NV16; ++u) {
-        const int tt = t0 + 4 * u;
-        if (tt < nv_ring) {
-          half8 ahi, alo;
-          weights(n_old32 + 32 * tt + 8 * lq, nullptr, ahi, alo);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            O[cb] = mfma16(ahi, as_h8(vw[u][cb]), O[cb]);
-            O[cb] = mfma16(alo, as_h8(vw[u][cb]), O[cb]);
-          }
-        }
-      }
-    }
-  }
-  // add the four waves' partial outputs in order (deterministic), then scale
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int g = 4 * lq + r;
-          if (g < G) {
-            const int idx = g * D + 16 * cb + lj;
-            obuf[idx] = (w == 0 ? 0.0f : obuf[idx]) + O[cb][r];
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  for (int idx = tid; idx < G * D; idx += kThreads)
-    a.out[(size_t)seg * G * D + idx] = f2h(obuf[idx] * finv * inv_l[idx / D]);
-
-  // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
-  // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
-  // Keys overwrite planes 0/1 of the row just read (same thread).
-  uint32_t n_live = 0, n_elig = 0;
-  const int pos_out = t - lay.W;
+  for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+  auto row_scale = [&](int i, float sv) { return (i < n_old && par.old_int8 && sv > 0.0f) ? sv : 1.0f; };
   for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
-    int32_t pos[KB];
-    float ev[KB];
+    if (i0 != tid) load_rows(i0);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int i = i0 + kThreads * u;
-      pos[u] = -1;
-      ev[u] = 0.0f;
-      if (i < n_old) {
-        pos[u] = opos[i];
-        ev[u] = kvpop ? oprio[i] : oema[i];
-      } else if (i >= n_old32 && i < rows && i - n_old32 < Wr) {
-        pos[u] = rpos[i - n_old32];
-        ev[u] = kvpop ? rprio[i - n_old32] : rema[i - n_old32];
+      if (i < rows) {
+        const float scf = row_scale(i, ksv[u]) * fscale;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = __expf(st.at(g, i) - M[g]);
+          lpart[g] += p;
+          const float wv = p * scf;
+          const _Float16 hi = (_Float16)wv, lo = (_Float16)(wv - (float)hi);
+          st.at(g, i) = __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                                                      ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+        }
       }
     }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float v = wave_sum(lpart[g]);
+    if (lane == 0) red_l[wave][g] = v;
+  }
+  __syncthreads();
+  float Lsum[G], inv_l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Lsum[g] = red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g];
+    inv_l[g] = 1.0f / Lsum[g];
+  }
+  // 1/l of the output rows 4*lq + r (lane-varying head index: from LDS)
+  float il4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * lq + r;
+    if (g < G) il4[r] = 1.0f / (red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g]);
+  }
+
+  // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
+  // with A = w as its fp16 hi and lo parts and B = V from the transposed
+  // tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj]. Waves split the
+  // columns: wave w owns column blocks CBW*w .. CBW*w+CBW-1 and streams every
+  // row, so no cross-wave reduction is needed.
+  floatx4 O[CBW];
+#pragma unroll
+  for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto weights = [&](int srow, half8& ahi, half8& alo) {
+    if (lj < G) {
+      const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
+      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
+                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
+                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
+                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
+      uint4 h, lw;
+      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
+      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
+      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
+      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
+      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
+      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
+      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
+      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
+      ahi = as_h8(h);
+      alo = as_h8(lw);
+    } else {
+      ahi = half8{};
+      alo = half8{};
+    }
+  };
+  auto pv16 = [&](const uint16_t* vbase, int srow0, int ntiles) {
+    pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
+        0, ntiles,
+        [&](int tt, PV16Buf<CBW>& bf) {
+          const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * lane;
+#pragma unroll
+          for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
+        },
+        [&](int tt, const PV16Buf<CBW>& bf) {
+          half8 ahi, alo;
+          weights(srow0 + 32 * tt + 8 * lq, ahi, alo);
+#pragma unroll
+          for (int k = 0; k < CBW; ++k) {
+            O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
+            O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
+          }
+        });
+  };
+  const int nv_old = n_old32 >> 5;
+  if (par.old_int8) {
+    pipelined<CONFKV_PV8_NPB, PV8Buf>(
+        0, nv_old,
+        [&](int tt, PV8Buf& bf) {
+          const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
+          if constexpr (CBW == 2) {
+            bf.v = ldnt4(tb + 1024 * wave);
+          } else {
+            const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+            bf.v = make_uint4(h.x, h.y, 0u, 0u);
+          }
+        },
+        [&](int tt, const PV8Buf& bf) {
+          half8 ahi, alo, blo, bhi;
+          weights(32 * tt + 8 * lq, ahi, alo);
+          i8x16_to_h8(bf.v, blo, bhi);
+          O[0] = mfma16(ahi, blo, O[0]);
+          O[0] = mfma16(alo, blo, O[0]);
+          if constexpr (CBW == 2) {
+            O[1] = mfma16(ahi, bhi, O[1]);
+            O[1] = mfma16(alo, bhi, O[1]);
+          }
+        });
+  } else {
+    pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old);
+  }
+  pv16(rvt, n_old32, (Wr + 31) >> 5);
+#pragma unroll
+  for (int k = 0; k < CBW; ++k) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * lq + r;
+      if (g < G) {
+        const int col = 16 * (CBW * wave + k) + lj;
+        a.out[((size_t)seg * G + g) * D + col] = f2h(O[k][r] * finv * il4[r]);
+      }
+    }
+  }
+
+  if (rows > kThreads * KB) load_rows(tid);  // the key pass starts again from the first rows
+  // prefetch of the row that may leave the FP16 window at the end of the step
+  // (16 consecutive elements of K or V per lane for lanes 0 .. 2*LPR-1)
+  uint4 aro0 = make_uint4(0u, 0u, 0u, 0u), aro1 = aro0;
+  if (pos_out >= 0 && wave == 0 && lane < 2 * LPR) {
+    const int slot = pos_out % Wr, cc = lane % LPR;
+    if (lane < LPR) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(rk + (size_t)slot * D + cc * 16);
+      aro0 = s4[0];
+      aro1 = s4[1];
+    } else {
+      uint32_t w8[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        w8[jj] = (uint32_t)rvt[vt16(slot, 16 * cc + 2 * jj, D)] |
+                 ((uint32_t)rvt[vt16(slot, 16 * cc + 2 * jj + 1, D)] << 16);
+      aro0 = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+      aro1 = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+    }
+  }
+  __syncthreads();  // every wave's PV has read the weights that the keys overwrite
+  // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
+  // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
+  // p_gi = (hi + lo) / (scale_i * f) from the stored weight. Keys overwrite
+  // planes 0/1 of the row just read (same thread).
+  uint32_t n_live = 0, n_elig = 0;
+  for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
+    if (i0 != tid) load_rows(i0);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int i = i0 + kThreads * u;
       if (i < rows) {
         uint64_t key = ~0ull;
         float score = NAN;
-        if (pos[u] >= 0) {
+        const int32_t pos = kpos[u];
+        if (pos >= 0) {
           ++n_live;
           if (!kvpop) {
+            const float inv_scf = 1.0f / (row_scale(i, ksv[u]) * fscale);
             float mass = 0.0f;
 #pragma unroll
-            for (int g = 0; g < G; ++g) mass = fmaf(st.at(g, i), inv_l[g], mass);
-            mass *= (1.0f / (float)G);
-            const float e = par.beta * ev[u] + (1.0f - par.beta) * mass;
+            for (int g = 0; g < G; ++g) {
+              const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
+              const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
+                               (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+              mass = fmaf(wv, inv_l[g], mass);
+            }
+            mass *= inv_scf * (1.0f / (float)G);
+            const float e = par.beta * kev[u] + (1.0f - par.beta) * mass;
             if (i < n_old)
               oema[i] = e;
             else
               rema[i - n_old32] = e;
-            const float rec = (float)(pos[u] + 1) / (float)(t + 1);
+            const float rec = (float)(pos + 1) / (float)(t + 1);
             score = par.alpha * e + (1.0f - par.alpha) * rec;
           } else {
-            score = ev[u];
+            score = kev[u];
           }
-          const bool elig = pos[u] >= par.s && pos[u] <= t - par.P;
+          const bool elig = pos >= par.s && pos <= t - par.P;
           if (!isfinite(score)) {
             atomicOr(lay.err, kErrNonFinite);
           } else if (elig) {
-            key = rank_key(score, pos[u]);
+            key = rank_key(score, pos);
             ++n_elig;
           }
-          if (pos[u] == pos_out && i >= n_old32) sh_out_live = 1;
+          if (pos == pos_out && i >= n_old32) sh_out_live = 1;
         }
         st.set_key(i, key);
         if (par.record) {
-          lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos[u];
-          lay.rec_score[(size_t)seg * lay.rows_max + i] = pos[u] >= 0 ? score : NAN;
+          lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
+          lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
         }
       }
     }
@@ -899,23 +1003,80 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
       T = block_min_u64(mk, red_k);
     }
   } else if (e > 8) {
-    T = radix_select(st, rows, e, hist4, red_u, sh);
+    T = radix_select(st, rows, e, hist, red_u, sh);
   }
 
-  // ---- compaction of the old region: victims below the new count m become
-  // holes, filled in ascending order by the survivors at or above m.
+  // ---- compaction of the old region. The row leaving the FP16 window (if it
+  // survived) takes the lowest victim's slot; the other victims below the new
+  // count m become holes, filled in ascending order by the survivors at or
+  // above m. The steady state (one old victim, one aged-out row) moves nothing.
+  const int slot_out = pos_out >= 0 ? pos_out % Wr : 0;
+  const bool age = pos_out >= 0 && sh_out_live && st.key(n_old32 + slot_out) > T;
   uint32_t ev_old = 0;
-  if (e > 0)
-    for (int i = tid; i < n_old; i += kThreads) ev_old += st.key(i) <= T ? 1u : 0u;
-  ev_old = block_sum_u32(ev_old, red_u);
-  const int m = n_old - (int)ev_old;
+  int vmin = n_old, vmax = -1;
+  if (e > 0) {
+    for (int i = tid; i < n_old; i += kThreads)
+      if (st.key(i) <= T) {
+        ++ev_old;
+        vmin = min(vmin, i);
+        vmax = max(vmax, i);
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      ev_old += __shfl_xor(ev_old, o, 64);
+      vmin = min(vmin, __shfl_xor(vmin, o, 64));
+      vmax = max(vmax, __shfl_xor(vmax, o, 64));
+    }
+    if (lane == 0) {
+      sh[wave] = vmin;
+      sh[4 + wave] = vmax;
+      red_u[wave] = ev_old;
+    }
+    __syncthreads();
+    ev_old = red_u[0] + red_u[1] + red_u[2] + red_u[3];
+    vmin = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
+    vmax = max(max(sh[4], sh[5]), max(sh[6], sh[7]));
+    __syncthreads();
+  }
+  const bool into_hole = age && ev_old > 0;         // aged-out row goes to slot vmin
+  const int rem = (int)ev_old - (into_hole ? 1 : 0);  // victims left to compact away
+  const int m = n_old - rem;                          // old rows after compaction (+1 if appended)
   uint32_t moved = 0;
-  if (ev_old > 0) {
+  if (rem == 1) {
+    const int v = into_hole ? vmax : vmin;  // the one remaining victim
+    if (v < m) {                            // move the last row (a survivor) into it
+      const int src = n_old - 1;
+      moved = 1;
+      if (rg == 0) {
+        const size_t rb = (size_t)D * ob;
+        const int cbytes = 16 * ob;
+        for (int off = 0; off < cbytes; off += 16)
+          *reinterpret_cast<uint4*>(okp + v * rb + c * cbytes + off) =
+              *reinterpret_cast<const uint4*>(okp + src * rb + c * cbytes + off);
+        if (ob == 1) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) ovt[vt8(v, 16 * c + jj, D)] = ovt[vt8(src, 16 * c + jj, D)];
+        } else {
+          uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) v16[vt16(v, 16 * c + jj, D)] = v16[vt16(src, 16 * c + jj, D)];
+        }
+        if (c == 0) {
+          opos[v] = opos[src];
+          oema[v] = oema[src];
+          oprio[v] = oprio[src];
+          oks[v] = oks[src];
+          ovs[v] = ovs[src];
+        }
+      }
+    }
+  } else if (rem > 1) {
+    // victim predicate for the hole fill: vmin is not a hole when it takes the aged-out row
+    auto hole = [&](int i) { return st.key(i) <= T && !(into_hole && i == vmin); };
     const int per = (n_old + kThreads - 1) / kThreads;
     const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
     uint32_t hv = 0, sv = 0;
     for (int i = lo; i < hi; ++i) {
-      const bool v = st.key(i) <= T;
+      const bool v = hole(i);
       hv += (v && i < m) ? 1u : 0u;
       sv += (!v && i >= m) ? 1u : 0u;
     }
@@ -925,7 +1086,7 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
     int32_t* holes = st.list(2);
     int32_t* srcs = st.list(3);
     for (int i = lo; i < hi; ++i) {
-      const bool v = st.key(i) <= T;
+      const bool v = hole(i);
       if (v && i < m) holes[ho++] = i;
       if (!v && i >= m) srcs[so++] = i;
     }
@@ -958,63 +1119,62 @@ __global__ void __launch_bounds__(kThreads, 2) fused_step_kernel(Layout lay, Par
   if (e > 0)
     for (int r = tid; r < Wr; r += kThreads)
       if (st.key(n_old32 + r) <= T) rpos[r] = -1;
-  __syncthreads();
 
   // ---- age-out: the row at t - W leaves the FP16 window; if it survived it
-  // is appended to the old region, quantized when old rows are INT8.
+  // is stored in the old region (quantized when old rows are INT8), in the
+  // lowest victim's slot or appended at m.
   int n_old_new = m;
   bool aged = false;
-  if (pos_out >= 0) {
-    const int slot = pos_out % Wr;
-    const bool alive = sh_out_live && st.key(n_old32 + slot) > T;
-    if (alive) {
-      if (m >= lay.cap) {
-        if (tid == 0) atomicOr(lay.err, kErrCapacity);
-      } else {
-        if (wave == 0 && lane < 2 * LPR) {
-          const bool isv = lane >= LPR;
-          const int cc = lane % LPR;
-          float x[16];
-          if (!isv) {
-            load16h(rk + (size_t)slot * D + cc * 16, x);
-          } else {
+  if (age) {
+    const int dst = into_hole ? vmin : m;
+    if (dst >= lay.cap) {
+      if (tid == 0) atomicOr(lay.err, kErrCapacity);
+    } else {
+      const int slot = slot_out;
+      if (wave == 0 && lane < 2 * LPR) {
+        const bool isv = lane >= LPR;
+        const int cc = lane % LPR;
+        float x[16];
+        {
+          const uint32_t w8[8] = {aro0.x, aro0.y, aro0.z, aro0.w, aro1.x, aro1.y, aro1.z, aro1.w};
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) x[jj] = h2f(rvt[vt16(slot, 16 * cc + jj, D)]);
-          }
-          if (par.old_int8) {
-            int8_t codes[16];
-            const float scale = quantize16<LPR>(x, codes);
-            if (!isv) {
-              *reinterpret_cast<uint4*>(okp + (size_t)m * D + cc * 16) = pack16(codes);
-              if (cc == 0) oks[m] = scale;
-            } else {
-#pragma unroll
-              for (int jj = 0; jj < 16; ++jj) ovt[vt8(m, 16 * cc + jj, D)] = (uint8_t)codes[jj];
-              if (cc == 0) ovs[m] = scale;
-            }
-          } else {
-            if (!isv) {
-              const uint4* s4 = reinterpret_cast<const uint4*>(rk + (size_t)slot * D + cc * 16);
-              uint4* d4 = reinterpret_cast<uint4*>(okp + ((size_t)m * D + cc * 16) * 2);
-              d4[0] = s4[0];
-              d4[1] = s4[1];
-            } else {
-              uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
-#pragma unroll
-              for (int jj = 0; jj < 16; ++jj) v16[vt16(m, 16 * cc + jj, D)] = f2h(x[jj]);
-            }
-            if (cc == 0) (isv ? ovs : oks)[m] = 0.0f;
+          for (int j = 0; j < 8; ++j) {
+            x[2 * j] = half_lo(w8[j]);
+            x[2 * j + 1] = half_hi(w8[j]);
           }
         }
-        if (tid == 0) {
-          opos[m] = pos_out;
-          oema[m] = rema[slot];
-          oprio[m] = rprio[slot];
+        if (par.old_int8) {
+          int8_t codes[16];
+          const float scale = quantize16<LPR>(x, codes);
+          if (!isv) {
+            *reinterpret_cast<uint4*>(okp + (size_t)dst * D + cc * 16) = pack16(codes);
+            if (cc == 0) oks[dst] = scale;
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) ovt[vt8(dst, 16 * cc + jj, D)] = (uint8_t)codes[jj];
+            if (cc == 0) ovs[dst] = scale;
+          }
+        } else {
+          if (!isv) {
+            uint4* d4 = reinterpret_cast<uint4*>(okp + ((size_t)dst * D + cc * 16) * 2);
+            d4[0] = aro0;
+            d4[1] = aro1;
+          } else {
+            uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) v16[vt16(dst, 16 * cc + jj, D)] = f2h(x[jj]);
+          }
+          if (cc == 0) (isv ? ovs : oks)[dst] = 0.0f;
+        }
+        if (lane == 0) {
+          opos[dst] = pos_out;
+          oema[dst] = rema[slot];
+          oprio[dst] = rprio[slot];
           rpos[slot] = -1;
         }
-        aged = true;
-        n_old_new = m + 1;
       }
+      aged = true;
+      if (!into_hole) n_old_new = m + 1;
     }
   }
   if (tid == 0) {
