@@ -241,10 +241,11 @@ def main():
     kv_per_step, alg_per_launch = algorithmic_bytes(w, st, args.steps, S)
     kv_gbps = kv_per_step / (ms_per_step * 1e-3) / 1e9
     fused_avg_ms = prof["fused_ms"] / max(prof["fused_launches"], 1)
-    reduce_avg_ms = prof["reduce_ms"] / max(prof["reduce_launches"], 1)
+    reduce_avg_ms = prof["reduce_ms"] / prof["reduce_launches"] if prof["reduce_launches"] else None
     achieved = alg_per_launch / (fused_avg_ms * 1e-3) / 1e9
     log(f"{steps_per_s:.1f} steps/s ({ms_per_step:.4f} ms/step), KV {kv_gbps:.0f} GB/s; fused kernel "
-        f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic; reducer {reduce_avg_ms * 1e3:.1f} us")
+        f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic"
+        + ("" if reduce_avg_ms is None else f"; reducer {reduce_avg_ms * 1e3:.1f} us"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -278,7 +279,7 @@ def main():
         "tokens_per_s": steps_per_s * B,
         "first_step_ms": first_ms,
         "first_step_kv_bytes": first_stats["kv_bytes"],
-        "reducer_us": reduce_avg_ms * 1e3,
+        "reducer_us": None if reduce_avg_ms is None else reduce_avg_ms * 1e3,
         "rows_evicted_per_step": st["rows_evicted"] / args.steps,
         "rows_moved_per_step": st["rows_moved"] / args.steps,
         "roofline": {

@@ -428,6 +428,17 @@ __device__ __forceinline__ void pipelined(int t0, int t1, LoadF&& load, CompF&& 
       if (base + NPB + u < t1) comp(base + NPB + u, B[u]);
   }
 }
+// As pipelined, with the first batch (tiles t0 .. t0+NPB-1) already loaded
+// into `first` by the caller, ahead of work that does not need them.
+template <int NPB, class Buf, class LoadF, class CompF>
+__device__ __forceinline__ void pipelined_from(int t0, int t1, const Buf (&first)[NPB], LoadF&& load,
+                                               CompF&& comp) {
+#pragma unroll
+  for (int u = 0; u < NPB; ++u)
+    if (t0 + u < t1) comp(t0 + u, first[u]);
+  pipelined<NPB, Buf>(t0 + NPB, t1, load, comp);
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 struct QK8Buf {
   uint4 k0, k1;
   float sk, sv;
@@ -543,17 +554,18 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   float* oema = lay.old_ema + obase;
   float* oprio = lay.old_prio + obase;
 
-  const int n_old = lay.seg_nold[seg];
+  // The host sizes the LDS planes for the most rows a segment can hold. Should
+  // a segment hold more, the step is computed on a clamped row count (every
+  // access stays in bounds) and an internal error is raised at the end; the
+  // state is then invalid and every later call refuses to run.
+  const int n_old_raw = lay.seg_nold[seg];
+  const int n_old = kLds ? min(n_old_raw, a.lds_rows - Wr32) : n_old_raw;
   const int n_old32 = (n_old + 31) & ~31;
   const int rows = n_old32 + Wr32;
   Stage<kLds> st;
   if constexpr (kLds) {
     st.p = dyn_lds;
     st.rs = a.lds_rows;
-    if (rows > a.lds_rows) {  // the host bound on rows was wrong: refuse, touch nothing
-      if (tid == 0) atomicOr(lay.err, kErrInternal);
-      return;
-    }
   } else {
     st.p = lay.stage + (size_t)seg * PL * lay.rows_max;
     st.rs = lay.rows_max;
@@ -563,27 +575,22 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
   const uint16_t* qrow = a.q + ((size_t)seg * G + (lj < G ? lj : 0)) * D;
   half8 qa8[KS], qa16[KS];
-  auto load_qa16 = [&]() {
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-      qa16[kk] = lj < G ? as_h8(u16) : half8{};
-    }
-  };
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
-    qa8[kk] = lj < G ? as_h8(u8) : half8{};
+    const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
+    qa16[kk] = lj < G ? as_h8(u16) : half8{};
   }
 
   // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
   // previous row (pos t - Wr) left the window at the end of the last step.
-  // The barrier that publishes it comes after the old-region QK, which does
-  // not read the ring.
+  // Nothing in this step reads these stores back: the ring QK takes the new
+  // row's K from k_new and the row-state passes substitute its position,
+  // EMA and (KVpop) the delayed priority, so no barrier is needed here.
   const int slot_new = t % Wr;
   const int pos_out = t - lay.W;
+  const uint16_t* kn = a.k_new + (size_t)seg * D;
+  const int pos_prio = (kvpop && t - par.P >= par.s) ? t - par.P : -1;  // row whose priority arrives now
   {
-    const uint16_t* kn = a.k_new + (size_t)seg * D;
     const uint16_t* vn = a.v_new + (size_t)seg * D;
     if (tid < D / 8)
       reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = reinterpret_cast<const uint4*>(kn)[tid];
@@ -594,25 +601,64 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
       rprio[slot_new] = 0.0f;
       // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
       // priority now, as it stops being protected.
-      const int pl = t - par.P;
-      if (kvpop && pl >= par.s) {
-        const int sl = pl % Wr;
-        if (rpos[sl] == pl) rprio[sl] = a.prio_new[seg];
+      if (pos_prio >= 0) {
+        const int sl = pos_prio % Wr;
+        if (rpos[sl] == pos_prio) rprio[sl] = a.prio_new[seg];
       }
       sh_out_live = 0;
     }
   }
 
   // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
-  // lane (lq, lj) receives S[4*lq + r][row lj]. Each wave takes a contiguous
-  // share of the tiles, stages s in LDS and keeps a running max per head.
+  // lane (lq, lj) receives S[4*lq + r][row lj]. The ring goes first (its
+  // tiles do not depend on the old-region count), then the old region. Each
+  // wave takes a contiguous share of the tiles, stages s in LDS and keeps a
+  // running max per head.
   const float sm = par.sm_scale;
   float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float sv_max = 0.0f;
+  {
+    const int nt_ring = (Wr + 15) >> 4;  // tiles wholly past slot Wr-1 are skipped
+    const int ta = (wave * nt_ring) >> 2, tb = ((wave + 1) * nt_ring) >> 2;
+    pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+        ta, tb,
+        [&](int tt, QK16Buf<KS>& bf) {
+          const int r = 16 * tt + lj;
+          const uint16_t* kr = r == slot_new ? kn : rk + (size_t)r * D;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+          bf.pr = rpos[r];
+        },
+        [&](int tt, const QK16Buf<KS>& bf) {
+          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
+          const int r = 16 * tt + lj;
+          const bool valid = r < Wr && (bf.pr >= 0 || r == slot_new);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int g = 4 * lq + rr;
+            if (g < G) {
+              const float sc = valid ? acc[rr] * sm : -INFINITY;
+              st.at(g, n_old32 + r) = sc;
+              mrun[rr] = fmaxf(mrun[rr], sc);
+            }
+          }
+        });
+    // ring slots past the last QK tile
+    for (int r = tid + 16 * nt_ring; r < Wr32; r += kThreads)
+#pragma unroll
+      for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
+  }
   const int nt_old = n_old32 >> 4;
   {
     const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
     if (par.old_int8) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
+        qa8[kk] = lj < G ? as_h8(u8) : half8{};
+      }
       pipelined<CONFKV_QK8_NPB, QK8Buf>(
           ta, tb,
           [&](int tt, QK8Buf& bf) {
@@ -650,7 +696,6 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
             }
           });
     } else {
-      load_qa16();
       pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
           ta, tb,
           [&](int tt, QK16Buf<KS>& bf) {
@@ -676,41 +721,25 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
           });
     }
   }
-  __syncthreads();  // the appended ring row is visible from here on
-  if (par.old_int8) load_qa16();
-  {
-    const int nt_ring = (Wr + 15) >> 4;  // tiles wholly past slot Wr-1 are skipped
-    const int ta = (wave * nt_ring) >> 2, tb = ((wave + 1) * nt_ring) >> 2;
-    pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
-        ta, tb,
-        [&](int tt, QK16Buf<KS>& bf) {
-          const int r = 16 * tt + lj;
-          const uint16_t* kr = rk + (size_t)r * D;
+  // The first INT8 V tiles of PV are loaded now: they are in flight during
+  // the max merge and the weight pass, which need none of them.
+  const int nv_old = n_old32 >> 5;
+  auto load_pv8 = [&](int tt, PV8Buf& bf) {
+    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
+    if constexpr (CBW == 2) {
+      bf.v = ldnt4(tb + 1024 * wave);
+    } else {
+      const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+      bf.v = make_uint4(h.x, h.y, 0u, 0u);
+    }
+  };
+  PV8Buf pv_first[CONFKV_PV8_NPB];
+  if (par.old_int8) {
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
-          bf.pr = rpos[r];
-        },
-        [&](int tt, const QK16Buf<KS>& bf) {
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
-          const int r = 16 * tt + lj;
-          const bool valid = r < Wr && bf.pr >= 0;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int g = 4 * lq + rr;
-            if (g < G) {
-              const float sc = valid ? acc[rr] * sm : -INFINITY;
-              st.at(g, n_old32 + r) = sc;
-              mrun[rr] = fmaxf(mrun[rr], sc);
-            }
-          }
-        });
-    // ring slots past the last QK tile
-    for (int r = tid + 16 * nt_ring; r < Wr32; r += kThreads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
+    for (int u = 0; u < CONFKV_PV8_NPB; ++u)
+      if (u < nv_old) load_pv8(u, pv_first[u]);
   }
+
   // per-head maxima: over the 16 lanes of each lane group, then per wave
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -736,8 +765,10 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
         ev = (kvpop ? oprio : oema)[i];
         sv = ovs[i];
       } else if (i >= n_old32 && i < rows && i - n_old32 < Wr) {
-        p = rpos[i - n_old32];
-        ev = (kvpop ? rprio : rema)[i - n_old32];
+        const int r = i - n_old32;
+        p = r == slot_new ? t : rpos[r];
+        ev = r == slot_new ? 0.0f : (kvpop ? rprio : rema)[r];
+        if (kvpop && p == pos_prio && p >= 0) ev = a.prio_new[seg];
       }
       kpos[u] = p;
       kev[u] = ev;
@@ -862,19 +893,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
           }
         });
   };
-  const int nv_old = n_old32 >> 5;
   if (par.old_int8) {
-    pipelined<CONFKV_PV8_NPB, PV8Buf>(
-        0, nv_old,
-        [&](int tt, PV8Buf& bf) {
-          const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
-          if constexpr (CBW == 2) {
-            bf.v = ldnt4(tb + 1024 * wave);
-          } else {
-            const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-            bf.v = make_uint4(h.x, h.y, 0u, 0u);
-          }
-        },
+    pipelined_from<CONFKV_PV8_NPB, PV8Buf>(
+        0, nv_old, pv_first, load_pv8,
         [&](int tt, const PV8Buf& bf) {
           half8 ahi, alo, blo, bhi;
           weights(32 * tt + 8 * lq, ahi, alo);
@@ -905,22 +926,19 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   if (rows > kThreads * KB) load_rows(tid);  // the key pass starts again from the first rows
   // prefetch of the row that may leave the FP16 window at the end of the step
   // (16 consecutive elements of K or V per lane for lanes 0 .. 2*LPR-1)
-  uint4 aro0 = make_uint4(0u, 0u, 0u, 0u), aro1 = aro0;
+  // One half per register (K: 16 consecutive halves of the row; V: the same
+  // columns from the transposed tile, 8 halves apart), combined only at the
+  // age-out, so nothing here waits for the loads.
+  uint32_t aro[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) aro[jj] = 0u;
   if (pos_out >= 0 && wave == 0 && lane < 2 * LPR) {
     const int slot = pos_out % Wr, cc = lane % LPR;
-    if (lane < LPR) {
-      const uint4* s4 = reinterpret_cast<const uint4*>(rk + (size_t)slot * D + cc * 16);
-      aro0 = s4[0];
-      aro1 = s4[1];
-    } else {
-      uint32_t w8[8];
+    const bool isv = lane >= LPR;
+    const uint16_t* src = isv ? rvt + vt16(slot, 16 * cc, D) : rk + (size_t)slot * D + cc * 16;
+    const int stride = isv ? 8 : 1;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        w8[jj] = (uint32_t)rvt[vt16(slot, 16 * cc + 2 * jj, D)] |
-                 ((uint32_t)rvt[vt16(slot, 16 * cc + 2 * jj + 1, D)] << 16);
-      aro0 = make_uint4(w8[0], w8[1], w8[2], w8[3]);
-      aro1 = make_uint4(w8[4], w8[5], w8[6], w8[7]);
-    }
+    for (int jj = 0; jj < 16; ++jj) aro[jj] = src[stride * jj];
   }
   __syncthreads();  // every wave's PV has read the weights that the keys overwrite
   // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
@@ -1136,12 +1154,8 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
         const int cc = lane % LPR;
         float x[16];
         {
-          const uint32_t w8[8] = {aro0.x, aro0.y, aro0.z, aro0.w, aro1.x, aro1.y, aro1.z, aro1.w};
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            x[2 * j] = half_lo(w8[j]);
-            x[2 * j + 1] = half_hi(w8[j]);
-          }
+          for (int j = 0; j < 16; ++j) x[j] = half_lo(aro[j]);
         }
         if (par.old_int8) {
           int8_t codes[16];
@@ -1157,8 +1171,11 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
         } else {
           if (!isv) {
             uint4* d4 = reinterpret_cast<uint4*>(okp + ((size_t)dst * D + cc * 16) * 2);
-            d4[0] = aro0;
-            d4[1] = aro1;
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = aro[2 * j] | (aro[2 * j + 1] << 16);
+            d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
           } else {
             uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
 #pragma unroll
@@ -1178,6 +1195,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
     }
   }
   if (tid == 0) {
+    if (n_old != n_old_raw) atomicOr(lay.err, kErrInternal);
     lay.seg_nold[seg] = n_old_new;
     const uint64_t live_ring = (uint64_t)n_live - (uint64_t)n_old;
     const uint64_t old_row = par.old_int8 ? (uint64_t)(2 * D + 8) : (uint64_t)(4 * D);
