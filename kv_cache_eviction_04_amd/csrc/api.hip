@@ -152,9 +152,6 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();
   lay.stage = hbm_stage ? (float*)take(S * lay.planes * (size_t)lay.rows_max * 4) : nullptr;
   lay.partials = (ConfPartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(ConfPartial));
-  lay.row_counter = (uint32_t*)take((size_t)lay.B * 4);
-  lay.row_conf = (float*)take((size_t)lay.B * 4);
-  lay.row_base = (int32_t*)take((size_t)lay.B * 4);
   lay.err = (uint32_t*)take(4);
   lay.stats_total = (uint64_t*)take(kStatFields * 8);
   if (c->record_scores) {
@@ -314,7 +311,7 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
   const Layout& lay = h->lay;
   if (conf) {
     if (record_event(h, h->pr, s, true)) goto hip_fail;
-    if (launch_conf_reduce(lay, h->par, logits, conf_out, budget_out, stream) != 0) goto hip_fail;
+    if (launch_conf_reduce(lay, logits, stream) != 0) goto hip_fail;
     if (record_event(h, h->pr, s, false)) goto hip_fail;
   }
   {
@@ -325,6 +322,8 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
     a.v_new = v_new;
     a.prio_new = prio_new;
     a.out = out;
+    a.conf_out = conf_out;
+    a.budget_out = budget_out;
     const int64_t old32 = (std::min<int64_t>(h->rows_bound, lay.cap) + 31) & ~(int64_t)31;
     const int64_t lds_rows = old32 + lay.Wr32;
     const int64_t lds_bytes = lds_rows * lay.planes * 4;

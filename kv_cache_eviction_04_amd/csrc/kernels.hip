@@ -200,9 +200,10 @@ __device__ __forceinline__ uint4 pack16(const int8_t (&c)[16]) {
 
 // ======================================================= logits -> confidence
 // [Conf-KV post, pseudocode] p = softmax(logits); c mixes the normalized
-// entropy, sigmoid of the top-2 log-prob gap and p_max. Per chunk: M = max z,
-// S = sum e^(z-M), T = sum e^(z-M)(z-M) (fp64 accumulation of fp32
-// exponentials), top-2 values. Merged over chunks with M* = max M_c:
+// entropy, sigmoid of the top-2 log-prob gap and p_max. Per chunk (reducer
+// kernel): M = max z, S = sum e^(z-M), T = sum e^(z-M)(z-M) (fp64
+// accumulation of fp32 exponentials), top-2 values. Merged over chunks (by
+// each segment of the row) with M* = max M_c:
 //   S* = sum S_c e^(M_c-M*),  T* = sum e^(M_c-M*) (T_c + (M_c-M*) S_c),
 // so H = log S* - T*/S*, p_max = 1/S*, margin = top1 - top2.
 __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
@@ -210,21 +211,13 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
   a2 = fmaxf(lo, fmaxf(a2, b2));
   a1 = hi;
 }
-__device__ __forceinline__ void mst_merge(double& pm, double& pS, double& pT, double qm, double qS, double qT) {
-  if (qm == -INFINITY) return;
-  const double mx = fmax(pm, qm);
-  const double f1 = pm > -INFINITY ? exp(pm - mx) : 0.0, f2 = exp(qm - mx);
-  pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0)) + f2 * (qT + (qm - mx) * qS);
-  pS = f1 * pS + f2 * qS;
-  pm = mx;
-}
 
-__global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par, const float* logits, float* conf_out,
-                                                          int32_t* budget_out) {
+// One workgroup per (chunk, batch row): the chunk's partial (M, S, T, top-2,
+// non-finite flag). The segments of the row merge the partials themselves.
+__global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, const float* logits) {
   __shared__ float s_t1[4], s_t2[4];
   __shared__ double s_S[4], s_T[4];
   __shared__ uint32_t s_bad[4];
-  __shared__ int s_last;
   const int b = blockIdx.y, ci = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = lay.V;
   const float* z = logits + (size_t)b * V;
@@ -288,61 +281,62 @@ __global__ void __launch_bounds__(256) conf_reduce_kernel(Layout lay, Params par
     P.nonfinite = bad;
     P.pad = 0;
     lay.partials[(size_t)b * lay.chunks + ci] = P;
-    __threadfence();
-    const uint32_t prev = atomicAdd(&lay.row_counter[b], 1u);
-    s_last = (prev == (uint32_t)(lay.chunks - 1));
   }
-  __syncthreads();
-  if (!s_last || wave != 0) return;
-  __threadfence();
+}
 
-  // Last chunk of row b: wave 0 merges the partials, one chunk per lane.
+// Merge of a batch row's chunk partials by one wave (partial c on lane c % 64,
+// the first 64 preloaded into `first`), then c and the step's base budget for
+// every lane. The chunk sums were accumulated in fp64; the merge and the final
+// terms run in fp32, whose error (~1e-7 on c) is far below what the gate
+// needs: H = log S + E[M - z] adds two non-negative terms, so nothing cancels.
+// A non-finite logit or confidence raises the error and takes the larger
+// budget.
+__device__ __forceinline__ void mst_merge_f(float& pm, float& pS, float& pT, float qm, float qS, float qT) {
+  if (qm == -INFINITY) return;
+  const float mx = fmaxf(pm, qm);
+  const float f1 = pm > -INFINITY ? expf(pm - mx) : 0.0f, f2 = expf(qm - mx);
+  pT = f1 * (pT + (pm > -INFINITY ? (pm - mx) * pS : 0.0f)) + f2 * (qT + (qm - mx) * qS);
+  pS = f1 * pS + f2 * qS;
+  pm = mx;
+}
+__device__ __forceinline__ void row_confidence(const Layout& lay, const Params& par, int b, int lane,
+                                               const ConfPartial& first, float& c_out, int& base_out) {
   const ConfPartial* parts = lay.partials + (size_t)b * lay.chunks;
   float a1 = -INFINITY, a2 = -INFINITY;
-  double pm = -INFINITY, pS = 0.0, pT = 0.0;
+  float pm = -INFINITY, pS = 0.0f, pT = 0.0f;
   uint32_t badall = 0;
   for (int c0 = 0; c0 < lay.chunks; c0 += 64) {
     const int c = c0 + lane;
     if (c < lay.chunks) {
-      const ConfPartial P = parts[c];
+      const ConfPartial P = c0 == 0 ? first : parts[c];
       badall |= P.nonfinite;
       top2_merge(a1, a2, P.m, P.top2);
-      mst_merge(pm, pS, pT, (double)P.m, P.S, P.T);
+      mst_merge_f(pm, pS, pT, P.m, (float)P.S, (float)P.T);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float o1 = __shfl_xor(a1, o, 64), o2 = __shfl_xor(a2, o, 64);
     top2_merge(a1, a2, o1, o2);
     badall |= __shfl_xor(badall, o, 64);
-    const double qm = __shfl_xor(pm, o, 64), qS = __shfl_xor(pS, o, 64), qT = __shfl_xor(pT, o, 64);
-    mst_merge(pm, pS, pT, qm, qS, qT);
+    const float qm = __shfl_xor(pm, o, 64), qS = __shfl_xor(pS, o, 64), qT = __shfl_xor(pT, o, 64);
+    mst_merge_f(pm, pS, pT, qm, qS, qT);
   }
-  if (lane != 0) return;
-  const double Sx = pS, Tx = pT;
-  const double H = log(Sx) - Tx / Sx;
-  const double Hn = H / log((double)V);
-  const double margin = (double)a1 - (double)a2;
-  const double sig = 1.0 / (1.0 + exp(-margin));
-  const double cval = (double)par.w_e * (1.0 - Hn) + (double)par.w_m * sig + (double)par.w_p * (1.0 / Sx);
-  int base;
-  float cout;
+  const float H = logf(pS) - pT / pS;
+  const float Hn = H / logf((float)lay.V);
+  const float sig = 1.0f / (1.0f + expf(-(a1 - a2)));
+  const float cval = par.w_e * (1.0f - Hn) + par.w_m * sig + par.w_p * (1.0f / pS);
   if (badall || !isfinite(cval)) {
-    atomicOr(lay.err, kErrNonFinite);
-    base = max(par.n_low, par.n_high);
-    cout = NAN;
+    if (lane == 0) atomicOr(lay.err, kErrNonFinite);
+    base_out = max(par.n_low, par.n_high);
+    c_out = NAN;
   } else {
-    const bool confident = cval >= (double)par.tau;
+    const bool confident = cval >= par.tau;
     if (par.gate_literal)
-      base = confident ? par.n_high : par.n_low;
+      base_out = confident ? par.n_high : par.n_low;
     else
-      base = confident ? min(par.n_low, par.n_high) : max(par.n_low, par.n_high);
-    cout = (float)cval;
+      base_out = confident ? min(par.n_low, par.n_high) : max(par.n_low, par.n_high);
+    c_out = cval;
   }
-  lay.row_conf[b] = cout;
-  lay.row_base[b] = base;
-  if (conf_out) conf_out[b] = cout;
-  if (budget_out) budget_out[b] = base;
-  lay.row_counter[b] = 0;
 }
 
 // ================================================== fused attend+evict step
@@ -529,7 +523,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   __shared__ uint64_t red_k[4];
   __shared__ uint32_t hist[256];
   __shared__ int32_t sh[8];
-  __shared__ int32_t sh_out_live;
+  __shared__ int32_t sh_out_live, sh_base;
   extern __shared__ float dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -940,6 +934,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) aro[jj] = src[stride * jj];
   }
+  // this row's logits partials, merged by wave 0 after the key pass
+  ConfPartial part0;
+  if (!kvpop && wave == 0 && lane < lay.chunks) part0 = lay.partials[(size_t)b * lay.chunks + lane];
   __syncthreads();  // every wave's PV has read the weights that the keys overwrite
   // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
   // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
@@ -995,13 +992,25 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
       }
     }
   }
+  if (!kvpop && wave == 0) {
+    float cval;
+    int base;
+    row_confidence(lay, par, b, lane, part0, cval, base);
+    if (lane == 0) {
+      sh_base = base;
+      if (l == 0 && seg % lay.Hkv == 0) {  // the row's first segment reports it
+        if (a.conf_out) a.conf_out[b] = cval;
+        if (a.budget_out) a.budget_out[b] = base;
+      }
+    }
+  }
   n_live = block_sum_u32(n_live, red_u);
   n_elig = block_sum_u32(n_elig, red_u);
 
   // ---- budget and selection of the e lowest keys among the eligible rows.
   int budget;
   if (!kvpop) {
-    const long long base = lay.row_base[b];
+    const long long base = sh_base;
     budget = (par.pyramid && lay.L > 1)
                  ? (int)((base * (long long)(3 * (lay.L - 1) - 2 * l)) / (long long)(2 * (lay.L - 1)))
                  : (int)base;
@@ -1416,10 +1425,8 @@ int launch_init(const Layout& lay, const Params& par, void* state, size_t state_
   return ok_or_err();
 }
 
-int launch_conf_reduce(const Layout& lay, const Params& par, const float* logits, float* conf_out,
-                       int32_t* budget_out, void* stream) {
-  hipLaunchKernelGGL(conf_reduce_kernel, dim3(lay.chunks, lay.B), dim3(256), 0, (hipStream_t)stream, lay, par,
-                     logits, conf_out, budget_out);
+int launch_conf_reduce(const Layout& lay, const float* logits, void* stream) {
+  hipLaunchKernelGGL(conf_reduce_kernel, dim3(lay.chunks, lay.B), dim3(256), 0, (hipStream_t)stream, lay, logits);
   return ok_or_err();
 }
 

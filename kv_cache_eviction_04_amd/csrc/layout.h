@@ -67,9 +67,6 @@ struct Layout {
   float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
   // confidence reducer
   ConfPartial* partials;  // [B][chunks]
-  uint32_t* row_counter;  // [B]
-  float* row_conf;        // [B]
-  int32_t* row_base;      // [B]
   uint32_t* err;          // [1]
   uint64_t* stats_total;  // [kStatFields]
   // last-step record (record_scores)
@@ -92,13 +89,14 @@ struct StepArgs {
   const uint16_t* v_new;
   const float* prio_new;     // [L][B][Hkv] or null
   uint16_t* out;             // [L][B][Hq][D]
+  float* conf_out;           // [B] or null (CONF)
+  int32_t* budget_out;       // [B] or null (CONF)
 };
 
 // Launchers (kernels.hip). All enqueue on `stream` and return the launch status.
 int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
                 const uint16_t* pv, int32_t P0, void* stream);
-int launch_conf_reduce(const Layout& lay, const Params& par, const float* logits, float* conf_out,
-                       int32_t* budget_out, void* stream);
+int launch_conf_reduce(const Layout& lay, const float* logits, void* stream);
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                       void* stream);
 int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, int32_t* len, int32_t* pos,
