@@ -137,16 +137,13 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   };
   lay.ring_k = (uint16_t*)take(S * Wr * D * 2);
   lay.ring_v = (uint16_t*)take(S * Wr * D * 2);
-  lay.ring_pos = (int32_t*)take(S * Wr * 4);
-  lay.ring_ema = (float*)take(S * Wr * 4);
-  lay.ring_prio = (float*)take(S * Wr * 4);
   lay.old_k = take(S * cap * D * lay.old_bytes);
   lay.old_v = take(S * cap * D * lay.old_bytes);
   lay.old_ks = (float*)take(S * cap * 4);
   lay.old_vs = (float*)take(S * cap * 4);
-  lay.old_pos = (int32_t*)take(S * cap * 4);
-  lay.old_ema = (float*)take(S * cap * 4);
-  lay.old_prio = (float*)take(S * cap * 4);
+  lay.row_pos = (int32_t*)take(S * (size_t)lay.rows_max * 4);
+  lay.row_ema = (float*)take(S * (size_t)lay.rows_max * 4);
+  lay.row_prio = (float*)take(S * (size_t)lay.rows_max * 4);
   lay.seg_nold = (int32_t*)take(S * 4);
   lay.seg_stats = (uint64_t*)take(S * kStatFields * 8);
   const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();

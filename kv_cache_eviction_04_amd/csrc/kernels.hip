@@ -422,16 +422,6 @@ __device__ __forceinline__ void pipelined(int t0, int t1, LoadF&& load, CompF&& 
       if (base + NPB + u < t1) comp(base + NPB + u, B[u]);
   }
 }
-// As pipelined, with the first batch (tiles t0 .. t0+NPB-1) already loaded
-// into `first` by the caller, ahead of work that does not need them.
-template <int NPB, class Buf, class LoadF, class CompF>
-__device__ __forceinline__ void pipelined_from(int t0, int t1, const Buf (&first)[NPB], LoadF&& load,
-                                               CompF&& comp) {
-#pragma unroll
-  for (int u = 0; u < NPB; ++u)
-    if (t0 + u < t1) comp(t0 + u, first[u]);
-  pipelined<NPB, Buf>(t0 + NPB, t1, load, comp);
-}
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 struct QK8Buf {
   uint4 k0, k1;
@@ -536,17 +526,18 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
 
   uint16_t* rk = lay.ring_k + (size_t)seg * Wr32 * D;
   uint16_t* rvt = lay.ring_v + (size_t)seg * Wr32 * D;
-  int32_t* rpos = lay.ring_pos + (size_t)seg * Wr32;
-  float* rema = lay.ring_ema + (size_t)seg * Wr32;
-  float* rprio = lay.ring_prio + (size_t)seg * Wr32;
   const size_t obase = (size_t)seg * lay.cap32;
   uint8_t* okp = lay.old_k + obase * D * ob;
   uint8_t* ovt = lay.old_v + obase * D * ob;
   float* oks = lay.old_ks + obase;
   float* ovs = lay.old_vs + obase;
-  int32_t* opos = lay.old_pos + obase;
-  float* oema = lay.old_ema + obase;
-  float* oprio = lay.old_prio + obase;
+  const size_t sbase = (size_t)seg * lay.rows_max;  // row state: old rows, then ring slots at cap32
+  int32_t* opos = lay.row_pos + sbase;
+  float* oema = lay.row_ema + sbase;
+  float* oprio = lay.row_prio + sbase;
+  int32_t* rpos = opos + lay.cap32;
+  float* rema = oema + lay.cap32;
+  float* rprio = oprio + lay.cap32;
 
   // The host sizes the LDS planes for the most rows a segment can hold. Should
   // a segment hold more, the step is computed on a clamped row count (every
@@ -575,33 +566,16 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
     qa16[kk] = lj < G ? as_h8(u16) : half8{};
   }
 
-  // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
-  // previous row (pos t - Wr) left the window at the end of the last step.
-  // Nothing in this step reads these stores back: the ring QK takes the new
-  // row's K from k_new and the row-state passes substitute its position,
-  // EMA and (KVpop) the delayed priority, so no barrier is needed here.
+  // ---- the new row (pos t): its data is loaded now and appended to the ring
+  // after the ring QK (below), so these loads do not hold up the first tiles.
   const int slot_new = t % Wr;
   const int pos_out = t - lay.W;
   const uint16_t* kn = a.k_new + (size_t)seg * D;
   const int pos_prio = (kvpop && t - par.P >= par.s) ? t - par.P : -1;  // row whose priority arrives now
-  {
-    const uint16_t* vn = a.v_new + (size_t)seg * D;
-    if (tid < D / 8)
-      reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = reinterpret_cast<const uint4*>(kn)[tid];
-    if (tid < D) rvt[vt16(slot_new, tid, D)] = vn[tid];
-    if (tid == 0) {
-      rpos[slot_new] = t;
-      rema[slot_new] = 0.0f;
-      rprio[slot_new] = 0.0f;
-      // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
-      // priority now, as it stops being protected.
-      if (pos_prio >= 0) {
-        const int sl = pos_prio % Wr;
-        if (rpos[sl] == pos_prio) rprio[sl] = a.prio_new[seg];
-      }
-      sh_out_live = 0;
-    }
-  }
+  const float prio_now = pos_prio >= 0 ? a.prio_new[seg] : 0.0f;
+  const uint4 kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
+  const uint16_t vn1 = a.v_new[(size_t)seg * D + tid % D];
+  const int32_t pos_prio_slot = pos_prio >= 0 ? rpos[pos_prio % Wr] : -1;
 
   // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
   // lane (lq, lj) receives S[4*lq + r][row lj]. The ring goes first (its
@@ -644,6 +618,23 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
 #pragma unroll
       for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
   }
+  // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
+  // previous row (pos t - Wr) left the window at the end of the last step.
+  // Nothing reads these stores back before a barrier: the ring QK took the
+  // new row's K from k_new, and the row-state passes substitute its position,
+  // EMA and (KVpop) the delayed priority.
+  if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
+  if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
+  if (tid == 0) {
+    rpos[slot_new] = t;
+    rema[slot_new] = 0.0f;
+    rprio[slot_new] = 0.0f;
+    // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
+    // priority now, as it stops being protected.
+    if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
+    sh_out_live = 0;
+  }
+
   const int nt_old = n_old32 >> 4;
   {
     const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
@@ -715,25 +706,6 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
           });
     }
   }
-  // The first INT8 V tiles of PV are loaded now: they are in flight during
-  // the max merge and the weight pass, which need none of them.
-  const int nv_old = n_old32 >> 5;
-  auto load_pv8 = [&](int tt, PV8Buf& bf) {
-    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
-    if constexpr (CBW == 2) {
-      bf.v = ldnt4(tb + 1024 * wave);
-    } else {
-      const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-      bf.v = make_uint4(h.x, h.y, 0u, 0u);
-    }
-  };
-  PV8Buf pv_first[CONFKV_PV8_NPB];
-  if (par.old_int8) {
-#pragma unroll
-    for (int u = 0; u < CONFKV_PV8_NPB; ++u)
-      if (u < nv_old) load_pv8(u, pv_first[u]);
-  }
-
   // per-head maxima: over the 16 lanes of each lane group, then per wave
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -748,26 +720,29 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   // prefetch of this thread's first rows for the weight and key passes
   int32_t kpos[KB];
   float kev[KB], ksv[KB];
+  // Row state of stage row i sits at one index of the unified row arrays
+  // (old row i, or ring slot i - n_old32 at cap32 + slot), so every row issues
+  // the same three loads with no branch between them; padding rows read valid
+  // padding entries and are masked after.
+  const float* uev = kvpop ? oprio : oema;
   auto load_rows = [&](int i0) {
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int i = i0 + kThreads * u;
-      int32_t p = -1;
-      float ev = 0.0f, sv = 0.0f;
-      if (i < n_old) {
-        p = opos[i];
-        ev = (kvpop ? oprio : oema)[i];
-        sv = ovs[i];
-      } else if (i >= n_old32 && i < rows && i - n_old32 < Wr) {
-        const int r = i - n_old32;
-        p = r == slot_new ? t : rpos[r];
-        ev = r == slot_new ? 0.0f : (kvpop ? rprio : rema)[r];
-        if (kvpop && p == pos_prio && p >= 0) ev = a.prio_new[seg];
-      }
-      kpos[u] = p;
-      kev[u] = ev;
-      ksv[u] = sv;
+      const int r = i - n_old32;
+      const int ix = r < 0 ? i : lay.cap32 + min(r, Wr32 - 1);
+      kpos[u] = opos[ix];
+      kev[u] = uev[ix];
+      ksv[u] = ovs[min(i, lay.cap32 - 1)];
     }
+  };
+  // the raw loaded state of stage row i, masked: position (-1: no row), EMA or priority
+  auto row_state = [&](int i, int32_t pl, float el, int32_t& p, float& ev) {
+    const int r = i - n_old32;
+    const bool is_old = i < n_old, is_ring = r >= 0 && r < Wr;
+    p = is_old ? pl : (is_ring ? (r == slot_new ? t : pl) : -1);
+    ev = (is_old || (is_ring && r != slot_new)) ? el : 0.0f;
+    if (kvpop && is_ring && p == pos_prio && p >= 0) ev = prio_now;
   };
   load_rows(tid);
   __syncthreads();
@@ -887,20 +862,29 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
           }
         });
   };
+  const int nv_old = n_old32 >> 5;
+  auto load_pv8 = [&](int tt, PV8Buf& bf) {
+    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
+    if constexpr (CBW == 2) {
+      bf.v = ldnt4(tb + 1024 * wave);
+    } else {
+      const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+      bf.v = make_uint4(h.x, h.y, 0u, 0u);
+    }
+  };
   if (par.old_int8) {
-    pipelined_from<CONFKV_PV8_NPB, PV8Buf>(
-        0, nv_old, pv_first, load_pv8,
-        [&](int tt, const PV8Buf& bf) {
-          half8 ahi, alo, blo, bhi;
-          weights(32 * tt + 8 * lq, ahi, alo);
-          i8x16_to_h8(bf.v, blo, bhi);
-          O[0] = mfma16(ahi, blo, O[0]);
-          O[0] = mfma16(alo, blo, O[0]);
-          if constexpr (CBW == 2) {
-            O[1] = mfma16(ahi, bhi, O[1]);
-            O[1] = mfma16(alo, bhi, O[1]);
-          }
-        });
+    auto pv8 = [&](int tt, const PV8Buf& bf) {
+      half8 ahi, alo, blo, bhi;
+      weights(32 * tt + 8 * lq, ahi, alo);
+      i8x16_to_h8(bf.v, blo, bhi);
+      O[0] = mfma16(ahi, blo, O[0]);
+      O[0] = mfma16(alo, blo, O[0]);
+      if constexpr (CBW == 2) {
+        O[1] = mfma16(ahi, bhi, O[1]);
+        O[1] = mfma16(alo, bhi, O[1]);
+      }
+    };
+    pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, pv8);
   } else {
     pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old);
   }
@@ -917,7 +901,11 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
     }
   }
 
-  if (rows > kThreads * KB) load_rows(tid);  // the key pass starts again from the first rows
+  if (rows > kThreads * KB) {  // the key pass starts again from the first rows
+    int i0 = tid;
+    asm volatile("" : "+v"(i0));  // recompute the addresses rather than keep them live
+    load_rows(i0);
+  }
   // prefetch of the row that may leave the FP16 window at the end of the step
   // (16 consecutive elements of K or V per lane for lanes 0 .. 2*LPR-1)
   // One half per register (K: 16 consecutive halves of the row; V: the same
@@ -951,7 +939,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
       if (i < rows) {
         uint64_t key = ~0ull;
         float score = NAN;
-        const int32_t pos = kpos[u];
+        int32_t pos;
+        float ev_u;
+        row_state(i, kpos[u], kev[u], pos, ev_u);
         if (pos >= 0) {
           ++n_live;
           if (!kvpop) {
@@ -965,7 +955,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
               mass = fmaf(wv, inv_l[g], mass);
             }
             mass *= inv_scf * (1.0f / (float)G);
-            const float e = par.beta * kev[u] + (1.0f - par.beta) * mass;
+            const float e = par.beta * ev_u + (1.0f - par.beta) * mass;
             if (i < n_old)
               oema[i] = e;
             else
@@ -973,7 +963,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
             const float rec = (float)(pos + 1) / (float)(t + 1);
             score = par.alpha * e + (1.0f - par.alpha) * rec;
           } else {
-            score = kev[u];
+            score = ev_u;
           }
           const bool elig = pos >= par.s && pos <= t - par.P;
           if (!isfinite(score)) {
@@ -1233,7 +1223,7 @@ __global__ void zero_kernel(uint4* p, size_t n16) {
 
 __global__ void init_meta_kernel(Layout lay, int32_t n_old_init) {
   const int seg = blockIdx.x, tid = threadIdx.x;
-  for (int r = tid; r < lay.Wr32; r += blockDim.x) lay.ring_pos[(size_t)seg * lay.Wr32 + r] = -1;
+  for (int r = tid; r < lay.Wr32; r += blockDim.x) lay.row_pos[(size_t)seg * lay.rows_max + lay.cap32 + r] = -1;
   if (tid == 0) lay.seg_nold[seg] = n_old_init;
 }
 
@@ -1279,7 +1269,7 @@ __global__ void __launch_bounds__(256) ingest_kernel(Layout lay, Params par, con
           tile[rr * D + 16 * c + e] = f2h(xv[e]);
         }
       }
-      if (c == 0) lay.old_pos[row] = p;
+      if (c == 0) lay.row_pos[(size_t)seg * lay.rows_max + p] = p;
     } else {
       const int slot = p % lay.Wr;
       uint16_t* dk = lay.ring_k + ((size_t)seg * lay.Wr32 + slot) * D + c * 16;
@@ -1289,7 +1279,7 @@ __global__ void __launch_bounds__(256) ingest_kernel(Layout lay, Params par, con
         dk[e] = f2h(xk[e]);
         dv[vt16(slot, 16 * c + e, D)] = f2h(xv[e]);
       }
-      if (c == 0) lay.ring_pos[(size_t)seg * lay.Wr32 + slot] = p;
+      if (c == 0) lay.row_pos[(size_t)seg * lay.rows_max + lay.cap32 + slot] = p;
     }
   }
   __syncthreads();
@@ -1336,8 +1326,8 @@ __global__ void __launch_bounds__(256) read_cache_kernel(Layout lay, int32_t seg
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int D = lay.D, Wr = lay.Wr;
   const int n_old = lay.seg_nold[seg];
-  const int32_t* opos = lay.old_pos + (size_t)seg * lay.cap32;
-  const int32_t* rpos = lay.ring_pos + (size_t)seg * lay.Wr32;
+  const int32_t* opos = lay.row_pos + (size_t)seg * lay.rows_max;
+  const int32_t* rpos = opos + lay.cap32;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     int live = 0;
     for (int r = 0; r < Wr; ++r) live += rpos[r] >= 0;
@@ -1360,8 +1350,9 @@ __global__ void __launch_bounds__(256) read_cache_kernel(Layout lay, int32_t seg
   if (pos_o) pos_o[orow] = pos;
   if (is8_o) is8_o[orow] = row8 ? 1 : 0;
   const size_t src = in_old ? (size_t)seg * lay.cap32 + row : (size_t)seg * lay.Wr32 + row;
-  if (ema_o) ema_o[orow] = in_old ? lay.old_ema[src] : lay.ring_ema[src];
-  if (prio_o) prio_o[orow] = in_old ? lay.old_prio[src] : lay.ring_prio[src];
+  const size_t us = (size_t)seg * lay.rows_max + (in_old ? row : lay.cap32 + row);
+  if (ema_o) ema_o[orow] = lay.row_ema[us];
+  if (prio_o) prio_o[orow] = lay.row_prio[us];
   if (ks_o) ks_o[orow] = row8 ? lay.old_ks[src] : 0.0f;
   if (vs_o) vs_o[orow] = row8 ? lay.old_vs[src] : 0.0f;
   const size_t vbase = (in_old ? (size_t)seg * lay.cap32 : (size_t)seg * lay.Wr32) * D;

@@ -3,7 +3,7 @@
 //
 // Per segment seg = (l*B + b)*Hkv + h the state holds two regions:
 //   ring  — the FP16 window: Wr = W + 1 slots, a row at position p lives in
-//           slot p mod Wr; ring_pos = -1 marks an empty or evicted slot. At
+//           slot p mod Wr; a position of -1 marks an empty or evicted slot. At
 //           step t the live slots hold positions in [t-W, t].
 //   old   — rows older than the window, densely packed in [0, n_old) in no
 //           particular order: INT8 codes + fp32 absmax scales (old_int8) or
@@ -51,17 +51,15 @@ struct Layout {
   // ring
   uint16_t* ring_k;   // [S][Wr32][D] row-major
   uint16_t* ring_v;   // [S][Wr32/32] transposed FP16 tiles
-  int32_t* ring_pos;  // [S][Wr32]
-  float* ring_ema;    // [S][Wr32]
-  float* ring_prio;   // [S][Wr32]
   // old
   uint8_t* old_k;     // [S][cap32][D * old_bytes] row-major
   uint8_t* old_v;     // [S][cap32/32] transposed tiles
   float* old_ks;      // [S][cap32] (old_int8)
   float* old_vs;
-  int32_t* old_pos;   // [S][cap32]
-  float* old_ema;     // [S][cap32]
-  float* old_prio;    // [S][cap32]
+  // row state of both regions: old row i at [i], ring slot r at [cap32 + r]
+  int32_t* row_pos;   // [S][rows_max]
+  float* row_ema;     // [S][rows_max]
+  float* row_prio;    // [S][rows_max]
   int32_t* seg_nold;  // [S]
   uint64_t* seg_stats;  // [S][kStatFields]
   float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
