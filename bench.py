@@ -268,7 +268,7 @@ def main():
         "config": {
             "workload": args.workload, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": d,
             "vocab": w["vocab"], "prefill": w["prefill"], "policy": w["policy"],
-            "n_low": w["n_low"], "n_high": w["n_high"], "protect_last": w["protect_last"],
+            "n_low": w.get("n_low"), "n_high": w.get("n_high"), "protect_last": w["protect_last"],
             "fp16_window": w["fp16_window"], "num_sink": w["num_sink"], "kvpop_k": w["kvpop_k"],
             "pyramid": w["pyramid"], "kv_storage": "fp16 window + int8 older rows" if w["old_int8"] else "fp16",
             "seed": args.seed,
