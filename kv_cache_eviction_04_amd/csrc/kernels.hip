@@ -314,7 +314,9 @@ __device__ __forceinline__ void row_confidence(const Layout& lay, const Params& 
       mst_merge_f(pm, pS, pT, P.m, (float)P.S, (float)P.T);
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
+  // lanes >= chunks hold empty partials; with at most 32 chunks the upper
+  // half of the wave has nothing to contribute
+  for (int o = lay.chunks > 32 ? 32 : 16; o > 0; o >>= 1) {
     const float o1 = __shfl_xor(a1, o, 64), o2 = __shfl_xor(a2, o, 64);
     top2_merge(a1, a2, o1, o2);
     badall |= __shfl_xor(badall, o, 64);
@@ -931,6 +933,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   // p_gi = (hi + lo) / (scale_i * f) from the stored weight. Keys overwrite
   // planes 0/1 of the row just read (same thread).
   uint32_t n_live = 0, n_elig = 0;
+  const float inv_t1 = 1.0f / (float)(t + 1);  // recency (pos+1)/(t+1) as a product, within an ulp
   for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
     if (i0 != tid) load_rows(i0);
 #pragma unroll
@@ -945,7 +948,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
         if (pos >= 0) {
           ++n_live;
           if (!kvpop) {
-            const float inv_scf = 1.0f / (row_scale(i, ksv[u]) * fscale);
+            const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
             float mass = 0.0f;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -956,11 +959,8 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
             }
             mass *= inv_scf * (1.0f / (float)G);
             const float e = par.beta * ev_u + (1.0f - par.beta) * mass;
-            if (i < n_old)
-              oema[i] = e;
-            else
-              rema[i - n_old32] = e;
-            const float rec = (float)(pos + 1) / (float)(t + 1);
+            oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
+            const float rec = (float)(pos + 1) * inv_t1;
             score = par.alpha * e + (1.0f - par.alpha) * rec;
           } else {
             score = ev_u;
