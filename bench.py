@@ -152,6 +152,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-steps", type=int, default=50,
+                    help="steps of the per-layer call sequence (attend per layer, then evict) timed after the "
+                         "fused steps; 0 skips it")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -247,6 +250,52 @@ def main():
         f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic"
         + ("" if reduce_avg_ms is None else f"; reducer {reduce_avg_ms * 1e3:.1f} us"))
 
+    # The same step as a model's layer loop issues it: one attend launch per
+    # layer, then the reducer and the evict launch. Python issues 33 calls a
+    # step, so the wall clock is host-bound; the device time per step is the
+    # sum of the kernels' event-timed durations.
+    split = None
+    if args.split_steps > 0:
+        sp_inputs = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(args.split_steps + 1)]
+
+        def run_split(x):
+            for l in range(L):
+                gpu.attend(l, x["q"][l], x["k"][l], x["v"][l], None if x["prio"] is None else x["prio"][l],
+                           out=out[l])
+            gpu.evict(x["logits"])
+
+        run_split(sp_inputs[0])
+        torch.cuda.synchronize()
+        gpu.profile(True)
+        for k in gpu.KERNELS:
+            gpu.profile_kernel(k, reset=True)
+        t_sp = time.perf_counter()
+        for x in sp_inputs[1:]:
+            run_split(x)
+        torch.cuda.synchronize()
+        sp_wall = time.perf_counter() - t_sp
+        gpu.profile(False)
+        step_i += args.split_steps + 1
+        att_ms, att_n = gpu.profile_kernel("attend")
+        ev_ms, ev_n = gpu.profile_kernel("evict")
+        red_ms, red_n = gpu.profile_kernel("reduce")
+        dev_ms = (att_ms + ev_ms + red_ms) / args.split_steps
+        if gpu.status() != confkv.OK:
+            log("device status after the per-layer steps is not OK")
+            sys.exit(1)
+        split = {
+            "steps": args.split_steps,
+            "device_ms_per_step": dev_ms,
+            "device_steps_per_s": 1e3 / dev_ms,
+            "attend_avg_us": att_ms / max(att_n, 1) * 1e3,
+            "evict_avg_us": ev_ms / max(ev_n, 1) * 1e3,
+            "reducer_avg_us": red_ms / red_n * 1e3 if red_n else None,
+            "launches_per_step": L + 1 + (1 if red_n else 0),
+            "wall_ms_per_step": sp_wall * 1e3 / args.split_steps,
+        }
+        log(f"per-layer calls: {dev_ms:.4f} ms/step of kernels (attend {split['attend_avg_us']:.1f} us x {L}, "
+            f"evict {split['evict_avg_us']:.1f} us), wall {split['wall_ms_per_step']:.3f} ms/step")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
@@ -294,6 +343,7 @@ def main():
             "avg_launch_us": fused_avg_ms * 1e3,
         },
         "cpu_baseline": cpu,
+        "per_layer_calls": split,
     }
     print(json.dumps(res), flush=True)
 

@@ -142,6 +142,37 @@ int confkv_step(confkv_handle* h, void* stream, const float* logits, const uint1
                 const uint16_t* k_new, const uint16_t* v_new, const float* prio_new, uint16_t* out,
                 float* conf_out, int32_t* budget_out);
 
+/* The same step split at the layer boundary, for a model whose layer l+1
+ * takes its queries from layer l's output. In the pages' decoding loop the
+ * model first runs every layer on the new token, extending each layer's
+ * cache and producing the logits; then each layer updates its EMA and evicts
+ * down to the budget that the logits' confidence picks ("Conf-KV" post,
+ * decoding-loop pseudocode). So:
+ *
+ * confkv_attend(layer) appends the new row to that layer's segments, attends
+ * over them and updates their EMA (steps 2 and 3 of confkv_step, one layer):
+ *   q         [B][Hq][d]  fp16   the layer's queries at position t
+ *   k_new     [B][Hkv][d] fp16   the layer's new key row (pos = t)
+ *   v_new     [B][Hkv][d] fp16
+ *   prio_new  [B][Hkv]    fp32   KVPOP: as in confkv_step; CONF: NULL
+ *   out       [B][Hq][d]  fp16   attention output (written)
+ * Each layer attends once per step, in any order. EINVAL (nothing enqueued)
+ * for a layer out of range or already attended at this position.
+ *
+ * confkv_evict, after every layer has attended at position t, runs the
+ * confidence reduction (CONF), ranks, selects, compacts and ages out for
+ * every segment (steps 1, 4 and 5), then moves to position t + 1. logits,
+ * conf_out and budget_out are those of confkv_step. EINVAL (nothing enqueued)
+ * while a layer has not attended at t.
+ *
+ * confkv_attend for every layer followed by confkv_evict leaves the state,
+ * outputs, confidences and budgets bit-identical to one confkv_step on the
+ * same inputs. confkv_step returns EINVAL between the first confkv_attend of
+ * a position and its confkv_evict. Both only enqueue work. */
+int confkv_attend(confkv_handle* h, void* stream, int32_t layer, const uint16_t* q, const uint16_t* k_new,
+                  const uint16_t* v_new, const float* prio_new, uint16_t* out);
+int confkv_evict(confkv_handle* h, void* stream, const float* logits, float* conf_out, int32_t* budget_out);
+
 /* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
  * ascending position order. Per segment i, rows 0..len[i]-1 of each
  * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max
@@ -173,12 +204,16 @@ int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, int32_t reset
 
 /* Profiling of the step's kernels with HIP events on the step's stream.
  * confkv_profile(h, 1) starts recording an event pair around each launch of
- * the fused attend+evict kernel and of the logits reducer;
- * confkv_profile_read synchronizes and writes HOST values: total milliseconds
- * and launch counts of each, then (if reset) clears them. */
+ * the fused attend+evict kernel of confkv_step, of the logits reducer (of
+ * confkv_step and confkv_evict), and of the kernels of confkv_attend and
+ * confkv_evict; confkv_profile_read synchronizes and writes HOST values: total
+ * milliseconds and launch counts of the fused kernel and of the reducer, then
+ * (if reset) clears them. confkv_profile_kernel does the same for one kernel:
+ * 0 fused step, 1 logits reducer, 2 attend, 3 evict (EINVAL otherwise). */
 int confkv_profile(confkv_handle* h, int32_t enable);
 int confkv_profile_read(confkv_handle* h, double* fused_ms, int64_t* fused_launches, double* reduce_ms,
                         int64_t* reduce_launches, int32_t reset);
+int confkv_profile_kernel(confkv_handle* h, int32_t kernel, double* ms, int64_t* launches, int32_t reset);
 
 /* Position the next confkv_step decodes. -1 for a NULL handle. */
 int64_t confkv_position(const confkv_handle* h);

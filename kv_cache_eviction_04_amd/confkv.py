@@ -51,12 +51,15 @@ def lib():
         "confkv_rows_max": (c_int32, [POINTER(Config)]),
         "confkv_init": (c_int, [POINTER(Config), P, c_size_t, P, P, P, c_int32, POINTER(P)]),
         "confkv_step": (c_int, [P, P, P, P, P, P, P, P, P, P]),
+        "confkv_attend": (c_int, [P, P, c_int32, P, P, P, P, P]),
+        "confkv_evict": (c_int, [P, P, P, P, P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
         "confkv_stats": (c_int, [P, P, POINTER(c_uint64), c_int32]),
         "confkv_profile": (c_int, [P, c_int32]),
         "confkv_profile_read": (c_int, [P, POINTER(c_double), POINTER(c_int64), POINTER(c_double),
                                         POINTER(c_int64), c_int32]),
+        "confkv_profile_kernel": (c_int, [P, c_int32, POINTER(c_double), POINTER(c_int64), c_int32]),
         "confkv_position": (c_int64, [P]),
         "confkv_status": (c_int, [P]),
         "confkv_destroy": (c_int, [P]),
@@ -71,8 +74,9 @@ def lib():
 
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
+            "confkv_attend", "confkv_evict",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
-            "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
+            "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
 
 class ConfKVError(RuntimeError):
@@ -174,6 +178,39 @@ class Cache:
                                  _ptr(out), _ptr(conf_out), _ptr(budget_out)), "confkv_step")
         return out
 
+    def attend(self, layer, q, k, v, prio=None, out=None):
+        """Append, attention and EMA update of one layer at the current position."""
+        c, dev = self.cfg, self.device
+        B, Hq, H, d = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        _expect(q, (B, Hq, d), torch.float16, dev, "q")
+        _expect(k, (B, H, d), torch.float16, dev, "k")
+        _expect(v, (B, H, d), torch.float16, dev, "v")
+        if c.policy == POLICY_KVPOP:
+            _expect(prio, (B, H), torch.float32, dev, "prio")
+        elif prio is not None:
+            raise ValueError("CONF takes no priorities")
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+        _expect(out, (B, Hq, d), torch.float16, dev, "out")
+        _check(lib().confkv_attend(self.h, self._stream(), int(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(prio),
+                                   _ptr(out)), "confkv_attend")
+        return out
+
+    def evict(self, logits=None, conf_out=None, budget_out=None):
+        """Confidence, ranking, eviction, compaction and age-out of every
+        segment once all layers have attended; moves to the next position."""
+        c, dev = self.cfg, self.device
+        if c.policy == POLICY_CONF:
+            _expect(logits, (c.batch, c.vocab), torch.float32, dev, "logits")
+        elif logits is not None:
+            raise ValueError("KVpop takes no logits")
+        if conf_out is not None:
+            _expect(conf_out, (c.batch,), torch.float32, dev, "conf_out")
+        if budget_out is not None:
+            _expect(budget_out, (c.batch,), torch.int32, dev, "budget_out")
+        _check(lib().confkv_evict(self.h, self._stream(), _ptr(logits), _ptr(conf_out), _ptr(budget_out)),
+               "confkv_evict")
+
     def read_cache(self, seg_first=0, seg_count=None):
         """Logical contents (ascending position) of a segment range, as torch
         tensors on the device; rows >= len[i] are zero."""
@@ -214,6 +251,15 @@ class Cache:
         _check(lib().confkv_profile_read(self.h, ctypes.byref(fm), ctypes.byref(fn), ctypes.byref(rm),
                                          ctypes.byref(rn), int(reset)), "confkv_profile_read")
         return dict(fused_ms=fm.value, fused_launches=fn.value, reduce_ms=rm.value, reduce_launches=rn.value)
+
+    KERNELS = ("step", "reduce", "attend", "evict")
+
+    def profile_kernel(self, kernel, reset=True):
+        """(total ms, launches) of one profiled kernel: step, reduce, attend or evict."""
+        ms, n = c_double(), c_int64()
+        _check(lib().confkv_profile_kernel(self.h, self.KERNELS.index(kernel), ctypes.byref(ms), ctypes.byref(n),
+                                           int(reset)), "confkv_profile_kernel")
+        return ms.value, n.value
 
     def status(self) -> int:
         return int(lib().confkv_status(self.h))

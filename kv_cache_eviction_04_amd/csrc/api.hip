@@ -49,6 +49,9 @@ struct confkv_handle {
   hipStream_t last_stream;
   int prof;
   EventPool pf, pr;    // fused kernel, logits reducer
+  EventPool pa, pe;    // attend kernel, evict kernel
+  std::vector<uint8_t> attended;  // per layer: attended at position t by confkv_attend
+  int32_t n_attended;             // layers attended at t (0: no split step under way)
 };
 
 namespace {
@@ -221,6 +224,31 @@ int collect(EventPool& pool) {
   return 0;
 }
 
+// Staging of a launch: LDS planes sized for the most rows a segment can hold
+// at this step, or the HBM stage when they do not fit.
+struct Staging {
+  bool use_lds;
+  int32_t lds_rows;
+  int lds_bytes;
+};
+
+Staging staging(const confkv_handle* h, int planes) {
+  const Layout& lay = h->lay;
+  const int64_t old32 = (std::min<int64_t>(h->rows_bound, lay.cap) + 31) & ~(int64_t)31;
+  const int64_t lds_rows = old32 + lay.Wr32;
+  const int64_t lds_bytes = lds_rows * planes * 4;
+  Staging st;
+  st.use_lds = lds_bytes <= fused_max_dynamic_lds();
+  st.lds_rows = st.use_lds ? (int32_t)lds_rows : 0;
+  st.lds_bytes = st.use_lds ? (int)lds_bytes : 0;
+  return st;
+}
+
+void advance(confkv_handle* h) {
+  h->t += 1;
+  h->rows_bound = std::min(h->rows_bound + 1, h->keep_max);
+}
+
 int device_status(confkv_handle* h) {
   if (hipStreamSynchronize(h->last_stream) != hipSuccess) {
     h->poisoned = 1;
@@ -279,6 +307,8 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   h->poisoned = 0;
   h->last_stream = (hipStream_t)stream;
   h->prof = 0;
+  h->attended.assign((size_t)cfg->num_layers, 0);
+  h->n_attended = 0;
   if (launch_init(h->lay, h->par, state, carve(cfg, nullptr, nullptr), prefill_k, prefill_v, prefill_len, stream) !=
       0) {
     h->magic = kDead;
@@ -303,6 +333,7 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
   if (conf && (!logits || prio_new)) return CONFKV_EINVAL;
   if (!conf && (logits || !prio_new || conf_out || budget_out)) return CONFKV_EINVAL;
   if (h->t >= (int64_t)INT32_MAX - 1) return CONFKV_EINVAL;
+  if (h->n_attended) return CONFKV_EINVAL;  // a split step is under way
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
   const Layout& lay = h->lay;
@@ -314,6 +345,7 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
   {
     StepArgs a;
     a.t = (int32_t)h->t;
+    a.seg0 = 0;
     a.q = q;
     a.k_new = k_new;
     a.v_new = v_new;
@@ -321,22 +353,87 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
     a.out = out;
     a.conf_out = conf_out;
     a.budget_out = budget_out;
-    const int64_t old32 = (std::min<int64_t>(h->rows_bound, lay.cap) + 31) & ~(int64_t)31;
-    const int64_t lds_rows = old32 + lay.Wr32;
-    const int64_t lds_bytes = lds_rows * lay.planes * 4;
-    const bool use_lds = lds_bytes <= fused_max_dynamic_lds();
-    a.lds_rows = use_lds ? (int32_t)lds_rows : 0;
-    if (!use_lds && !lay.stage) return CONFKV_EINVAL;  // cannot happen: carve sized the staging
+    const Staging sg = staging(h, lay.planes);
+    a.lds_rows = sg.lds_rows;
+    if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;  // cannot happen: carve sized the staging
     if (record_event(h, h->pf, s, true)) goto hip_fail;
-    if (launch_fused_step(lay, h->par, a, use_lds, use_lds ? (int)lds_bytes : 0, stream) != 0) goto hip_fail;
+    if (launch_fused_step(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0) goto hip_fail;
     if (record_event(h, h->pf, s, false)) goto hip_fail;
   }
-  h->t += 1;
-  h->rows_bound = std::min(h->rows_bound + 1, h->keep_max);
+  advance(h);
   return CONFKV_OK;
 hip_fail:
   h->poisoned = 1;
   return CONFKV_EHIP;
+}
+
+CONFKV_API int confkv_attend(confkv_handle* h, void* stream, int32_t layer, const uint16_t* q,
+                             const uint16_t* k_new, const uint16_t* v_new, const float* prio_new, uint16_t* out) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  if (!q || !k_new || !v_new || !out) return CONFKV_EINVAL;
+  const bool conf = h->cfg.policy == CONFKV_POLICY_CONF;
+  if (conf == (prio_new != nullptr)) return CONFKV_EINVAL;
+  if (layer < 0 || layer >= h->lay.L || h->attended[(size_t)layer]) return CONFKV_EINVAL;
+  if (h->t >= (int64_t)INT32_MAX - 1) return CONFKV_EINVAL;
+  const Layout& lay = h->lay;
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.t = (int32_t)h->t;
+  a.seg0 = layer * lay.B * lay.Hkv;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.prio_new = prio_new;
+  a.out = out;
+  const Staging sg = staging(h, lay.planes);
+  a.lds_rows = sg.lds_rows;
+  if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  if (record_event(h, h->pa, s, true) || launch_attend(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0 ||
+      record_event(h, h->pa, s, false)) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  h->attended[(size_t)layer] = 1;
+  h->n_attended += 1;
+  return CONFKV_OK;
+}
+
+CONFKV_API int confkv_evict(confkv_handle* h, void* stream, const float* logits, float* conf_out,
+                            int32_t* budget_out) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  const bool conf = h->cfg.policy == CONFKV_POLICY_CONF;
+  if (conf && !logits) return CONFKV_EINVAL;
+  if (!conf && (logits || conf_out || budget_out)) return CONFKV_EINVAL;
+  if (h->n_attended != h->lay.L) return CONFKV_EINVAL;  // every layer attends before the eviction
+  const Layout& lay = h->lay;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  if (conf && (record_event(h, h->pr, s, true) || launch_conf_reduce(lay, logits, stream) != 0 ||
+               record_event(h, h->pr, s, false))) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.t = (int32_t)h->t;
+  a.conf_out = conf_out;
+  a.budget_out = budget_out;
+  const Staging sg = staging(h, 4);  // keys (two planes) and the compaction lists
+  a.lds_rows = sg.lds_rows;
+  if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
+  if (record_event(h, h->pe, s, true) || launch_evict(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0 ||
+      record_event(h, h->pe, s, false)) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  std::fill(h->attended.begin(), h->attended.end(), (uint8_t)0);
+  h->n_attended = 0;
+  advance(h);
+  return CONFKV_OK;
 }
 
 CONFKV_API int confkv_read_cache(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count, int32_t* len,
@@ -419,6 +516,25 @@ CONFKV_API int confkv_profile_read(confkv_handle* h, double* fused_ms, int64_t* 
   return CONFKV_OK;
 }
 
+CONFKV_API int confkv_profile_kernel(confkv_handle* h, int32_t kernel, double* ms, int64_t* launches,
+                                    int32_t reset) {
+  if (!live(h)) return CONFKV_ESTATE;
+  EventPool* pools[4] = {&h->pf, &h->pr, &h->pa, &h->pe};
+  if (kernel < 0 || kernel > 3) return CONFKV_EINVAL;
+  EventPool& p = *pools[kernel];
+  if (collect(p)) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  if (ms) *ms = p.ms;
+  if (launches) *launches = p.n;
+  if (reset) {
+    p.ms = 0.0;
+    p.n = 0;
+  }
+  return CONFKV_OK;
+}
+
 CONFKV_API int64_t confkv_position(const confkv_handle* h) { return live(h) ? h->t : -1; }
 
 CONFKV_API int confkv_status(confkv_handle* h) {
@@ -434,6 +550,8 @@ CONFKV_API int confkv_destroy(confkv_handle* h) {
   }
   for (hipEvent_t e : h->pf.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->pr.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->pa.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->pe.ev) (void)hipEventDestroy(e);
   h->magic = kDead;
   delete h;
   return CONFKV_OK;

@@ -494,8 +494,10 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
 
 // One workgroup per segment. Stage-row index space: old rows [0, n_old32)
 // (rows >= n_old are padding), ring slots [n_old32, n_old32 + Wr32).
-template <int D, int G, bool kLds>
+template <int D, int G, bool kLds, int MODE>
 __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_step_kernel(Layout lay, Params par, StepArgs a) {
+  constexpr bool kAtt = MODE != kModeEvict;  // append, attention, output (and the EMA update)
+  constexpr bool kEv = MODE != kModeAttend;  // keys, selection, compaction, age-out
   constexpr int LPR = D / 16;          // lanes per row for row-wise work
   constexpr int RPB = kThreads / LPR;  // rows per block iteration for row-wise work
   constexpr int KS = D / 32;           // MFMA k-steps over d
@@ -521,7 +523,10 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rg = tid / LPR;
   const int lq = lane >> 4, lj = lane & 15;  // MFMA lane coordinates
-  const int seg = blockIdx.x;
+  // Attend launches cover one layer (segments seg0 .. seg0 + B*Hkv - 1, its
+  // inputs indexed from 0); the other modes cover every segment.
+  const int si = blockIdx.x;
+  const int seg = MODE == kModeAttend ? a.seg0 + si : si;
   const int b = (seg / lay.Hkv) % lay.B, l = seg / (lay.Hkv * lay.B);
   const int t = a.t, Wr = lay.Wr, Wr32 = lay.Wr32, ob = lay.old_bytes;
   const bool kvpop = par.policy == 1;
@@ -558,168 +563,15 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
     st.rs = lay.rows_max;
   }
 
-  // ---- q as MFMA A operands (row g = lane%16; zero rows g >= G). INT8 K tiles
-  // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
-  const uint16_t* qrow = a.q + ((size_t)seg * G + (lj < G ? lj : 0)) * D;
-  half8 qa8[KS], qa16[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-    qa16[kk] = lj < G ? as_h8(u16) : half8{};
-  }
-
-  // ---- the new row (pos t): its data is loaded now and appended to the ring
-  // after the ring QK (below), so these loads do not hold up the first tiles.
+  // The new row (pos t) goes to ring slot t mod Wr; the row at t - W leaves
+  // the FP16 window at the end of the step; under KVpop the row at t - w gets
+  // its priority now.
   const int slot_new = t % Wr;
   const int pos_out = t - lay.W;
-  const uint16_t* kn = a.k_new + (size_t)seg * D;
-  const int pos_prio = (kvpop && t - par.P >= par.s) ? t - par.P : -1;  // row whose priority arrives now
-  const float prio_now = pos_prio >= 0 ? a.prio_new[seg] : 0.0f;
-  const uint4 kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
-  const uint16_t vn1 = a.v_new[(size_t)seg * D + tid % D];
-  const int32_t pos_prio_slot = pos_prio >= 0 ? rpos[pos_prio % Wr] : -1;
+  const int pos_prio = (kvpop && t - par.P >= par.s) ? t - par.P : -1;
+  float prio_now = 0.0f;
 
-  // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
-  // lane (lq, lj) receives S[4*lq + r][row lj]. The ring goes first (its
-  // tiles do not depend on the old-region count), then the old region. Each
-  // wave takes a contiguous share of the tiles, stages s in LDS and keeps a
-  // running max per head.
-  const float sm = par.sm_scale;
-  float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float sv_max = 0.0f;
-  {
-    const int nt_ring = (Wr + 15) >> 4;  // tiles wholly past slot Wr-1 are skipped
-    const int ta = (wave * nt_ring) >> 2, tb = ((wave + 1) * nt_ring) >> 2;
-    pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
-        ta, tb,
-        [&](int tt, QK16Buf<KS>& bf) {
-          const int r = 16 * tt + lj;
-          const uint16_t* kr = r == slot_new ? kn : rk + (size_t)r * D;
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
-          bf.pr = rpos[r];
-        },
-        [&](int tt, const QK16Buf<KS>& bf) {
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
-          const int r = 16 * tt + lj;
-          const bool valid = r < Wr && (bf.pr >= 0 || r == slot_new);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int g = 4 * lq + rr;
-            if (g < G) {
-              const float sc = valid ? acc[rr] * sm : -INFINITY;
-              st.at(g, n_old32 + r) = sc;
-              mrun[rr] = fmaxf(mrun[rr], sc);
-            }
-          }
-        });
-    // ring slots past the last QK tile
-    for (int r = tid + 16 * nt_ring; r < Wr32; r += kThreads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
-  }
-  // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
-  // previous row (pos t - Wr) left the window at the end of the last step.
-  // Nothing reads these stores back before a barrier: the ring QK took the
-  // new row's K from k_new, and the row-state passes substitute its position,
-  // EMA and (KVpop) the delayed priority.
-  if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
-  if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
-  if (tid == 0) {
-    rpos[slot_new] = t;
-    rema[slot_new] = 0.0f;
-    rprio[slot_new] = 0.0f;
-    // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
-    // priority now, as it stops being protected.
-    if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
-    sh_out_live = 0;
-  }
-
-  const int nt_old = n_old32 >> 4;
-  {
-    const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
-    if (par.old_int8) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
-        qa8[kk] = lj < G ? as_h8(u8) : half8{};
-      }
-      pipelined<CONFKV_QK8_NPB, QK8Buf>(
-          ta, tb,
-          [&](int tt, QK8Buf& bf) {
-            const int row = 16 * tt + lj;
-            const uint8_t* kr = okp + (size_t)row * D;
-            bf.k0 = ldnt4(kr + 16 * lq);
-            if constexpr (D == 128) bf.k1 = ldnt4(kr + 16 * (lq + 4));
-            bf.sk = oks[row];
-            bf.sv = ovs[row];
-          },
-          [&](int tt, const QK8Buf& bf) {
-            half8 b0, b1;
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            i8x16_to_h8(bf.k0, b0, b1);
-            acc = mfma16(qa8[0], b0, acc);
-            acc = mfma16(qa8[1], b1, acc);
-            if constexpr (D == 128) {
-              half8 b2, b3;
-              i8x16_to_h8(bf.k1, b2, b3);
-              acc = mfma16(qa8[2], b2, acc);
-              acc = mfma16(qa8[3], b3, acc);
-            }
-            const int row = 16 * tt + lj;
-            const bool valid = row < n_old;
-            if (valid) sv_max = fmaxf(sv_max, bf.sv);
-            const float f = bf.sk * sm;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int g = 4 * lq + r;
-              if (g < G) {
-                const float sc = valid ? acc[r] * f : -INFINITY;
-                st.at(g, row) = sc;
-                mrun[r] = fmaxf(mrun[r], sc);
-              }
-            }
-          });
-    } else {
-      pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
-          ta, tb,
-          [&](int tt, QK16Buf<KS>& bf) {
-            const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)(16 * tt + lj) * D;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
-          },
-          [&](int tt, const QK16Buf<KS>& bf) {
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
-            const int row = 16 * tt + lj;
-            const bool valid = row < n_old;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int g = 4 * lq + r;
-              if (g < G) {
-                const float sc = valid ? acc[r] * sm : -INFINITY;
-                st.at(g, row) = sc;
-                mrun[r] = fmaxf(mrun[r], sc);
-              }
-            }
-          });
-    }
-  }
-  // per-head maxima: over the 16 lanes of each lane group, then per wave
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float m = mrun[r];
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const int g = 4 * lq + r;
-    if (lj == 0 && g < G) red_m[wave][g] = m;
-  }
-  sv_max = wave_max(sv_max);
-  if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
-
-  // prefetch of this thread's first rows for the weight and key passes
+  // rows of this thread in flight in the weight and key passes
   int32_t kpos[KB];
   float kev[KB], ksv[KB];
   // Row state of stage row i sits at one index of the unified row arrays
@@ -738,172 +590,361 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
       ksv[u] = ovs[min(i, lay.cap32 - 1)];
     }
   };
-  // the raw loaded state of stage row i, masked: position (-1: no row), EMA or priority
+  // the raw loaded state of stage row i, masked: position (-1: no row), EMA or
+  // priority. Until the attend pass has stored the new row's state (an evict
+  // launch comes after it), the new row and the delayed priority are
+  // substituted here.
   auto row_state = [&](int i, int32_t pl, float el, int32_t& p, float& ev) {
     const int r = i - n_old32;
     const bool is_old = i < n_old, is_ring = r >= 0 && r < Wr;
-    p = is_old ? pl : (is_ring ? (r == slot_new ? t : pl) : -1);
-    ev = (is_old || (is_ring && r != slot_new)) ? el : 0.0f;
-    if (kvpop && is_ring && p == pos_prio && p >= 0) ev = prio_now;
+    if constexpr (MODE == kModeEvict) {
+      p = (is_old || is_ring) ? pl : -1;
+      ev = el;
+    } else {
+      p = is_old ? pl : (is_ring ? (r == slot_new ? t : pl) : -1);
+      ev = (is_old || (is_ring && r != slot_new)) ? el : 0.0f;
+      if (kvpop && is_ring && p == pos_prio && p >= 0) ev = prio_now;
+    }
   };
-  load_rows(tid);
-  __syncthreads();
-  float M[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = red_m[0][g];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) m = fmaxf(m, red_m[w][g]);
-    M[g] = m;
-  }
-  float svm = 0.0f;
-  for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
-  // PV weights are prescaled by a power of two that keeps p*sV*f below 2^14
-  // (fp16 range) while lifting small weights out of the fp16 subnormals.
-  int fexp = 10;
-  if (svm > 0.0f) {
-    int e2;
-    frexpf(svm, &e2);
-    fexp = min(10, max(-30, 14 - e2));
-  }
-  const float fscale = ldexpf(1.0f, fexp), finv = ldexpf(1.0f, -fexp);
-
-  // ---- weight pass, once per (row, head): p = exp(s - M_g), l_g = sum p, and
-  // the PV weight w = p * scale * f stored in place of s as an fp16 pair
-  // (hi | lo << 16) with hi + lo = w to about 22 bits. scale is the row's V
-  // scale for INT8 rows with a nonzero scale, else 1.
-  float lpart[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
   auto row_scale = [&](int i, float sv) { return (i < n_old && par.old_int8 && sv > 0.0f) ? sv : 1.0f; };
-  for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
-    if (i0 != tid) load_rows(i0);
+  float inv_l[G];  // 1 / sum of p per head (attention)
+  float finv = 1.0f;  // 1 / the power-of-two prescale of the PV weights
+  if constexpr (!kAtt) {
+    if (tid == 0) sh_out_live = 0;
+  }
+
+  if constexpr (kAtt) {
+    // ---- q as MFMA A operands (row g = lane%16; zero rows g >= G). INT8 K tiles
+    // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
+    const uint16_t* qrow = a.q + ((size_t)si * G + (lj < G ? lj : 0)) * D;
+    half8 qa8[KS], qa16[KS];
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int i = i0 + kThreads * u;
-      if (i < rows) {
-        const float scf = row_scale(i, ksv[u]) * fscale;
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
+      qa16[kk] = lj < G ? as_h8(u16) : half8{};
+    }
+
+    // ---- the new row (pos t): its data is loaded now and appended to the ring
+    // after the ring QK (below), so these loads do not hold up the first tiles.
+    const uint16_t* kn = a.k_new + (size_t)si * D;
+    if (pos_prio >= 0) prio_now = a.prio_new[si];
+    const uint4 kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
+    const uint16_t vn1 = a.v_new[(size_t)si * D + tid % D];
+    const int32_t pos_prio_slot = pos_prio >= 0 ? rpos[pos_prio % Wr] : -1;
+
+    // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
+    // lane (lq, lj) receives S[4*lq + r][row lj]. The ring goes first (its
+    // tiles do not depend on the old-region count), then the old region. Each
+    // wave takes a contiguous share of the tiles, stages s in LDS and keeps a
+    // running max per head.
+    const float sm = par.sm_scale;
+    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float sv_max = 0.0f;
+    {
+      const int nt_ring = (Wr + 15) >> 4;  // tiles wholly past slot Wr-1 are skipped
+      const int ta = (wave * nt_ring) >> 2, tb = ((wave + 1) * nt_ring) >> 2;
+      pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+          ta, tb,
+          [&](int tt, QK16Buf<KS>& bf) {
+            const int r = 16 * tt + lj;
+            const uint16_t* kr = r == slot_new ? kn : rk + (size_t)r * D;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p = __expf(st.at(g, i) - M[g]);
-          lpart[g] += p;
-          const float wv = p * scf;
-          const _Float16 hi = (_Float16)wv, lo = (_Float16)(wv - (float)hi);
-          st.at(g, i) = __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                                                      ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+            for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+            bf.pr = rpos[r];
+          },
+          [&](int tt, const QK16Buf<KS>& bf) {
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
+            const int r = 16 * tt + lj;
+            const bool valid = r < Wr && (bf.pr >= 0 || r == slot_new);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int g = 4 * lq + rr;
+              if (g < G) {
+                const float sc = valid ? acc[rr] * sm : -INFINITY;
+                st.at(g, n_old32 + r) = sc;
+                mrun[rr] = fmaxf(mrun[rr], sc);
+              }
+            }
+          });
+      // ring slots past the last QK tile
+      for (int r = tid + 16 * nt_ring; r < Wr32; r += kThreads)
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
+    }
+    // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
+    // previous row (pos t - Wr) left the window at the end of the last step.
+    // Nothing reads these stores back before a barrier: the ring QK took the
+    // new row's K from k_new, and the row-state passes substitute its position,
+    // EMA and (KVpop) the delayed priority.
+    if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
+    if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
+    if (tid == 0) {
+      rpos[slot_new] = t;
+      rema[slot_new] = 0.0f;
+      rprio[slot_new] = 0.0f;
+      // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
+      // priority now, as it stops being protected.
+      if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
+      sh_out_live = 0;
+    }
+
+    const int nt_old = n_old32 >> 4;
+    {
+      const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
+      if (par.old_int8) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
+          qa8[kk] = lj < G ? as_h8(u8) : half8{};
+        }
+        pipelined<CONFKV_QK8_NPB, QK8Buf>(
+            ta, tb,
+            [&](int tt, QK8Buf& bf) {
+              const int row = 16 * tt + lj;
+              const uint8_t* kr = okp + (size_t)row * D;
+              bf.k0 = ldnt4(kr + 16 * lq);
+              if constexpr (D == 128) bf.k1 = ldnt4(kr + 16 * (lq + 4));
+              bf.sk = oks[row];
+              bf.sv = ovs[row];
+            },
+            [&](int tt, const QK8Buf& bf) {
+              half8 b0, b1;
+              floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+              i8x16_to_h8(bf.k0, b0, b1);
+              acc = mfma16(qa8[0], b0, acc);
+              acc = mfma16(qa8[1], b1, acc);
+              if constexpr (D == 128) {
+                half8 b2, b3;
+                i8x16_to_h8(bf.k1, b2, b3);
+                acc = mfma16(qa8[2], b2, acc);
+                acc = mfma16(qa8[3], b3, acc);
+              }
+              const int row = 16 * tt + lj;
+              const bool valid = row < n_old;
+              if (valid) sv_max = fmaxf(sv_max, bf.sv);
+              const float f = bf.sk * sm;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int g = 4 * lq + r;
+                if (g < G) {
+                  const float sc = valid ? acc[r] * f : -INFINITY;
+                  st.at(g, row) = sc;
+                  mrun[r] = fmaxf(mrun[r], sc);
+                }
+              }
+            });
+      } else {
+        pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+            ta, tb,
+            [&](int tt, QK16Buf<KS>& bf) {
+              const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)(16 * tt + lj) * D;
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+            },
+            [&](int tt, const QK16Buf<KS>& bf) {
+              floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
+              const int row = 16 * tt + lj;
+              const bool valid = row < n_old;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int g = 4 * lq + r;
+                if (g < G) {
+                  const float sc = valid ? acc[r] * sm : -INFINITY;
+                  st.at(g, row) = sc;
+                  mrun[r] = fmaxf(mrun[r], sc);
+                }
+              }
+            });
+      }
+    }
+    // per-head maxima: over the 16 lanes of each lane group, then per wave
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = mrun[r];
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      const int g = 4 * lq + r;
+      if (lj == 0 && g < G) red_m[wave][g] = m;
+    }
+    sv_max = wave_max(sv_max);
+    if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
+
+    load_rows(tid);
+    __syncthreads();
+    float M[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = red_m[0][g];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) m = fmaxf(m, red_m[w][g]);
+      M[g] = m;
+    }
+    float svm = 0.0f;
+    for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
+    // PV weights are prescaled by a power of two that keeps p*sV*f below 2^14
+    // (fp16 range) while lifting small weights out of the fp16 subnormals.
+    int fexp = 10;
+    if (svm > 0.0f) {
+      int e2;
+      frexpf(svm, &e2);
+      fexp = min(10, max(-30, 14 - e2));
+    }
+    const float fscale = ldexpf(1.0f, fexp);
+    finv = ldexpf(1.0f, -fexp);
+
+    // ---- weight pass, once per (row, head): p = exp(s - M_g), l_g = sum p, and
+    // the PV weight w = p * scale * f stored in place of s as an fp16 pair
+    // (hi | lo << 16) with hi + lo = w to about 22 bits. scale is the row's V
+    // scale for INT8 rows with a nonzero scale, else 1.
+    float lpart[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+    for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
+      if (i0 != tid) load_rows(i0);
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + kThreads * u;
+        if (i < rows) {
+          const float scf = row_scale(i, ksv[u]) * fscale;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float p = __expf(st.at(g, i) - M[g]);
+            lpart[g] += p;
+            const float wv = p * scf;
+            const _Float16 hi = (_Float16)wv, lo = (_Float16)(wv - (float)hi);
+            st.at(g, i) = __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                                                        ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+          }
         }
       }
     }
-  }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float v = wave_sum(lpart[g]);
-    if (lane == 0) red_l[wave][g] = v;
-  }
-  __syncthreads();
-  float Lsum[G], inv_l[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    Lsum[g] = red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g];
-    inv_l[g] = 1.0f / Lsum[g];
-  }
-  // 1/l of the output rows 4*lq + r (lane-varying head index: from LDS)
-  float il4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * lq + r;
-    if (g < G) il4[r] = 1.0f / (red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g]);
-  }
-
-  // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
-  // with A = w as its fp16 hi and lo parts and B = V from the transposed
-  // tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj]. Waves split the
-  // columns: wave w owns column blocks CBW*w .. CBW*w+CBW-1 and streams every
-  // row, so no cross-wave reduction is needed.
-  floatx4 O[CBW];
-#pragma unroll
-  for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto weights = [&](int srow, half8& ahi, half8& alo) {
-    if (lj < G) {
-      const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
-      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
-                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
-                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
-                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
-      uint4 h, lw;
-      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
-      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
-      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
-      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
-      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
-      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
-      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
-      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
-      ahi = as_h8(h);
-      alo = as_h8(lw);
-    } else {
-      ahi = half8{};
-      alo = half8{};
+    for (int g = 0; g < G; ++g) {
+      const float v = wave_sum(lpart[g]);
+      if (lane == 0) red_l[wave][g] = v;
     }
-  };
-  auto pv16 = [&](const uint16_t* vbase, int srow0, int ntiles) {
-    pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
-        0, ntiles,
-        [&](int tt, PV16Buf<CBW>& bf) {
-          const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * lane;
+    __syncthreads();
+    float Lsum[G];
 #pragma unroll
-          for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
-        },
-        [&](int tt, const PV16Buf<CBW>& bf) {
-          half8 ahi, alo;
-          weights(srow0 + 32 * tt + 8 * lq, ahi, alo);
-#pragma unroll
-          for (int k = 0; k < CBW; ++k) {
-            O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
-            O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
-          }
-        });
-  };
-  const int nv_old = n_old32 >> 5;
-  auto load_pv8 = [&](int tt, PV8Buf& bf) {
-    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
-    if constexpr (CBW == 2) {
-      bf.v = ldnt4(tb + 1024 * wave);
-    } else {
-      const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-      bf.v = make_uint4(h.x, h.y, 0u, 0u);
+    for (int g = 0; g < G; ++g) {
+      Lsum[g] = red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g];
+      inv_l[g] = 1.0f / Lsum[g];
     }
-  };
-  if (par.old_int8) {
-    auto pv8 = [&](int tt, const PV8Buf& bf) {
-      half8 ahi, alo, blo, bhi;
-      weights(32 * tt + 8 * lq, ahi, alo);
-      i8x16_to_h8(bf.v, blo, bhi);
-      O[0] = mfma16(ahi, blo, O[0]);
-      O[0] = mfma16(alo, blo, O[0]);
-      if constexpr (CBW == 2) {
-        O[1] = mfma16(ahi, bhi, O[1]);
-        O[1] = mfma16(alo, bhi, O[1]);
-      }
-    };
-    pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, pv8);
-  } else {
-    pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old);
-  }
-  pv16(rvt, n_old32, (Wr + 31) >> 5);
-#pragma unroll
-  for (int k = 0; k < CBW; ++k) {
+    // 1/l of the output rows 4*lq + r (lane-varying head index: from LDS)
+    float il4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * lq + r;
-      if (g < G) {
-        const int col = 16 * (CBW * wave + k) + lj;
-        a.out[((size_t)seg * G + g) * D + col] = f2h(O[k][r] * finv * il4[r]);
+      if (g < G) il4[r] = 1.0f / (red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g]);
+    }
+
+    // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
+    // with A = w as its fp16 hi and lo parts and B = V from the transposed
+    // tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj]. Waves split the
+    // columns: wave w owns column blocks CBW*w .. CBW*w+CBW-1 and streams every
+    // row, so no cross-wave reduction is needed.
+    floatx4 O[CBW];
+#pragma unroll
+    for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto weights = [&](int srow, half8& ahi, half8& alo) {
+      if (lj < G) {
+        const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
+        const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
+                                __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
+                                __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
+                                __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
+        uint4 h, lw;
+        h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
+        h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
+        h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
+        h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
+        lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
+        lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
+        lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
+        lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
+        ahi = as_h8(h);
+        alo = as_h8(lw);
+      } else {
+        ahi = half8{};
+        alo = half8{};
+      }
+    };
+    auto pv16 = [&](const uint16_t* vbase, int srow0, int ntiles) {
+      pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
+          0, ntiles,
+          [&](int tt, PV16Buf<CBW>& bf) {
+            const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * lane;
+#pragma unroll
+            for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
+          },
+          [&](int tt, const PV16Buf<CBW>& bf) {
+            half8 ahi, alo;
+            weights(srow0 + 32 * tt + 8 * lq, ahi, alo);
+#pragma unroll
+            for (int k = 0; k < CBW; ++k) {
+              O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
+              O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
+            }
+          });
+    };
+    const int nv_old = n_old32 >> 5;
+    auto load_pv8 = [&](int tt, PV8Buf& bf) {
+      const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * lane;
+      if constexpr (CBW == 2) {
+        bf.v = ldnt4(tb + 1024 * wave);
+      } else {
+        const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+        bf.v = make_uint4(h.x, h.y, 0u, 0u);
+      }
+    };
+    if (par.old_int8) {
+      auto pv8 = [&](int tt, const PV8Buf& bf) {
+        half8 ahi, alo, blo, bhi;
+        weights(32 * tt + 8 * lq, ahi, alo);
+        i8x16_to_h8(bf.v, blo, bhi);
+        O[0] = mfma16(ahi, blo, O[0]);
+        O[0] = mfma16(alo, blo, O[0]);
+        if constexpr (CBW == 2) {
+          O[1] = mfma16(ahi, bhi, O[1]);
+          O[1] = mfma16(alo, bhi, O[1]);
+        }
+      };
+      pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, pv8);
+    } else {
+      pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old);
+    }
+    pv16(rvt, n_old32, (Wr + 31) >> 5);
+#pragma unroll
+    for (int k = 0; k < CBW; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * lq + r;
+        if (g < G) {
+          const int col = 16 * (CBW * wave + k) + lj;
+          a.out[((size_t)si * G + g) * D + col] = f2h(O[k][r] * finv * il4[r]);
+        }
       }
     }
-  }
+    if (par.record && tid == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) lay.rec_lse[(size_t)seg * G + g] = M[g] + logf(Lsum[g]);
+    }
 
-  if (rows > kThreads * KB) {  // the key pass starts again from the first rows
+  }  // attention
+
+  // An attend launch under KVpop has no per-row pass left: the priorities
+  // need no update and the ranking waits for the evict launch.
+  if constexpr (MODE == kModeAttend) {
+    if (kvpop) {
+      if (tid == 0 && n_old != n_old_raw) atomicOr(lay.err, kErrInternal);
+      return;
+    }
+  }
+  // the row pass starts from the first rows again (an evict launch loads them here first)
+  if (MODE == kModeEvict || rows > kThreads * KB) {
     int i0 = tid;
     asm volatile("" : "+v"(i0));  // recompute the addresses rather than keep them live
     load_rows(i0);
@@ -916,7 +957,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   uint32_t aro[16];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) aro[jj] = 0u;
-  if (pos_out >= 0 && wave == 0 && lane < 2 * LPR) {
+  if (kEv && pos_out >= 0 && wave == 0 && lane < 2 * LPR) {
     const int slot = pos_out % Wr, cc = lane % LPR;
     const bool isv = lane >= LPR;
     const uint16_t* src = isv ? rvt + vt16(slot, 16 * cc, D) : rk + (size_t)slot * D + cc * 16;
@@ -926,12 +967,15 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   }
   // this row's logits partials, merged by wave 0 after the key pass
   ConfPartial part0;
-  if (!kvpop && wave == 0 && lane < lay.chunks) part0 = lay.partials[(size_t)b * lay.chunks + lane];
-  __syncthreads();  // every wave's PV has read the weights that the keys overwrite
+  if (kEv && !kvpop && wave == 0 && lane < lay.chunks) part0 = lay.partials[(size_t)b * lay.chunks + lane];
+  // every wave's PV has read the weights that the keys overwrite (evict: the
+  // flag sh_out_live is cleared)
+  if constexpr (kEv) __syncthreads();
   // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
   // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
   // p_gi = (hi + lo) / (scale_i * f) from the stored weight. Keys overwrite
-  // planes 0/1 of the row just read (same thread).
+  // planes 0/1 of the row just read (same thread). An attend launch stops at
+  // the EMA; an evict launch takes the EMA the attend launches stored.
   uint32_t n_live = 0, n_elig = 0;
   const float inv_t1 = 1.0f / (float)(t + 1);  // recency (pos+1)/(t+1) as a product, within an ulp
   for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
@@ -948,39 +992,50 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
         if (pos >= 0) {
           ++n_live;
           if (!kvpop) {
-            const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
-            float mass = 0.0f;
+            float e = ev_u;
+            if constexpr (kAtt) {
+              const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
+              float mass = 0.0f;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
-              const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
-                               (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
-              mass = fmaf(wv, inv_l[g], mass);
+              for (int g = 0; g < G; ++g) {
+                const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
+                const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
+                                 (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+                mass = fmaf(wv, inv_l[g], mass);
+              }
+              mass *= inv_scf * (1.0f / (float)G);
+              e = par.beta * ev_u + (1.0f - par.beta) * mass;
+              oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
             }
-            mass *= inv_scf * (1.0f / (float)G);
-            const float e = par.beta * ev_u + (1.0f - par.beta) * mass;
-            oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
             const float rec = (float)(pos + 1) * inv_t1;
             score = par.alpha * e + (1.0f - par.alpha) * rec;
           } else {
             score = ev_u;
           }
-          const bool elig = pos >= par.s && pos <= t - par.P;
-          if (!isfinite(score)) {
-            atomicOr(lay.err, kErrNonFinite);
-          } else if (elig) {
-            key = rank_key(score, pos);
-            ++n_elig;
+          if constexpr (kEv) {
+            const bool elig = pos >= par.s && pos <= t - par.P;
+            if (!isfinite(score)) {
+              atomicOr(lay.err, kErrNonFinite);
+            } else if (elig) {
+              key = rank_key(score, pos);
+              ++n_elig;
+            }
+            if (pos == pos_out && i >= n_old32) sh_out_live = 1;
           }
-          if (pos == pos_out && i >= n_old32) sh_out_live = 1;
         }
-        st.set_key(i, key);
-        if (par.record) {
-          lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
-          lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
+        if constexpr (kEv) {
+          st.set_key(i, key);
+          if (par.record) {
+            lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
+            lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
+          }
         }
       }
     }
+  }
+  if constexpr (MODE == kModeAttend) {
+    if (tid == 0 && n_old != n_old_raw) atomicOr(lay.err, kErrInternal);
+    return;
   }
   if (!kvpop && wave == 0) {
     float cval;
@@ -1209,8 +1264,6 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
       mp[1] = (int32_t)n_live;
       mp[2] = budget;
       mp[3] = (int32_t)e;
-#pragma unroll
-      for (int g = 0; g < G; ++g) lay.rec_lse[(size_t)seg * G + g] = M[g] + logf(Lsum[g]);
     }
   }
 }
@@ -1421,35 +1474,54 @@ int launch_conf_reduce(const Layout& lay, const float* logits, void* stream) {
   return ok_or_err();
 }
 
-template <int D, int G>
-static void launch_fused_dg(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
-                            hipStream_t s) {
+template <int D, int G, int MODE>
+static void launch_fused_dg(const Layout& lay, const Params& par, const StepArgs& a, int grid, bool use_lds,
+                            int lds_bytes, hipStream_t s) {
   if (use_lds)
-    hipLaunchKernelGGL((fused_step_kernel<D, G, true>), dim3(lay.S), dim3(kThreads), lds_bytes, s, lay, par, a);
+    hipLaunchKernelGGL((fused_step_kernel<D, G, true, MODE>), dim3(grid), dim3(kThreads), lds_bytes, s, lay, par, a);
   else
-    hipLaunchKernelGGL((fused_step_kernel<D, G, false>), dim3(lay.S), dim3(kThreads), 0, s, lay, par, a);
+    hipLaunchKernelGGL((fused_step_kernel<D, G, false, MODE>), dim3(grid), dim3(kThreads), 0, s, lay, par, a);
 }
 
-template <int D>
-static int launch_fused_d(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
-                          hipStream_t s) {
-  switch (lay.G) {
-    case 1: launch_fused_dg<D, 1>(lay, par, a, use_lds, lds_bytes, s); break;
-    case 2: launch_fused_dg<D, 2>(lay, par, a, use_lds, lds_bytes, s); break;
-    case 4: launch_fused_dg<D, 4>(lay, par, a, use_lds, lds_bytes, s); break;
-    case 5: launch_fused_dg<D, 5>(lay, par, a, use_lds, lds_bytes, s); break;
-    case 8: launch_fused_dg<D, 8>(lay, par, a, use_lds, lds_bytes, s); break;
-    default: return -1;
+template <int D, int MODE>
+static int launch_fused_d(const Layout& lay, const Params& par, const StepArgs& a, int grid, bool use_lds,
+                          int lds_bytes, hipStream_t s) {
+  if constexpr (MODE == kModeEvict) {  // no per-head work: one instance serves every group size
+    launch_fused_dg<D, 1, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
+  } else {
+    switch (lay.G) {
+      case 1: launch_fused_dg<D, 1, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+      case 2: launch_fused_dg<D, 2, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+      case 4: launch_fused_dg<D, 4, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+      case 5: launch_fused_dg<D, 5, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+      case 8: launch_fused_dg<D, 8, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+      default: return -1;
+    }
   }
   return ok_or_err();
 }
 
+template <int MODE>
+static int launch_mode(const Layout& lay, const Params& par, const StepArgs& a, int grid, bool use_lds, int lds_bytes,
+                       hipStream_t s) {
+  if (lay.D == 64) return launch_fused_d<64, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
+  if (lay.D == 128) return launch_fused_d<128, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
+  return -1;
+}
+
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                       void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (lay.D == 64) return launch_fused_d<64>(lay, par, a, use_lds, lds_bytes, s);
-  if (lay.D == 128) return launch_fused_d<128>(lay, par, a, use_lds, lds_bytes, s);
-  return -1;
+  return launch_mode<kModeStep>(lay, par, a, lay.S, use_lds, lds_bytes, (hipStream_t)stream);
+}
+
+int launch_attend(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
+                  void* stream) {
+  return launch_mode<kModeAttend>(lay, par, a, lay.B * lay.Hkv, use_lds, lds_bytes, (hipStream_t)stream);
+}
+
+int launch_evict(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
+                 void* stream) {
+  return launch_mode<kModeEvict>(lay, par, a, lay.S, use_lds, lds_bytes, (hipStream_t)stream);
 }
 
 int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, int32_t* len, int32_t* pos,

@@ -28,6 +28,10 @@ constexpr int kThreads = 256;          // fused-step workgroup
 constexpr int kChunk = 4096;           // logits per reducer workgroup (256 x 16)
 constexpr int kStatFields = 4;         // kv bytes, rows attended, rows moved, rows evicted
 constexpr uint32_t kErrNonFinite = 1u, kErrCapacity = 2u, kErrInternal = 4u;
+// What one launch of the step kernel covers: the whole step for every
+// segment; append + attention + EMA for one layer; or ranking, selection,
+// compaction and age-out for every segment after all layers have attended.
+enum { kModeStep = 0, kModeAttend = 1, kModeEvict = 2 };
 
 struct ConfPartial {                   // one logits chunk: m = top1
   double S;                            // sum exp(z - m)
@@ -81,14 +85,15 @@ struct Params {
 
 struct StepArgs {
   int32_t t;                 // position decoded this step
+  int32_t seg0;              // attend: first segment of the layer (inputs are that layer's)
   int32_t lds_rows;          // staged-row capacity of the LDS planes (LDS variant)
-  const uint16_t* q;         // [L][B][Hq][D]
-  const uint16_t* k_new;     // [L][B][Hkv][D]
+  const uint16_t* q;         // [L][B][Hq][D] (attend: [B][Hq][D])
+  const uint16_t* k_new;     // [L][B][Hkv][D] (attend: [B][Hkv][D])
   const uint16_t* v_new;
-  const float* prio_new;     // [L][B][Hkv] or null
-  uint16_t* out;             // [L][B][Hq][D]
-  float* conf_out;           // [B] or null (CONF)
-  int32_t* budget_out;       // [B] or null (CONF)
+  const float* prio_new;     // [L][B][Hkv] (attend: [B][Hkv]) or null
+  uint16_t* out;             // [L][B][Hq][D] (attend: [B][Hq][D])
+  float* conf_out;           // [B] or null (CONF; step and evict)
+  int32_t* budget_out;       // [B] or null (CONF; step and evict)
 };
 
 // Launchers (kernels.hip). All enqueue on `stream` and return the launch status.
@@ -97,6 +102,10 @@ int launch_init(const Layout& lay, const Params& par, void* state, size_t state_
 int launch_conf_reduce(const Layout& lay, const float* logits, void* stream);
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                       void* stream);
+int launch_attend(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
+                  void* stream);
+int launch_evict(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
+                 void* stream);
 int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, int32_t* len, int32_t* pos,
                       float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8, int8_t* v8,
                       float* ks, float* vs, uint8_t* is8, int32_t old_int8, void* stream);

@@ -1,0 +1,135 @@
+"""The decode step split at the layer boundary (confkv_attend for each layer,
+then confkv_evict) against the one-call confkv_step on identical inputs.
+
+Both calls sequences compute the same arithmetic in the same order, so the
+bar is bit-identity at every step: attention outputs, confidences, base
+budgets, the recorded ranking values and LSEs, and the whole logical cache
+(positions, EMA, priorities, FP16 rows, INT8 codes and scales). The fused
+step itself is held to the oracle by the parity tests; this file pins the
+split to it. Layers attend in a different order each step, since nothing
+ties one layer's cache to another's.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_lockstep import DEV, log
+from kv_cache_eviction_04_amd import confkv, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def wl(name, **over):
+    w = synth.workload(name)
+    w.update(over)
+    return w
+
+
+def twins(w, seed):
+    pk, pv = synth.prefill(w, seed, DEV) if w["prefill"] else (None, None)
+    fused = confkv.Cache(w, pk, pv, record=True)
+    split = confkv.Cache(w, pk, pv, record=True)
+    return fused, split
+
+
+def same(a, b, what):
+    if a.dtype.is_floating_point:  # NaN-marked entries compare by bits
+        a = a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16)
+        b = b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16)
+    assert torch.equal(a, b), what
+
+
+def compare(fused, split, step):
+    ra, rb = fused.read_cache(), split.read_cache()
+    for k in ra:
+        same(ra[k], rb[k], f"step {step}: cache field {k}")
+    la, lb = fused.read_last_step(), split.read_last_step()
+    for k in la:
+        same(la[k], lb[k], f"step {step}: last-step field {k}")
+
+
+def drive(w, steps, seed=0, compare_every=1):
+    fused, split = twins(w, seed)
+    L, B = w["num_layers"], w["batch"]
+    conf = w["policy"] != "kvpop"
+    rng = np.random.default_rng(seed)
+    for i in range(steps):
+        x = synth.step_inputs(w, seed, i, DEV)
+        ca = cb = ba = bb = None
+        if conf:
+            ca, cb = torch.zeros(B, device=DEV), torch.zeros(B, device=DEV)
+            ba, bb = torch.zeros(B, dtype=torch.int32, device=DEV), torch.zeros(B, dtype=torch.int32, device=DEV)
+        out_a = fused.step(x["logits"], x["q"], x["k"], x["v"], x["prio"], conf_out=ca, budget_out=ba)
+        out_b = torch.empty_like(out_a)
+        for l in rng.permutation(L):
+            split.attend(int(l), x["q"][l], x["k"][l], x["v"][l], None if x["prio"] is None else x["prio"][l],
+                         out=out_b[l])
+        split.evict(x["logits"], conf_out=cb, budget_out=bb)
+        same(out_a, out_b, f"step {i}: attention output")
+        if conf:
+            same(ca, cb, f"step {i}: confidence")
+            same(ba, bb, f"step {i}: budget")
+        if i % compare_every == 0 or i == steps - 1:
+            compare(fused, split, i)
+    assert fused.position == split.position
+    assert fused.stats() == split.stats()
+    assert fused.status() == confkv.OK and split.status() == confkv.OK
+    log(f"{w['name']}: split == fused over {steps} steps")
+    return fused, split
+
+
+def test_split_toy_stream():
+    # window fill, steady eviction, age-out; one layer
+    drive(wl("toy"), 120)
+
+
+def test_split_pyramid_layers_and_prefill():
+    # several layers with pyramidal budgets; the first step evicts from a prefill
+    drive(wl("gpt2_small", num_layers=3, prefill=300, n_low=64, n_high=128, protect_last=16,
+             fp16_window=32), 12, seed=1)
+
+
+def test_split_hbm_staged_first_step():
+    # GQA 32/8, d 128: a 5000-row prefill is staged in HBM on the first step
+    # (radix select), then LDS-staged
+    drive(wl("llama3_8b_32k", num_layers=2, batch=2, prefill=5000), 4, seed=2)
+
+
+def test_split_group5_and_degenerate_cases():
+    drive(wl("qwen32b", num_layers=2, batch=2, prefill=200), 6, seed=3)
+    drive(wl("toy", fp16_window=0, prefill=70), 10, seed=4)      # every row INT8 right after its step
+    drive(wl("toy", old_int8=False, prefill=100), 10, seed=5)    # FP16-only storage
+    drive(wl("toy", n_low=4, n_high=6, protect_last=16, num_sink=3, prefill=40), 10, seed=6)
+
+
+def test_split_kvpop():
+    # delayed priorities arrive through the attend launch; fill-up and eviction
+    w = wl("kvpop_qwen3_8b", num_layers=2, batch=2, protect_last=32, fp16_window=32, kvpop_k=60)
+    drive(w, 130, seed=7, compare_every=16)
+
+
+def test_split_call_order_is_enforced():
+    w = wl("toy", num_layers=2, prefill=50)
+    fused, split = twins(w, 8)
+    x = synth.step_inputs(w, 8, 0, DEV)
+    out = torch.empty_like(x["q"])
+    with pytest.raises(confkv.ConfKVError) as e:
+        split.evict(x["logits"])                       # no layer has attended
+    assert e.value.code == confkv.EINVAL
+    split.attend(1, x["q"][1], x["k"][1], x["v"][1], out=out[1])
+    for bad in (lambda: split.attend(1, x["q"][1], x["k"][1], x["v"][1], out=out[1]),  # twice
+                lambda: split.attend(2, x["q"][1], x["k"][1], x["v"][1], out=out[1]),  # out of range
+                lambda: split.evict(x["logits"]),                                    # layer 0 missing
+                lambda: split.step(x["logits"], x["q"], x["k"], x["v"])):           # step mid-split
+        with pytest.raises(confkv.ConfKVError) as e:
+            bad()
+        assert e.value.code == confkv.EINVAL
+    assert split.position == 50
+    # the rejected calls left the state as it was: finishing the step matches the fused one
+    split.attend(0, x["q"][0], x["k"][0], x["v"][0], out=out[0])
+    split.evict(x["logits"])
+    ref = fused.step(x["logits"], x["q"], x["k"], x["v"])
+    same(ref, out, "output after rejected calls")
+    compare(fused, split, 0)
+    assert split.position == 51 and split.status() == confkv.OK
