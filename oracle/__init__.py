@@ -31,6 +31,7 @@ Modules:
     policy      EMA, recency, composite score, protected-window eviction
     kvpop       sink + window + top-k fixed budget over static priorities
     cache       the whole per-step loop over every (layer, batch, kv-head)
+    sampling    the next token from p = softmax(logits): greedy or inverse-CDF
 """
 
-from . import confidence, attention, quant, policy, kvpop, cache  # noqa: F401
+from . import confidence, attention, quant, policy, kvpop, cache, sampling  # noqa: F401
