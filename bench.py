@@ -296,6 +296,30 @@ def main():
         log(f"per-layer calls: {dev_ms:.4f} ms/step of kernels (attend {split['attend_avg_us']:.1f} us x {L}, "
             f"evict {split['evict_avg_us']:.1f} us), wall {split['wall_ms_per_step']:.3f} ms/step")
 
+    # The next-token draw from this step's logits (greedy and inverse-CDF),
+    # timed with events on the stream it runs on.
+    sampling = None
+    if w["policy"] == "conf":
+        x = synth.step_inputs(w, args.seed, step_i, dev)
+        u = torch.rand((B,), generator=torch.Generator(device=dev).manual_seed(args.seed), device=dev)
+        tok = torch.empty((B,), dtype=torch.int32, device=dev)
+        sampling = {"logits_bytes": B * w["vocab"] * 4}
+        for name, uu in (("greedy", None), ("draw", u)):
+            gpu.sample(x["logits"], uu, out=tok)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 50
+            e0.record()
+            for _ in range(n):
+                gpu.sample(x["logits"], uu, out=tok)
+            e1.record()
+            torch.cuda.synchronize()
+            sampling[f"{name}_us"] = e0.elapsed_time(e1) * 1e3 / n
+        if gpu.status() != confkv.OK:
+            log("device status after sampling is not OK")
+            sys.exit(1)
+        log(f"sampling: greedy {sampling['greedy_us']:.1f} us, draw {sampling['draw_us']:.1f} us per call "
+            f"({sampling['logits_bytes'] / 1e6:.1f} MB of logits)")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
@@ -344,6 +368,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "per_layer_calls": split,
+        "sampling": sampling,
     }
     print(json.dumps(res), flush=True)
 

@@ -173,6 +173,25 @@ int confkv_attend(confkv_handle* h, void* stream, int32_t layer, const uint16_t*
                   const uint16_t* v_new, const float* prio_new, uint16_t* out);
 int confkv_evict(confkv_handle* h, void* stream, const float* logits, float* conf_out, int32_t* budget_out);
 
+/* The next token of each batch row from a step's logits: the decoding loop
+ * of the "Conf-KV" post ends each step by drawing x_t from the same
+ * p = softmax(logits) whose confidence set the budget (temperature 1, no
+ * truncation).
+ *   logits     [B][V] fp32
+ *   u          [B] fp32 in [0, 1), or NULL. NULL: greedy, the largest logit
+ *              (lowest index among equal maxima). Otherwise an inverse-CDF
+ *              draw: the smallest j with p_0 + ... + p_j > u[b], the sums
+ *              formed in binary64 (a u within about 1e-12 of a running sum
+ *              may land on either neighbour; where rounding leaves u past
+ *              the last sum, the last token with p_j > 0).
+ *   token_out  [B] int32 (written); -1 for a row holding a non-finite logit,
+ *              which also sets the sticky CONFKV_ENONFINITE.
+ * CONF only (EINVAL for KVPOP, which has no vocabulary). Touches no cache
+ * state, so it may come anywhere between steps; it shares a scratch area
+ * with nothing else but itself, so two draws on one handle must be ordered
+ * on one stream. Only enqueues work. */
+int confkv_sample(confkv_handle* h, void* stream, const float* logits, const float* u, int32_t* token_out);
+
 /* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
  * ascending position order. Per segment i, rows 0..len[i]-1 of each
  * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max

@@ -53,6 +53,7 @@ def lib():
         "confkv_step": (c_int, [P, P, P, P, P, P, P, P, P, P]),
         "confkv_attend": (c_int, [P, P, c_int32, P, P, P, P, P]),
         "confkv_evict": (c_int, [P, P, P, P, P]),
+        "confkv_sample": (c_int, [P, P, P, P, P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
         "confkv_stats": (c_int, [P, P, POINTER(c_uint64), c_int32]),
@@ -74,7 +75,7 @@ def lib():
 
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
-            "confkv_attend", "confkv_evict",
+            "confkv_attend", "confkv_evict", "confkv_sample",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
             "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
@@ -210,6 +211,18 @@ class Cache:
             _expect(budget_out, (c.batch,), torch.int32, dev, "budget_out")
         _check(lib().confkv_evict(self.h, self._stream(), _ptr(logits), _ptr(conf_out), _ptr(budget_out)),
                "confkv_evict")
+
+    def sample(self, logits, u=None, out=None):
+        """Next token per batch row: greedy (u None) or the inverse-CDF draw of u [B]."""
+        c, dev = self.cfg, self.device
+        _expect(logits, (c.batch, c.vocab), torch.float32, dev, "logits")
+        if u is not None:
+            _expect(u, (c.batch,), torch.float32, dev, "u")
+        if out is None:
+            out = torch.empty((c.batch,), dtype=torch.int32, device=dev)
+        _expect(out, (c.batch,), torch.int32, dev, "out")
+        _check(lib().confkv_sample(self.h, self._stream(), _ptr(logits), _ptr(u), _ptr(out)), "confkv_sample")
+        return out
 
     def read_cache(self, seg_first=0, seg_count=None):
         """Logical contents (ascending position) of a segment range, as torch

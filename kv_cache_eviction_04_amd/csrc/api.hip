@@ -152,6 +152,7 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();
   lay.stage = hbm_stage ? (float*)take(S * lay.planes * (size_t)lay.rows_max * 4) : nullptr;
   lay.partials = (ConfPartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(ConfPartial));
+  lay.spart = (SamplePartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(SamplePartial));
   lay.err = (uint32_t*)take(4);
   lay.stats_total = (uint64_t*)take(kStatFields * 8);
   if (c->record_scores) {
@@ -433,6 +434,19 @@ CONFKV_API int confkv_evict(confkv_handle* h, void* stream, const float* logits,
   std::fill(h->attended.begin(), h->attended.end(), (uint8_t)0);
   h->n_attended = 0;
   advance(h);
+  return CONFKV_OK;
+}
+
+CONFKV_API int confkv_sample(confkv_handle* h, void* stream, const float* logits, const float* u,
+                             int32_t* token_out) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  if (h->cfg.policy != CONFKV_POLICY_CONF || !logits || !token_out) return CONFKV_EINVAL;
+  h->last_stream = (hipStream_t)stream;
+  if (launch_sample(h->lay, logits, u, token_out, stream) != 0) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
   return CONFKV_OK;
 }
 

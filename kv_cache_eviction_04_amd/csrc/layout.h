@@ -40,6 +40,12 @@ struct ConfPartial {                   // one logits chunk: m = top1
   uint32_t nonfinite, pad;
 };
 
+struct SamplePartial {                 // one logits chunk for the next-token draw
+  double S;                            // sum exp(z - m) (only for a random draw)
+  float m;                             // the chunk's largest logit (NaN if idx < 0)
+  int32_t idx;                         // its lowest index; -1: a non-finite logit
+};
+
 struct Layout {
   int32_t L, B, Hq, Hkv, G, D, V;
   int32_t S;          // segments
@@ -69,6 +75,7 @@ struct Layout {
   float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
   // confidence reducer
   ConfPartial* partials;  // [B][chunks]
+  SamplePartial* spart;   // [B][chunks] (next-token draw)
   uint32_t* err;          // [1]
   uint64_t* stats_total;  // [kStatFields]
   // last-step record (record_scores)
@@ -100,6 +107,7 @@ struct StepArgs {
 int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
                 const uint16_t* pv, int32_t P0, void* stream);
 int launch_conf_reduce(const Layout& lay, const float* logits, void* stream);
+int launch_sample(const Layout& lay, const float* logits, const float* u, int32_t* token, void* stream);
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                       void* stream);
 int launch_attend(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
