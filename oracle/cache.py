@@ -61,6 +61,8 @@ class Config:
     kvpop_k: int = 0
     old_int8: bool = True
     softmax_scale: float = 0.0
+    ranker: str = "score"         # "score": alpha*ema + (1-alpha)*recency; "random": SplitMix64 ranks
+    seed: int = 0                 # seed of the random ranker
 
     @property
     def group(self) -> int:
@@ -169,15 +171,19 @@ class StepRecord:
     seg: dict = field(default_factory=dict)        # seg -> SegmentRecord
 
 
-def conf_segment_step(seg: Segment, t, qg, k_new, v_new, budget, cfg: Config, score_override=None):
-    """One CONF-KV step of one segment, in the pseudocode's order."""
+def conf_segment_step(seg: Segment, t, qg, k_new, v_new, budget, cfg: Config, score_override=None,
+                      segment_id=0):
+    """One CONF-KV step of one segment, in the pseudocode's order. With the
+    random ranker the EMA is still kept; only the ranking value changes."""
     seg.append(t, k_new, v_new, ema=0.0)
     K, V = seg.dequantized()
     o, lse, p = attention.attend_two_pass(qg, K, V, cfg.scale)
     mass = attention.attention_mass(p)
     seg.ema = policy.ema_update(seg.ema, mass, cfg.ema_beta)
-    score = policy.composite_score(seg.ema, policy.recency(seg.pos, t), cfg.alpha)
-    score32 = score.astype(np.float32)
+    if cfg.ranker == "random":
+        score32 = policy.random_rank(cfg.seed, t, segment_id, seg.pos)
+    else:
+        score32 = policy.composite_score(seg.ema, policy.recency(seg.pos, t), cfg.alpha).astype(np.float32)
     rank_by = score32 if score_override is None else np.asarray(score_override, np.float32)
     present = seg.pos.copy()
     victims = policy.select_victims(seg.pos, rank_by, t, budget, cfg.num_sink, cfg.protect_last)
@@ -259,7 +265,7 @@ class OracleCache:
             ov = None if overrides is None else overrides.get(s)
             if cfg.policy == "conf":
                 bud = confidence.layer_budget(rec.base[b], l, cfg.num_layers, cfg.pyramid)
-                rec.seg[s] = conf_segment_step(self.segs[s], t, qg, kn, vn, bud, cfg, ov)
+                rec.seg[s] = conf_segment_step(self.segs[s], t, qg, kn, vn, bud, cfg, ov, segment_id=s)
             else:
                 rec.seg[s] = kvpop_segment_step(self.segs[s], t, qg, kn, vn, float(prio[l][b][h]), cfg, ov)
         self.t = t + 1
