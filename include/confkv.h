@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CONFKV_ABI_VERSION 1
+#define CONFKV_ABI_VERSION 2
 
 enum {
   CONFKV_OK = 0,
@@ -67,6 +67,13 @@ enum {
 };
 
 enum { CONFKV_POLICY_CONF = 0, CONFKV_POLICY_KVPOP = 1 };
+
+/* How CONF ranks the rows inside the budget. The "Conf-KV" post's
+ * matched-rate ablation keeps the confidence-gated schedule and swaps the
+ * ranker: recency only (SCORE with alpha 0), attention only (SCORE with
+ * alpha 1), or random victims (RANDOM). A fixed-budget sliding window is
+ * SCORE with alpha 0 and n_low == n_high. */
+enum { CONFKV_RANKER_SCORE = 0, CONFKV_RANKER_RANDOM = 1 };
 
 typedef struct confkv_handle confkv_handle;
 
@@ -100,6 +107,14 @@ typedef struct confkv_config {
   float softmax_scale;     /* 0 -> 1/sqrt(d)                                       */
   int32_t record_scores;   /* 1: keep the last step's per-row positions, ranking
                               values and LSEs for confkv_read_last_step            */
+  int32_t ranker;          /* CONFKV_RANKER_SCORE: alpha * ema + (1 - alpha) *
+                              recency. CONFKV_RANKER_RANDOM (CONF only): every
+                              row gets a fresh uniform rank each step, the top
+                              24 bits of x = out(out(out(seed, t+1), seg+1),
+                              pos+1) times 2^-24, where out(k, n) is the n-th
+                              output of SplitMix64 (Steele, Lea and Flood 2014)
+                              started from state k; the EMA is still kept     */
+  uint32_t seed;           /* seed of CONFKV_RANKER_RANDOM                        */
 } confkv_config;
 
 /* Host-only check of a configuration with a given prefill length. Returns

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconfkv.s
 
 OK, EINVAL, ECAPACITY, EHIP, ENONFINITE, ESTATE = 0, -1, -2, -3, -4, -5
 POLICY_CONF, POLICY_KVPOP = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
+RANKER_SCORE, RANKER_RANDOM = 0, 1
 
 
 class Config(ctypes.Structure):
@@ -29,7 +30,7 @@ class Config(ctypes.Structure):
         ("fp16_window", c_int32), ("num_sink", c_int32), ("tau", c_float), ("alpha", c_float),
         ("ema_beta", c_float), ("w_entropy", c_float), ("w_margin", c_float), ("w_pmax", c_float),
         ("gate_literal", c_int32), ("pyramid", c_int32), ("kvpop_k", c_int32), ("old_int8", c_int32),
-        ("softmax_scale", c_float), ("record_scores", c_int32),
+        ("softmax_scale", c_float), ("record_scores", c_int32), ("ranker", c_int32), ("seed", ctypes.c_uint32),
     ]
 
 
@@ -108,6 +109,8 @@ def make_config(w: dict, capacity: int | None = None, record: bool = False) -> C
     c.old_int8 = int(bool(w.get("old_int8", True)))
     c.capacity = int(capacity if capacity is not None else default_capacity(w))
     c.record_scores = int(bool(record))
+    c.ranker = RANKER_RANDOM if w.get("ranker") == "random" else RANKER_SCORE
+    c.seed = int(w.get("seed", 0)) & 0xFFFFFFFF
     return c
 
 

@@ -89,6 +89,8 @@ int check_cfg(const confkv_config* c, int32_t P0) {
   if (c->policy != CONFKV_POLICY_CONF && c->policy != CONFKV_POLICY_KVPOP) return CONFKV_EINVAL;
   if (c->protect_last < 0 || c->fp16_window < 0 || c->num_sink < 0 || P0 < 0) return CONFKV_EINVAL;
   if (c->old_int8 != 0 && c->old_int8 != 1) return CONFKV_EINVAL;
+  if (c->ranker != CONFKV_RANKER_SCORE && c->ranker != CONFKV_RANKER_RANDOM) return CONFKV_EINVAL;
+  if (c->ranker == CONFKV_RANKER_RANDOM && c->policy != CONFKV_POLICY_CONF) return CONFKV_EINVAL;
   if (!finite_all({c->softmax_scale}) || c->softmax_scale < 0.0f) return CONFKV_EINVAL;
   if (c->policy == CONFKV_POLICY_CONF) {
     if (c->vocab < 2 || c->n_low < 0 || c->n_high < 0) return CONFKV_EINVAL;
@@ -185,6 +187,8 @@ Params make_params(const confkv_config* c) {
   p.pyramid = c->pyramid ? 1 : 0;
   p.old_int8 = c->old_int8;
   p.record = c->record_scores ? 1 : 0;
+  p.ranker = c->ranker;
+  p.seed = c->seed;
   return p;
 }
 

@@ -97,6 +97,17 @@ __device__ __forceinline__ uint64_t rank_key(float score, int32_t pos) {
   return ((uint64_t)orderable(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
 }
 
+// Random ranks for the random-victim ranker: SplitMix64 (Steele, Lea and
+// Flood, OOPSLA 2014). out(k, n) is the n-th output of the generator started
+// from state k: the state advances by the golden-ratio increment and the
+// output function applies two xor-shift-multiply rounds and an xor-shift.
+__device__ __forceinline__ uint64_t splitmix64_out(uint64_t k, uint64_t n) {
+  uint64_t z = k + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 // ------------------------------------------------------------ block helpers
 // 256 threads = 4 wavefronts of 64.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -1178,6 +1189,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
   // the EMA; an evict launch takes the EMA the attend launches stored.
   uint32_t n_live = 0, n_elig = 0;
   const float inv_t1 = 1.0f / (float)(t + 1);  // recency (pos+1)/(t+1) as a product, within an ulp
+  // random ranker: this step's and segment's generator state; a row's rank
+  // is the top 24 bits of out(k2, pos + 1) times 2^-24
+  const uint64_t rnd_k2 = splitmix64_out(splitmix64_out(par.seed, (uint64_t)t + 1), (uint64_t)seg + 1);
   for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
     if (i0 != tid) load_rows(i0);
 #pragma unroll
@@ -1207,8 +1221,12 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_ste
               e = par.beta * ev_u + (1.0f - par.beta) * mass;
               oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
             }
-            const float rec = (float)(pos + 1) * inv_t1;
-            score = par.alpha * e + (1.0f - par.alpha) * rec;
+            if (par.ranker == 0) {
+              const float rec = (float)(pos + 1) * inv_t1;
+              score = par.alpha * e + (1.0f - par.alpha) * rec;
+            } else {
+              score = (float)(uint32_t)(splitmix64_out(rnd_k2, (uint64_t)pos + 1) >> 40) * 0x1p-24f;
+            }
           } else {
             score = ev_u;
           }

@@ -88,6 +88,8 @@ struct Layout {
 struct Params {
   float tau, alpha, beta, w_e, w_m, w_p, sm_scale;
   int32_t n_low, n_high, P, s, kvpop_k, policy, gate_literal, pyramid, old_int8, record;
+  int32_t ranker;  // 0: alpha-blend score; 1: SplitMix64 random rank
+  uint32_t seed;
 };
 
 struct StepArgs {

@@ -135,6 +135,10 @@ class Lockstep:
             assert gpu_victims == set(sr.victims.tolist()), \
                 f"step {t} seg {s}: victims gpu {sorted(gpu_victims)[:10]} oracle {sorted(sr.victims.tolist())[:10]}"
             assert int(meta[3]) == len(sr.victims)
+            if cfg.policy == "conf" and cfg.ranker == "random":  # counter-based ranks: bit-exact
+                assert np.array_equal(overrides[s].view(np.uint32), sr.score32.view(np.uint32)), \
+                    f"step {t} seg {s}: random ranks differ"
+
             self.compare_state(s, oc.segs[s], post[s], t)
         return dict(t=t, worst_out=worst, orc=orc, post=post)
 

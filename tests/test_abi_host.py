@@ -49,7 +49,8 @@ def test_workloads_validate(name):
     ("head_dim", 96, confkv.EINVAL),
     ("vocab", 1, confkv.EINVAL),
     ("num_kv_heads", 0, confkv.EINVAL),
-    ("abi_version", 2, confkv.EINVAL),
+    ("abi_version", 1, confkv.EINVAL),
+    ("ranker", 2, confkv.EINVAL),
     ("capacity", 50, confkv.ECAPACITY),        # below the largest budget + 1
     ("policy", 7, confkv.EINVAL),
     ("tau", float("nan"), confkv.EINVAL),

@@ -104,6 +104,21 @@ def test_degenerate_cases():
     run(wl("toy", alpha=0.0, prefill=100), 10, seed=11)
 
 
+def test_ranker_variants_of_the_matched_rate_ablation():
+    # random victims (SplitMix64 ranks, compared bit-exactly) on one and on
+    # several segments; recency only with one fixed budget is a sliding window
+    run(wl("toy", ranker="random", seed=12345, prefill=100), 30, seed=13)
+    run(wl("qwen32b", num_layers=2, batch=2, ranker="random", seed=7), 6, seed=14)
+    N, s_ = 40, 2
+    w = wl("toy", alpha=0.0, n_low=N, n_high=N, num_sink=s_, protect_last=8, fp16_window=12, prefill=90)
+    ls = run(w, 25, seed=15, check_every=6)
+    t = ls.gpu.position - 1
+    ro = ls.gpu.read_cache(0, 4)
+    for seg in range(4):
+        n = int(ro["len"][seg])
+        assert ro["pos"][seg, :n].tolist() == list(range(s_)) + list(range(t - (N - s_) + 1, t + 1))
+
+
 def test_ragged_tails_and_many_evictions():
     # prefill not a multiple of any tile; budget drops force multi-row evictions
     run(wl("toy", prefill=331, n_low=37, n_high=77, protect_last=5, fp16_window=13), 40, seed=12)
