@@ -180,6 +180,7 @@ int confkv_step(confkv_handle* h, void* stream, const float* logits, const uint1
  * conf_out and budget_out are those of confkv_step. EINVAL (nothing enqueued)
  * while a layer has not attended at t.
  *
+ * With one workgroup per segment (confkv_set_attend_splits(h, 1)),
  * confkv_attend for every layer followed by confkv_evict leaves the state,
  * outputs, confidences and budgets bit-identical to one confkv_step on the
  * same inputs. confkv_step returns EINVAL between the first confkv_attend of
@@ -187,6 +188,22 @@ int confkv_step(confkv_handle* h, void* stream, const float* logits, const uint1
 int confkv_attend(confkv_handle* h, void* stream, int32_t layer, const uint16_t* q, const uint16_t* k_new,
                   const uint16_t* v_new, const float* prio_new, uint16_t* out);
 int confkv_evict(confkv_handle* h, void* stream, const float* logits, float* conf_out, int32_t* budget_out);
+
+/* One layer holds only B * Hkv segments, too few workgroups to fill the GPU
+ * when each takes a whole segment. confkv_attend therefore splits each
+ * segment's rows over several workgroups (split-K) and combines their
+ * partial softmax statistics and outputs by the log-sum-exp rule (CONF-KV
+ * abstract: blockwise online-softmax attention); the EMA is then updated
+ * from the combined normaliser. The split result equals the whole-segment
+ * one up to float rounding (not bit for bit).
+ * confkv_set_attend_splits: 0 (default) chooses the split count per call,
+ * 1 takes one workgroup per segment (bit-identical to confkv_step), 2..32
+ * asks for that many (raised where one split's rows would not fit on chip;
+ * one workgroup per segment where no count up to 32 fits). EINVAL outside
+ * 0..32. confkv_attend_splits returns the count the next confkv_attend will
+ * use (-1 for an unknown handle). Host-only. */
+int confkv_set_attend_splits(confkv_handle* h, int32_t splits);
+int32_t confkv_attend_splits(const confkv_handle* h);
 
 /* The next token of each batch row from a step's logits: the decoding loop
  * of the "Conf-KV" post ends each step by drawing x_t from the same

@@ -55,6 +55,8 @@ def lib():
         "confkv_attend": (c_int, [P, P, c_int32, P, P, P, P, P]),
         "confkv_evict": (c_int, [P, P, P, P, P]),
         "confkv_sample": (c_int, [P, P, P, P, P]),
+        "confkv_set_attend_splits": (c_int, [P, c_int32]),
+        "confkv_attend_splits": (c_int32, [P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
         "confkv_stats": (c_int, [P, P, POINTER(c_uint64), c_int32]),
@@ -76,7 +78,7 @@ def lib():
 
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
-            "confkv_attend", "confkv_evict", "confkv_sample",
+            "confkv_attend", "confkv_evict", "confkv_sample", "confkv_set_attend_splits", "confkv_attend_splits",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
             "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
@@ -199,6 +201,14 @@ class Cache:
         _check(lib().confkv_attend(self.h, self._stream(), int(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(prio),
                                    _ptr(out)), "confkv_attend")
         return out
+
+    def set_attend_splits(self, splits: int):
+        """0: automatic split-K for attend; 1: one workgroup per segment; 2..32: that many."""
+        _check(lib().confkv_set_attend_splits(self.h, int(splits)), "confkv_set_attend_splits")
+
+    @property
+    def attend_splits(self) -> int:
+        return int(lib().confkv_attend_splits(self.h))
 
     def evict(self, logits=None, conf_out=None, budget_out=None):
         """Confidence, ranking, eviction, compaction and age-out of every

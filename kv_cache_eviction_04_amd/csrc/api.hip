@@ -25,6 +25,9 @@ namespace {
 constexpr uint32_t kMagic = 0xC0F4B1E5u;
 constexpr uint32_t kDead = 0xDEADDEADu;
 constexpr int kMaxProfilePairs = 1 << 15;
+constexpr int kSplitMax = 32;        // most workgroups per segment in a split-K attend
+constexpr int kSplitTarget = 1024;   // workgroups an automatic split-K attend aims for (one per CU slot)
+constexpr int kSplitMinTiles = 4;    // 32-row tiles per split at least, when splitting for occupancy
 
 struct EventPool {
   std::vector<hipEvent_t> ev;  // pairs: start, stop
@@ -52,6 +55,7 @@ struct confkv_handle {
   EventPool pa, pe;    // attend kernel, evict kernel
   std::vector<uint8_t> attended;  // per layer: attended at position t by confkv_attend
   int32_t n_attended;             // layers attended at t (0: no split step under way)
+  int32_t attend_splits;          // 0: automatic; 1: one workgroup per segment; >= 2: that many
 };
 
 namespace {
@@ -153,6 +157,11 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   lay.seg_stats = (uint64_t*)take(S * kStatFields * 8);
   const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();
   lay.stage = hbm_stage ? (float*)take(S * lay.planes * (size_t)lay.rows_max * 4) : nullptr;
+  const size_t segs_l = (size_t)lay.B * lay.Hkv;
+  lay.ns_max = kSplitMax;
+  lay.sk_o = (float*)take(segs_l * kSplitMax * lay.G * D * 4);
+  lay.sk_ml = (SplitML*)take(segs_l * kSplitMax * lay.G * sizeof(SplitML));
+  lay.sk_s = (float*)take(segs_l * lay.G * (size_t)lay.rows_max * 4);
   lay.partials = (ConfPartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(ConfPartial));
   lay.spart = (SamplePartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(SamplePartial));
   lay.err = (uint32_t*)take(4);
@@ -249,6 +258,29 @@ Staging staging(const confkv_handle* h, int planes) {
   return st;
 }
 
+// Workgroups per segment for one layer's attend: 1 selects the whole-segment
+// kernel. Automatic: enough splits for about kSplitTarget workgroups, at least
+// kSplitMinTiles 32-row tiles per split, and few enough rows per split for
+// the LDS.
+int attend_splits(const confkv_handle* h) {
+  const Layout& lay = h->lay;
+  const int64_t segs = (int64_t)lay.B * lay.Hkv;
+  const int64_t tiles = ((std::min<int64_t>(h->rows_bound, lay.cap) + 31) >> 5) + (lay.Wr32 >> 5);
+  auto lds_ok = [&](int64_t ns) {
+    return ((tiles + ns - 1) / ns) * 32 * lay.G * 4 <= (int64_t)fused_max_dynamic_lds();
+  };
+  int64_t ns;
+  if (h->attend_splits == 1) return 1;
+  if (h->attend_splits >= 2) {
+    ns = std::min<int64_t>(h->attend_splits, tiles);
+  } else {
+    ns = std::min<int64_t>({(kSplitTarget + segs - 1) / segs, tiles / kSplitMinTiles, (int64_t)kSplitMax});
+  }
+  while (ns <= kSplitMax && ns >= 2 && !lds_ok(ns)) ++ns;
+  if (ns < 2 || ns > kSplitMax || !lds_ok(ns)) return 1;
+  return (int)ns;
+}
+
 void advance(confkv_handle* h) {
   h->t += 1;
   h->rows_bound = std::min(h->rows_bound + 1, h->keep_max);
@@ -314,6 +346,7 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   h->prof = 0;
   h->attended.assign((size_t)cfg->num_layers, 0);
   h->n_attended = 0;
+  h->attend_splits = 0;
   if (launch_init(h->lay, h->par, state, carve(cfg, nullptr, nullptr), prefill_k, prefill_v, prefill_len, stream) !=
       0) {
     h->magic = kDead;
@@ -391,19 +424,42 @@ CONFKV_API int confkv_attend(confkv_handle* h, void* stream, int32_t layer, cons
   a.v_new = v_new;
   a.prio_new = prio_new;
   a.out = out;
-  const Staging sg = staging(h, lay.planes);
-  a.lds_rows = sg.lds_rows;
-  if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
-  if (record_event(h, h->pa, s, true) || launch_attend(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0 ||
-      record_event(h, h->pa, s, false)) {
-    h->poisoned = 1;
-    return CONFKV_EHIP;
+  const int ns = attend_splits(h);
+  int rc;
+  if (ns >= 2) {
+    const int64_t tiles = ((std::min<int64_t>(h->rows_bound, lay.cap) + 31) >> 5) + (lay.Wr32 >> 5);
+    a.ns = ns;
+    a.lds_rows = (int32_t)(((tiles + ns - 1) / ns) * 32);
+    if (record_event(h, h->pa, s, true)) goto hip_fail;
+    rc = launch_attend_split(lay, h->par, a, a.lds_rows * lay.G * 4, stream);
+  } else {
+    const Staging sg = staging(h, lay.planes);
+    a.lds_rows = sg.lds_rows;
+    if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
+    if (record_event(h, h->pa, s, true)) goto hip_fail;
+    rc = launch_attend(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream);
   }
+  if (rc != 0 || record_event(h, h->pa, s, false)) goto hip_fail;
   h->attended[(size_t)layer] = 1;
   h->n_attended += 1;
   return CONFKV_OK;
+hip_fail:
+  h->poisoned = 1;
+  return CONFKV_EHIP;
+}
+
+CONFKV_API int confkv_set_attend_splits(confkv_handle* h, int32_t splits) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (splits < 0 || splits > kSplitMax) return CONFKV_EINVAL;
+  h->attend_splits = splits;
+  return CONFKV_OK;
+}
+
+CONFKV_API int32_t confkv_attend_splits(const confkv_handle* h) {
+  if (!live(h)) return -1;
+  return attend_splits(h);
 }
 
 CONFKV_API int confkv_evict(confkv_handle* h, void* stream, const float* logits, float* conf_out,

@@ -46,6 +46,11 @@ struct SamplePartial {                 // one logits chunk for the next-token dr
   int32_t idx;                         // its lowest index; -1: a non-finite logit
 };
 
+struct SplitML {                       // one split's softmax statistics for one head
+  float m;                             // maximum of its scores (-inf: no valid row)
+  float l;                             // sum of exp(s - m)
+};
+
 struct Layout {
   int32_t L, B, Hq, Hkv, G, D, V;
   int32_t S;          // segments
@@ -73,6 +78,11 @@ struct Layout {
   int32_t* seg_nold;  // [S]
   uint64_t* seg_stats;  // [S][kStatFields]
   float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
+  // split-K attend of one layer (reused by every layer)
+  int32_t ns_max;     // most splits per segment
+  float* sk_o;        // [B*Hkv][ns_max][G][D] unnormalised partial outputs
+  SplitML* sk_ml;     // [B*Hkv][ns_max][G]
+  float* sk_s;        // [B*Hkv][G][rows_max] raw attention scores
   // confidence reducer
   ConfPartial* partials;  // [B][chunks]
   SamplePartial* spart;   // [B][chunks] (next-token draw)
@@ -95,6 +105,7 @@ struct Params {
 struct StepArgs {
   int32_t t;                 // position decoded this step
   int32_t seg0;              // attend: first segment of the layer (inputs are that layer's)
+  int32_t ns;                // split-K attend: workgroups per segment
   int32_t lds_rows;          // staged-row capacity of the LDS planes (LDS variant)
   const uint16_t* q;         // [L][B][Hq][D] (attend: [B][Hq][D])
   const uint16_t* k_new;     // [L][B][Hkv][D] (attend: [B][Hkv][D])
@@ -112,6 +123,7 @@ int launch_conf_reduce(const Layout& lay, const float* logits, void* stream);
 int launch_sample(const Layout& lay, const float* logits, const float* u, int32_t* token, void* stream);
 int launch_fused_step(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                       void* stream);
+int launch_attend_split(const Layout& lay, const Params& par, const StepArgs& a, int lds_bytes, void* stream);
 int launch_attend(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,
                   void* stream);
 int launch_evict(const Layout& lay, const Params& par, const StepArgs& a, bool use_lds, int lds_bytes,

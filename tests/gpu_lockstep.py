@@ -55,17 +55,35 @@ def segment_from_readout(ro, i, d):
 
 
 class Lockstep:
-    def __init__(self, w, seed, segs, capacity=None, prefill=None):
+    """split: None drives confkv_step; an int drives confkv_attend per layer
+    (with that many workgroups per segment, 0 = automatic) and confkv_evict."""
+
+    def __init__(self, w, seed, segs, capacity=None, prefill=None, split=None):
         self.w, self.seed, self.segs = w, seed, sorted(segs)
+        self.split = split
         self.cfg = OC.Config.from_dict(w)
         if prefill is None and w["prefill"]:
             prefill = synth.prefill(w, seed, DEV)
         pk, pv = prefill if prefill is not None else (None, None)
         self.prefill = prefill
         self.gpu = confkv.Cache(w, pk, pv, capacity=capacity, record=True)
+        if split is not None:
+            self.gpu.set_attend_splits(split)
+        self.splits_used = set()
         self.step_i = 0
         self.d = w["head_dim"]
         self.G = self.gpu.G
+
+    def gpu_step(self, x, conf=None, budget=None):
+        if self.split is None:
+            return self.gpu.step(x["logits"], x["q"], x["k"], x["v"], x["prio"], conf_out=conf, budget_out=budget)
+        out = torch.empty_like(x["q"])
+        for l in range(self.w["num_layers"]):
+            self.splits_used.add(self.gpu.attend_splits)
+            self.gpu.attend(l, x["q"][l], x["k"][l], x["v"][l], None if x["prio"] is None else x["prio"][l],
+                            out=out[l])
+        self.gpu.evict(x["logits"], conf_out=conf, budget_out=budget)
+        return out
 
     def read(self):
         return {s: readout_np(self.gpu.read_cache(s, 1)) for s in self.segs}
@@ -75,7 +93,7 @@ class Lockstep:
         x = synth.step_inputs(w, self.seed, self.step_i, DEV)
         self.step_i += 1
         if not check:
-            self.gpu.step(x["logits"], x["q"], x["k"], x["v"], x["prio"])
+            self.gpu_step(x)
             return None
         t = self.gpu.position
         pre = self.read()
@@ -83,7 +101,7 @@ class Lockstep:
         if cfg.policy == "conf":
             conf = torch.empty(w["batch"], dtype=torch.float32, device=DEV)
             budget = torch.empty(w["batch"], dtype=torch.int32, device=DEV)
-        out = self.gpu.step(x["logits"], x["q"], x["k"], x["v"], x["prio"], conf_out=conf, budget_out=budget)
+        out = self.gpu_step(x, conf, budget)
         rec = {s: readout_np(self.gpu.read_last_step(s, 1)) for s in self.segs}
         post = self.read()
         out_np = out.float().cpu().numpy()

@@ -1,20 +1,23 @@
 """The decode step split at the layer boundary (confkv_attend for each layer,
-then confkv_evict) against the one-call confkv_step on identical inputs.
+then confkv_evict).
 
-Both calls sequences compute the same arithmetic in the same order, so the
-bar is bit-identity at every step: attention outputs, confidences, base
-budgets, the recorded ranking values and LSEs, and the whole logical cache
-(positions, EMA, priorities, FP16 rows, INT8 codes and scales). The fused
-step itself is held to the oracle by the parity tests; this file pins the
-split to it. Layers attend in a different order each step, since nothing
-ties one layer's cache to another's.
+With one workgroup per segment, both call sequences compute the same
+arithmetic in the same order, so the bar is bit-identity with confkv_step at
+every step: attention outputs, confidences, base budgets, the recorded
+ranking values and LSEs, and the whole logical cache (positions, EMA,
+priorities, FP16 rows, INT8 codes and scales). Layers attend in a different
+order each step, since nothing ties one layer's cache to another's.
+
+With split-K (several workgroups per segment, combined by the log-sum-exp
+rule) the arithmetic differs in rounding, so those runs are held to the
+oracle in lockstep at the parity bars instead.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_lockstep import DEV, log
+from gpu_lockstep import DEV, Lockstep, log
 from kv_cache_eviction_04_amd import confkv, synth
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +33,7 @@ def twins(w, seed):
     pk, pv = synth.prefill(w, seed, DEV) if w["prefill"] else (None, None)
     fused = confkv.Cache(w, pk, pv, record=True)
     split = confkv.Cache(w, pk, pv, record=True)
+    split.set_attend_splits(1)
     return fused, split
 
 
@@ -133,3 +137,52 @@ def test_split_call_order_is_enforced():
     same(ref, out, "output after rejected calls")
     compare(fused, split, 0)
     assert split.position == 51 and split.status() == confkv.OK
+
+
+def lockstep_split(w, steps, split, seed=0, check_every=1):
+    S = w["num_layers"] * w["batch"] * w["num_kv_heads"]
+    ls = Lockstep(w, seed, range(S), split=split)
+    worst = 0.0
+    for i in range(steps):
+        r = ls.step(check=(i % check_every == 0 or i == steps - 1))
+        if r:
+            worst = max(worst, r["worst_out"])
+    assert ls.gpu.status() == confkv.OK
+    log(f"{w['name']} split-K {split}: splits used {sorted(ls.splits_used)}, {steps} steps, worst out err {worst:.2e}")
+    return ls
+
+
+@pytest.mark.parametrize("split", [0, 2, 3, 7, 32])
+def test_split_k_attend_lockstep_toy(split):
+    # one layer of four segments, window fill, steady eviction, age-out
+    ls = lockstep_split(wl("toy", prefill=600), 40, split, seed=20 + split)
+    assert max(ls.splits_used) >= 2
+
+
+def test_split_k_attend_lockstep_shapes():
+    # GQA 32/8 d 128 with an HBM-sized first step (5000-row prefill) cut into
+    # splits, pyramid layers, G = 5, G = 8, W = 0, FP16-only storage, KVpop
+    ls = lockstep_split(wl("llama3_8b_32k", num_layers=2, batch=2, prefill=5000), 4, 0, seed=30)
+    assert max(ls.splits_used) >= 2
+    lockstep_split(wl("gpt2_small", num_layers=3, prefill=400, n_low=64, n_high=128, protect_last=16,
+                      fp16_window=32), 8, 0, seed=31)
+    lockstep_split(wl("qwen32b", num_layers=2, batch=2, prefill=300), 6, 5, seed=32)
+    lockstep_split(wl("toy", num_q_heads=16, num_kv_heads=2, head_dim=128, prefill=200, n_low=40, n_high=90,
+                      protect_last=8, fp16_window=20), 8, 4, seed=33)
+    lockstep_split(wl("toy", fp16_window=0, prefill=70), 10, 3, seed=34)
+    lockstep_split(wl("toy", old_int8=False, prefill=100), 10, 2, seed=35)
+    lockstep_split(wl("kvpop_qwen3_8b", num_layers=2, batch=2, protect_last=32, fp16_window=32, kvpop_k=60),
+                   120, 3, seed=36, check_every=13)
+
+
+def test_split_k_choice():
+    w = wl("llama3_8b_32k", num_layers=2, batch=2, prefill=9000)
+    pk, pv = synth.prefill(w, 0, DEV)
+    c = confkv.Cache(w, pk, pv)
+    assert c.attend_splits == 32         # 16 segments per layer: as many splits as allowed
+    c.set_attend_splits(1)
+    assert c.attend_splits == 1
+    c.set_attend_splits(2)                # 9288 rows in two splits overflow the LDS: raised
+    assert c.attend_splits == 3
+    with pytest.raises(confkv.ConfKVError):
+        c.set_attend_splits(33)
