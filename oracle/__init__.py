@@ -32,6 +32,7 @@ Modules:
     kvpop       sink + window + top-k fixed budget over static priorities
     cache       the whole per-step loop over every (layer, batch, kv-head)
     sampling    the next token from p = softmax(logits): greedy or inverse-CDF
+    kvpop_prefill  KVpop's multi-query mask and masked prefill attention
 """
 
-from . import confidence, attention, quant, policy, kvpop, cache, sampling  # noqa: F401
+from . import confidence, attention, quant, policy, kvpop, cache, sampling, kvpop_prefill  # noqa: F401
