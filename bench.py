@@ -22,6 +22,7 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 METRIC = "decode steps/s + KV GB/s (fraction of HBM peak) for fused evict+attend step"
 
 
@@ -152,6 +153,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-len", type=int, default=16384,
+                    help="KVpop workloads: sequence length of the masked-prefill measurement (0 skips it)")
     ap.add_argument("--split-steps", type=int, default=50,
                     help="steps of the per-layer call sequence (attend per layer, then evict) timed after the "
                          "fused steps; 0 skips it")
@@ -320,6 +323,44 @@ def main():
         log(f"sampling: greedy {sampling['greedy_us']:.1f} us, draw {sampling['draw_us']:.1f} us per call "
             f"({sampling['logits_bytes'] / 1e6:.1f} MB of logits)")
 
+    # KVpop prefill with the multi-query mask at the pages' 16384-token
+    # training length, one layer per call: algorithmic FLOPs count 4*d per
+    # allowed (query head, key) pair (QK and PV multiply-adds).
+    prefill = None
+    if w["policy"] == "kvpop" and args.prefill_len > 0:
+        S = args.prefill_len
+        gq = torch.Generator(device=dev).manual_seed(args.seed + 1)
+        pq = torch.randn((B, Hq, S, d), generator=gq, device=dev).half()
+        pk_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
+        pv_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
+        pp = torch.rand((B, H, S), generator=gq, device=dev)
+        pout = torch.empty_like(pq)
+        s_, wnd, kk = w["num_sink"], w["protect_last"], w["kvpop_k"]
+        pairs = 0
+        for qq in range(S):
+            pairs += min(s_, qq + 1) + max(0, qq - max(s_, qq - wnd) + 1) + min(kk, max(0, qq - wnd - s_))
+        flops = 4.0 * d * pairs * B * Hq
+        _, _, ws = gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        e0.record()
+        for _ in range(n):
+            gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        if gpu.status() != confkv.OK:
+            log("device status after the prefill is not OK")
+            sys.exit(1)
+        prefill = {"seq_len": S, "batch": B, "ms_per_layer": ms, "allowed_pairs_per_head": pairs,
+                   "tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
+                   "frac": flops / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
+        log(f"kvpop prefill S={S} B={B}: {ms:.3f} ms per layer, {prefill['tflops']:.0f} TFLOP/s "
+            f"({100 * prefill['frac']:.1f}% of fp16 MFMA peak)")
+        del pq, pk_, pv_, pp, pout, ws
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
@@ -369,6 +410,7 @@ def main():
         "cpu_baseline": cpu,
         "per_layer_calls": split,
         "sampling": sampling,
+        "kvpop_prefill": prefill,
     }
     print(json.dumps(res), flush=True)
 

@@ -224,6 +224,35 @@ int32_t confkv_attend_splits(const confkv_handle* h);
  * on one stream. Only enqueues work. */
 int confkv_sample(confkv_handle* h, void* stream, const float* logits, const float* u, int32_t* token_out);
 
+/* KVpop prefill (or teacher-forced pass) over seq_len = S positions whose
+ * static priorities are all known, with the multi-query mask of
+ * "Resumen Técnico: KVpop" §2.4: query q sees key j iff
+ *   j <= q and (j < s or j >= q - w or j in topk(C_q)),  C_q = [s, q-1-w],
+ * top-k by (priority descending, position ascending). That is exactly the
+ * set a decode step at t = q attends to (§2.1 budget, §2.3 delayed scoring).
+ * The mask is never stored: per (batch row, KV head) a sort ranks the
+ * priorities, one pass over q moves the k-th-rank threshold, and the
+ * attention kernel tests each (query, key) pair against it. One layer per
+ * call; the handle's config supplies B, Hq, Hkv, d, s (num_sink),
+ * w (protect_last), k (kvpop_k) and the softmax scale. KVPOP only. The
+ * decode cache is not touched.
+ *   q     [B][Hq][S][d]  fp16      k, v [B][Hkv][S][d] fp16
+ *   prio  [B][Hkv][S]    fp32      (non-finite: sticky CONFKV_ENONFINITE)
+ *   out   [B][Hq][S][d]  fp16      lse [B][Hq][S] fp32 or NULL
+ *   workspace: device, 256-byte aligned, at least
+ *     confkv_kvpop_prefill_workspace(h, S) bytes (0: invalid handle or S).
+ *     Afterwards it holds, each part starting at a 256-byte boundary:
+ *     sort keys [B*Hkv][N] uint64 (N the power of two >= max(S - s, 1)),
+ *     ranks [B*Hkv][S] int32 (0 for the highest priority, -1 for sinks),
+ *     thresholds [B*Hkv][S] int32 (the k-th smallest rank of C_q; S while
+ *     |C_q| < k; -1 when k = 0).
+ * 1 <= S <= 131072; EINVAL where one query tile's key list (s + k + w + 24
+ * entries) would not fit on chip. Only enqueues work. */
+size_t confkv_kvpop_prefill_workspace(const confkv_handle* h, int32_t seq_len);
+int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const float* prio, uint16_t* out, float* lse, void* workspace,
+                         size_t workspace_bytes);
+
 /* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
  * ascending position order. Per segment i, rows 0..len[i]-1 of each
  * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max

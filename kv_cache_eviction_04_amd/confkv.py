@@ -56,6 +56,8 @@ def lib():
         "confkv_evict": (c_int, [P, P, P, P, P]),
         "confkv_sample": (c_int, [P, P, P, P, P]),
         "confkv_set_attend_splits": (c_int, [P, c_int32]),
+        "confkv_kvpop_prefill_workspace": (c_size_t, [P, c_int32]),
+        "confkv_kvpop_prefill": (c_int, [P, P, c_int32, P, P, P, P, P, P, P, c_size_t]),
         "confkv_attend_splits": (c_int32, [P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
@@ -79,6 +81,7 @@ def lib():
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
             "confkv_attend", "confkv_evict", "confkv_sample", "confkv_set_attend_splits", "confkv_attend_splits",
+            "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
             "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
@@ -236,6 +239,45 @@ class Cache:
         _expect(out, (c.batch,), torch.int32, dev, "out")
         _check(lib().confkv_sample(self.h, self._stream(), _ptr(logits), _ptr(u), _ptr(out)), "confkv_sample")
         return out
+
+    def kvpop_prefill(self, q, k, v, prio, out=None, lse=None, workspace=None):
+        """Masked prefill attention of one layer (KVpop). q [B][Hq][S][d], k/v
+        [B][Hkv][S][d] fp16, prio [B][Hkv][S] fp32. Returns (out, lse, workspace)."""
+        c, dev = self.cfg, self.device
+        B, Hq, H, d = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        S = int(q.shape[2]) if q is not None and q.dim() == 4 else 0
+        _expect(q, (B, Hq, S, d), torch.float16, dev, "q")
+        _expect(k, (B, H, S, d), torch.float16, dev, "k")
+        _expect(v, (B, H, S, d), torch.float16, dev, "v")
+        _expect(prio, (B, H, S), torch.float32, dev, "prio")
+        if out is None:
+            out = torch.empty((B, Hq, S, d), dtype=torch.float16, device=dev)
+        _expect(out, (B, Hq, S, d), torch.float16, dev, "out")
+        if lse is not None:
+            _expect(lse, (B, Hq, S), torch.float32, dev, "lse")
+        nbytes = int(lib().confkv_kvpop_prefill_workspace(self.h, S))
+        if nbytes == 0:
+            raise ValueError("no KVpop prefill for this handle or length")
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _check(lib().confkv_kvpop_prefill(self.h, self._stream(), S, _ptr(q), _ptr(k), _ptr(v), _ptr(prio),
+                                          _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel()),
+               "confkv_kvpop_prefill")
+        return out, lse, workspace
+
+    def kvpop_prefill_ranks(self, workspace, S):
+        """(ranks, thresholds) [B*Hkv][S] int32 from a prefill's workspace (its documented layout)."""
+        c = self.cfg
+        segs = c.batch * c.num_kv_heads
+        N = 1
+        while N < max(S - c.num_sink, 1):
+            N <<= 1
+        a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        o_rank = a256(segs * N * 8)
+        o_thr = o_rank + a256(segs * S * 4)
+        ranks = workspace[o_rank:o_rank + segs * S * 4].view(torch.int32).view(segs, S)
+        thr = workspace[o_thr:o_thr + segs * S * 4].view(torch.int32).view(segs, S)
+        return ranks, thr
 
     def read_cache(self, seg_first=0, seg_count=None):
         """Logical contents (ascending position) of a segment range, as torch

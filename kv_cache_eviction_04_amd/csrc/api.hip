@@ -510,6 +510,81 @@ CONFKV_API int confkv_sample(confkv_handle* h, void* stream, const float* logits
   return CONFKV_OK;
 }
 
+namespace {
+constexpr int64_t kPrefillMaxLen = 1 << 17;
+
+struct PrefillSizes {
+  int64_t N, sort_bytes, rank_bytes, total;
+};
+
+PrefillSizes prefill_sizes(const confkv_handle* h, int64_t S) {
+  const int64_t segs = (int64_t)h->lay.B * h->lay.Hkv;
+  int64_t N = 1;
+  while (N < std::max<int64_t>(S - h->cfg.num_sink, 1)) N <<= 1;
+  PrefillSizes z;
+  z.N = N;
+  z.sort_bytes = (int64_t)align256((size_t)(segs * N * 8));
+  z.rank_bytes = (int64_t)align256((size_t)(segs * S * 4));
+  z.total = z.sort_bytes + 2 * z.rank_bytes;
+  return z;
+}
+
+int prefill_list_cap(const confkv_handle* h, int64_t S) {
+  const confkv_config& c = h->cfg;
+  return (int)(std::min<int64_t>(c.num_sink, S) + std::min<int64_t>(c.kvpop_k, S) + c.protect_last + 16 + 8);
+}
+}  // namespace
+
+CONFKV_API size_t confkv_kvpop_prefill_workspace(const confkv_handle* h, int32_t seq_len) {
+  if (!live(h) || h->cfg.policy != CONFKV_POLICY_KVPOP || seq_len < 1 || seq_len > kPrefillMaxLen) return 0;
+  return (size_t)prefill_sizes(h, seq_len).total;
+}
+
+CONFKV_API int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* v, const float* prio, uint16_t* out,
+                                    float* lse, void* workspace, size_t workspace_bytes) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  if (h->cfg.policy != CONFKV_POLICY_KVPOP) return CONFKV_EINVAL;
+  if (seq_len < 1 || seq_len > kPrefillMaxLen) return CONFKV_EINVAL;
+  if (!q || !k || !v || !prio || !out || !workspace || ((uintptr_t)workspace & 255)) return CONFKV_EINVAL;
+  const PrefillSizes z = prefill_sizes(h, seq_len);
+  if (workspace_bytes < (size_t)z.total) return CONFKV_ECAPACITY;
+  const int cap = prefill_list_cap(h, seq_len);
+  if (kvpop_prefill_attend_lds(h->lay.D, cap) > fused_max_dynamic_lds()) return CONFKV_EINVAL;
+  KvpopPrefillArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  pa.B = h->lay.B;
+  pa.Hq = h->lay.Hq;
+  pa.Hkv = h->lay.Hkv;
+  pa.G = h->lay.G;
+  pa.D = h->lay.D;
+  pa.S = seq_len;
+  pa.sinks = h->cfg.num_sink;
+  pa.window = h->cfg.protect_last;
+  pa.topk = h->cfg.kvpop_k;
+  pa.N = (int32_t)z.N;
+  pa.list_cap = cap;
+  pa.scale = h->par.sm_scale;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.prio = prio;
+  pa.out = out;
+  pa.lse = lse;
+  uint8_t* ws = (uint8_t*)workspace;
+  pa.sort = (uint64_t*)ws;
+  pa.rank = (int32_t*)(ws + z.sort_bytes);
+  pa.thr = (int32_t*)(ws + z.sort_bytes + z.rank_bytes);
+  pa.err = h->lay.err;
+  h->last_stream = (hipStream_t)stream;
+  if (launch_kvpop_prefill(pa, stream) != 0) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  return CONFKV_OK;
+}
+
 CONFKV_API int confkv_read_cache(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count, int32_t* len,
                                  int32_t* pos, float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8,
                                  int8_t* v8, float* k_scale, float* v_scale, uint8_t* is_int8) {

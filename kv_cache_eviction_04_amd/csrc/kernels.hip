@@ -1955,6 +1955,323 @@ __global__ void __launch_bounds__(kThreads) attend_combine_kernel(Layout lay, Pa
   }
 }
 
+// ==================================================== KVpop prefill mask
+// [KVpop summary §2.4] The k long-range slots follow a running threshold over
+// static priorities, so the sparse mask of a prefill over S known priorities
+// is generated inside the attention kernel, never stored as S x S. Query q
+// may see key j iff
+//   j <= q and (j < s or j >= q - w or rank(j) <= thr(q)),
+// where rank orders positions >= s by (priority descending, position
+// ascending) and thr(q) is the k-th smallest rank among [s, q-1-w]: the rows
+// a decode step at q attends to. Per segment (batch row, KV head): a sort
+// gives the ranks, one pass over q moves the threshold, and the attention
+// kernel evaluates the predicate per (query, key).
+
+// Ranks: keys (orderable priority << 32 | ~position) sorted descending by a
+// bitonic network in the workspace, then rank[position] = sorted index
+// (-1 for sinks).
+__global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
+  const int tid = threadIdx.x, seg = blockIdx.x;
+  const int S = pa.S, s = pa.sinks, N = pa.N;
+  const float* pr = pa.prio + (size_t)seg * S;
+  uint64_t* A = pa.sort + (size_t)seg * N;
+  int32_t* rank = pa.rank + (size_t)seg * S;
+  for (int i = tid; i < N; i += 1024) {
+    const int j = s + i;
+    A[i] = j < S ? rank_key(pr[j], j) : 0ull;  // padding sorts last
+    if (j < S && !isfinite(pr[j])) atomicOr(pa.err, kErrNonFinite);
+  }
+  for (int j = tid; j < min(s, S); j += 1024) rank[j] = -1;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < N; i += 1024) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const uint64_t a = A[i], b = A[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            A[i] = b;
+            A[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < S - s; i += 1024) rank[0xFFFFFFFFu - (uint32_t)A[i]] = i;
+}
+
+// Thresholds: one pass over q. Position q-1-w joins the candidates at query
+// q; a bitmap over ranks holds the candidates. With n candidates, thr = S
+// (all pass) while n < k, the largest rank at n = k, and after that an
+// inserted rank below thr moves thr to the next candidate rank below it
+// (the old k-th is pushed out). k = 0 gives thr = -1 (none pass).
+__global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
+  extern __shared__ uint32_t kbits[];  // ceil(N/32) words, then 1024 staged ranks
+  const int tid = threadIdx.x, seg = blockIdx.x;
+  const int S = pa.S, s = pa.sinks, w = pa.window, k = pa.topk, nw = (pa.N + 31) >> 5;
+  int32_t* stage = reinterpret_cast<int32_t*>(kbits + nw);
+  const int32_t* rank = pa.rank + (size_t)seg * S;
+  int32_t* thr = pa.thr + (size_t)seg * S;
+  for (int i = tid; i < nw; i += 64) kbits[i] = 0u;
+  int n = 0, t = k > 0 ? S : -1, maxr = -1;
+  for (int q0 = 0; q0 < S; q0 += 1024) {
+    __syncthreads();
+    for (int i = tid; i < 1024; i += 64) {
+      const int p = q0 + i - 1 - w;
+      stage[i] = (q0 + i < S && p >= s) ? rank[p] : -2;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const int cnt = min(1024, S - q0);
+      for (int i = 0; i < cnt; ++i) {
+        const int r = stage[i];
+        if (r >= 0 && k > 0) {
+          kbits[r >> 5] |= 1u << (r & 31);
+          ++n;
+          if (n <= k) maxr = max(maxr, r);
+          if (n == k) {
+            t = maxr;
+          } else if (n > k && r < t) {
+            int wi = t >> 5;
+            uint32_t word = kbits[wi] & ((1u << (t & 31)) - 1u);
+            while (word == 0u) word = kbits[--wi];
+            t = (wi << 5) + 31 - __clz((int)word);
+          }
+        }
+        thr[q0 + i] = t;
+      }
+    }
+  }
+}
+
+// Masked prefill attention: one workgroup per 16 queries of a segment. The
+// key list holds the sinks, the long-range keys that pass the first query's
+// threshold (a superset for the later queries, whose thresholds are no
+// larger), and the contiguous run [q0 - w, q1). Per 32-key chunk the K rows
+// (row-major) and V rows (transposed) go through LDS; wave w takes query
+// heads w, w+4, ...: S = Q K^T on MFMA, the predicate per (query, key),
+// online softmax per query row, and PV with the weights as fp16 hi and lo
+// parts.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+  constexpr int KS = D / 32, NCB = D / 16, HPW = (G + 3) / 4;
+  constexpr int KSTR = D + 8;   // K tile row stride (halves)
+  constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
+  constexpr int PSTR = 40;      // P tile row stride (halves)
+  constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
+  constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
+  extern __shared__ __align__(16) uint16_t plds[];
+  uint16_t* Kt = plds;                        // [32][KSTR]
+  uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
+  uint16_t* Pw = Vt + D * VSTR;               // [4 waves][2][16][PSTR]
+  int32_t* lpos = reinterpret_cast<int32_t*>(Pw + 4 * 2 * 16 * PSTR);
+  int32_t* lrank = lpos + pa.list_cap;
+  __shared__ uint32_t red[4];
+  __shared__ int32_t sh_ng;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, lj = lane & 15;
+  const int S = pa.S, s = pa.sinks, w = pa.window;
+  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int q0 = 16 * blockIdx.x, q1 = min(q0 + 16, S);
+  const int32_t* rank = pa.rank + (size_t)seg * S;
+  const int32_t* thr = pa.thr + (size_t)seg * S;
+  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
+  const uint16_t* vseg = pa.v + (size_t)seg * S * D;
+
+  // ---- key list: sinks, long-range keys passing thr(q0), contiguous run
+  const int n_sink = min(s, q1);
+  const int g_end = max(s, q0 - w);            // long-range positions [s, g_end)
+  const int thr0 = thr[q0];
+  const int glen = g_end - s;
+  const int per = (glen + kThreads - 1) / kThreads;
+  const int ga = s + min(glen, tid * per), gb = s + min(glen, tid * per + per);
+  uint32_t cnt = 0;
+  for (int j = ga; j < gb; ++j) cnt += rank[j] <= thr0 ? 1u : 0u;
+  uint32_t ng;
+  uint32_t off = block_excl_scan_u32(cnt, red, &ng);
+  for (int j = ga; j < gb; ++j) {
+    const int r = rank[j];
+    if (r <= thr0) {
+      if (n_sink + (int)off < pa.list_cap) {
+        lpos[n_sink + off] = j;
+        lrank[n_sink + off] = r;
+      }
+      ++off;
+    }
+  }
+  const int c0 = g_end;
+  const int n_cont = max(0, q1 - c0);
+  const int nk = n_sink + (int)ng + n_cont;
+  for (int i = tid; i < n_sink; i += kThreads) {
+    lpos[i] = i;
+    lrank[i] = -1;
+  }
+  for (int i = tid; i < n_cont; i += kThreads) {
+    if (n_sink + (int)ng + i < pa.list_cap) {
+      lpos[n_sink + ng + i] = c0 + i;
+      lrank[n_sink + ng + i] = rank[c0 + i];
+    }
+  }
+  if (tid == 0 && nk > pa.list_cap) atomicOr(pa.err, kErrInternal);  // cannot happen: host bound
+  __syncthreads();
+  const int nkc = min(nk, pa.list_cap);
+
+  // ---- per-wave query heads: Q operands, thresholds of this lane's rows
+  half8 qa[HPW][KS];
+  float m[HPW][4], l[HPW][4];
+  floatx4 O[HPW][NCB];
+  int thr_r[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) thr_r[r] = q0 + 4 * lq + r < q1 ? thr[q0 + 4 * lq + r] : -1;
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int g = wave + 4 * i;
+    const int hq = h * G + (g < G ? g : 0);
+    const uint16_t* qrow = pa.q + (((size_t)b * pa.Hq + hq) * S + min(q0 + lj, S - 1)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
+      qa[i][kk] = (q0 + lj < q1) ? as_h8(u) : half8{};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[i][r] = -INFINITY;
+      l[i][r] = 0.0f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) O[i][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
+  uint4 rk[PPT], rv[PPT];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      if (e < PIECES) {
+        const int key = e / (D / 8), piece = e - key * (D / 8);
+        const int li = 32 * c + key;
+        const int pos = li < nkc ? lpos[li] : 0;
+        rk[u] = *reinterpret_cast<const uint4*>(kseg + (size_t)pos * D + 8 * piece);
+        rv[u] = *reinterpret_cast<const uint4*>(vseg + (size_t)pos * D + 8 * piece);
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      if (e < PIECES) {
+        const int key = e / (D / 8), piece = e - key * (D / 8);
+        *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
+        const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          Vt[(8 * piece + x) * VSTR + key] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
+      }
+    }
+  };
+  const int nchunks = (nkc + 31) >> 5;
+  uint16_t* Phi = Pw + wave * 2 * 16 * PSTR;
+  uint16_t* Plo = Phi + 16 * PSTR;
+  if (nchunks > 0) load_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    store_chunk();
+    __syncthreads();
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    // this lane's two keys of the chunk
+    int kpos[2], krank[2];
+    bool kin[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int li = 32 * c + 16 * kb + lj;
+      kin[kb] = li < nkc;
+      kpos[kb] = kin[kb] ? lpos[li] : 0;
+      krank[kb] = kin[kb] ? lrank[li] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+      if (wave + 4 * i >= G) continue;
+      floatx4 acc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        acc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(Kt + (16 * kb + lj) * KSTR + 8 * (lq + 4 * kk));
+          acc[kb] = mfma16(qa[i][kk], as_h8(kv), acc[kb]);
+        }
+      }
+      float p[2][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qr = q0 + 4 * lq + r;
+        float sc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int j = kpos[kb];
+          const bool ok = kin[kb] && qr < q1 && j <= qr && (j < s || j >= qr - w || krank[kb] <= thr_r[r]);
+          sc[kb] = ok ? acc[kb][r] * pa.scale : -INFINITY;
+        }
+        float mt = fmaxf(sc[0], sc[1]);
+        for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+        const float mn = fmaxf(m[i][r], mt);
+        const float alpha = m[i][r] == -INFINITY ? 0.0f : __expf(m[i][r] - mn);
+        p[0][r] = mn == -INFINITY ? 0.0f : __expf(sc[0] - mn);
+        p[1][r] = mn == -INFINITY ? 0.0f : __expf(sc[1] - mn);
+        float ls = p[0][r] + p[1][r];
+        for (int o = 1; o < 16; o <<= 1) ls += __shfl_xor(ls, o, 64);
+        l[i][r] = l[i][r] * alpha + ls;
+        m[i][r] = mn;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) O[i][cb][r] *= alpha;
+      }
+      // weights to LDS as fp16 hi and lo parts, read back as PV A operands
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const _Float16 hi = (_Float16)p[kb][r];
+          const _Float16 lo = (_Float16)(p[kb][r] - (float)hi);
+          Phi[(4 * lq + r) * PSTR + 16 * kb + lj] = __builtin_bit_cast(uint16_t, hi);
+          Plo[(4 * lq + r) * PSTR + 16 * kb + lj] = __builtin_bit_cast(uint16_t, lo);
+        }
+      __builtin_amdgcn_wave_barrier();
+      const half8 ahi = as_h8(*reinterpret_cast<const uint4*>(Phi + lj * PSTR + 8 * lq));
+      const half8 alo = as_h8(*reinterpret_cast<const uint4*>(Plo + lj * PSTR + 8 * lq));
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const half8 bv = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
+        O[i][cb] = mfma16(ahi, bv, O[i][cb]);
+        O[i][cb] = mfma16(alo, bv, O[i][cb]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+  }
+  // ---- output rows and LSE
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int g = wave + 4 * i;
+    if (g >= G) continue;
+    const int hq = h * G + g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = q0 + 4 * lq + r;
+      if (qr < q1) {
+        const float il = 1.0f / l[i][r];
+        uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) orow[16 * cb + lj] = f2h(O[i][cb][r] * il);
+        if (pa.lse && lj == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[i][r] + logf(l[i][r]);
+      }
+    }
+  }
+}
+
 // ================================================================ init/ingest
 __global__ void zero_kernel(uint4* p, size_t n16) {
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -2231,6 +2548,37 @@ int launch_attend_split(const Layout& lay, const Params& par, const StepArgs& a,
   if (a.ns < 2 || a.ns > lay.ns_max) return -1;
   if (lay.D == 64) return launch_split_d<64>(lay, par, a, lds_bytes, s);
   if (lay.D == 128) return launch_split_d<128>(lay, par, a, lds_bytes, s);
+  return -1;
+}
+
+template <int D>
+static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipStream_t s) {
+  const dim3 grid((pa.S + 15) / 16, pa.B * pa.Hkv);
+  switch (pa.G) {
+    case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 4: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 4>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 5: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 5>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 8: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 8>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    default: return -1;
+  }
+  return ok_or_err();
+}
+
+int kvpop_prefill_attend_lds(int D, int list_cap) {
+  return (32 * (D + 8) + D * 40 + 4 * 2 * 16 * 40) * 2 + list_cap * 8;
+}
+
+int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int segs = pa.B * pa.Hkv;
+  hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), 0, s, pa);
+  if (hipGetLastError() != hipSuccess) return -3;
+  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4 + 1024 * 4, s, pa);
+  if (hipGetLastError() != hipSuccess) return -3;
+  const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
+  if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
+  if (pa.D == 128) return launch_kvpop_attend_d<128>(pa, lds, s);
   return -1;
 }
 

@@ -116,6 +116,25 @@ struct StepArgs {
   int32_t* budget_out;       // [B] or null (CONF; step and evict)
 };
 
+// KVpop prefill over S known priorities with the multi-query mask.
+struct KvpopPrefillArgs {
+  int32_t B, Hq, Hkv, G, D, S;
+  int32_t sinks, window, topk;  // s, w, k of B = s + w + k
+  int32_t N;                 // sort length: the power of two >= max(S - s, 1)
+  int32_t list_cap;          // key-list entries per query tile
+  float scale;
+  const uint16_t* q;         // [B][Hq][S][D]
+  const uint16_t* k;         // [B][Hkv][S][D]
+  const uint16_t* v;
+  const float* prio;         // [B][Hkv][S]
+  uint16_t* out;             // [B][Hq][S][D]
+  float* lse;                // [B][Hq][S] or null
+  uint64_t* sort;            // workspace [B*Hkv][N]
+  int32_t* rank;             // workspace [B*Hkv][S]
+  int32_t* thr;              // workspace [B*Hkv][S]
+  uint32_t* err;             // the handle's sticky error word
+};
+
 // Launchers (kernels.hip). All enqueue on `stream` and return the launch status.
 int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
                 const uint16_t* pv, int32_t P0, void* stream);
@@ -132,6 +151,8 @@ int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, i
                       float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8, int8_t* v8,
                       float* ks, float* vs, uint8_t* is8, int32_t old_int8, void* stream);
 int launch_stats_total(const Layout& lay, int32_t reset, void* stream);
+int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream);
+int kvpop_prefill_attend_lds(int D, int list_cap);
 int fused_max_dynamic_lds();
 
 }  // namespace confkv
