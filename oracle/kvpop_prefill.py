@@ -115,3 +115,37 @@ def masked_attention(q, K, V, mask, scale):
         out[hq] = (e / l) @ V[h]
         lse[hq] = m[:, 0] + np.log(l[:, 0])
     return out, lse
+
+
+def future_attention_target(q, K, lse, window, scale):
+    """[KVpop summary] §2.2: the scorer's training target for key position t
+    is the log of the attention mass that future queries d >= t + w give it.
+    With each query's log-sum-exp normaliser LSE handed in (the attention
+    pass already produced it), the mass needs no softmax over a dense map:
+
+        target[h, t] = log sum_{g < G} sum_{d = t + w}^{S - 1} exp(s[d, g, t] - LSE[d, g]),
+        s[d, g, t] = scale * q[h*G + g, d] . k[h, t],
+
+    summed over the G query heads of KV head h (-inf where no query counts).
+    q [Hq][S][d], K [Hkv][S][d], lse [Hq][S]. Returns [Hkv][S] float64.
+    Reading: the heads of a group add up, as the rows of one KV head's
+    budget serve all of them."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    Hq, S, _ = q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    d_idx = np.arange(S)[:, None]
+    t_idx = np.arange(S)[None, :]
+    future = d_idx >= t_idx + window                      # [query d, key t]
+    out = np.full((Hkv, S), -np.inf)
+    for h in range(Hkv):
+        mass = np.zeros(S)
+        for g in range(G):
+            s_ = (q[h * G + g] @ K[h].T) * scale             # [d, t]
+            p = np.where(future, np.exp(s_ - lse[h * G + g][:, None]), 0.0)
+            mass += p.sum(axis=0)
+        with np.errstate(divide="ignore"):
+            out[h] = np.log(mass)
+    return out

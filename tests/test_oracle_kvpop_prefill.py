@@ -7,6 +7,9 @@
   tied priorities, k = 0, tiny and huge k, w = 0 and sinks.
 * Prefill attention under the mask equals the decode oracle's output at
   every step of a stream on the same rows, queries and priorities.
+* The future-attention target: identical keys give harmonic sums in closed
+  form; with causal normalisers the masses add up to the number of query
+  rows; explicit loops agree.
 """
 
 import numpy as np
@@ -92,3 +95,57 @@ def test_masked_attention_without_eviction_is_causal_attention():
     p = rng.random(S).astype(np.float32)
     M = KPP.mask_brute_force(p, 0, 2, S)
     assert np.array_equal(M, np.tril(np.ones((S, S), dtype=bool)))
+
+
+def causal_lse(q, K, scale):
+    """LSE of plain causal attention, per query head: [Hq][S]."""
+    Hq, S, _ = q.shape
+    G = Hq // K.shape[0]
+    out = np.zeros((Hq, S))
+    for hq in range(Hq):
+        s_ = (np.asarray(q[hq], np.float64) @ np.asarray(K[hq // G], np.float64).T) * scale
+        s_ = np.where(np.tril(np.ones((S, S), bool)), s_, -np.inf)
+        m = s_.max(axis=1)
+        out[hq] = m + np.log(np.exp(s_ - m[:, None]).sum(axis=1))
+    return out
+
+
+def test_future_target_identical_keys_is_harmonic():
+    # every key equal: causal attention is uniform, p(d, t) = 1/(d+1), so the
+    # target is log(G * sum_{d=t+w}^{S-1} 1/(d+1))
+    S, d, G, w = 30, 8, 3, 4
+    rng = np.random.default_rng(9)
+    q = rng.normal(size=(G, S, d))
+    K = np.tile(rng.normal(size=(1, 1, d)), (1, S, 1))
+    scale = 0.25
+    lse = causal_lse(q, K, scale)
+    tgt = KPP.future_attention_target(q, K, lse, w, scale)
+    for t in range(S):
+        if t + w < S:
+            want = np.log(G * sum(1.0 / (dd + 1) for dd in range(t + w, S)))
+            assert tgt[0, t] == pytest.approx(want, rel=1e-12, abs=1e-12)
+        else:
+            assert tgt[0, t] == -np.inf
+
+
+def test_future_target_masses_add_up_to_the_rows():
+    # with causal LSEs each query row sums to 1: the masses over all keys add
+    # up to the number of (query, head) pairs whose keys lie at least w back
+    S, d, Hq, Hkv, w = 25, 8, 4, 2, 3
+    rng = np.random.default_rng(10)
+    q = rng.normal(size=(Hq, S, d))
+    K = rng.normal(size=(Hkv, S, d))
+    scale = 1 / np.sqrt(d)
+    lse = causal_lse(q, K, scale)
+    tgt = KPP.future_attention_target(q, K, lse, 0, scale)
+    assert np.exp(tgt).sum() == pytest.approx(Hq * S, rel=1e-12)
+    # brute force with explicit loops for w > 0
+    tw = KPP.future_attention_target(q, K, lse, w, scale)
+    G = Hq // Hkv
+    for h in range(Hkv):
+        for t in range(S):
+            m = 0.0
+            for g in range(G):
+                for dd in range(t + w, S):
+                    m += np.exp(scale * float(np.dot(q[h * G + g, dd], K[h, t])) - lse[h * G + g, dd])
+            assert (np.log(m) if m > 0 else -np.inf) == pytest.approx(tw[h, t], rel=1e-12, abs=1e-12)
