@@ -358,6 +358,25 @@ def main():
                    "frac": flops / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
         log(f"kvpop prefill S={S} B={B}: {ms:.3f} ms per layer, {prefill['tflops']:.0f} TFLOP/s "
             f"({100 * prefill['frac']:.1f}% of fp16 MFMA peak)")
+        # the transposed pass: 2*d FLOPs per counted (query head, key) pair
+        plse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, lse=plse, workspace=ws)
+        tgt = gpu.kvpop_future_target(pq, pk_, plse)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            gpu.kvpop_future_target(pq, pk_, plse, out=tgt)
+        e1.record()
+        torch.cuda.synchronize()
+        tms = e0.elapsed_time(e1) / n
+        tpairs = sum(max(0, S - t - wnd) for t in range(S))
+        tflops = 2.0 * d * tpairs * B * Hq
+        prefill["future_target"] = {"ms_per_layer": tms, "counted_pairs_per_head": tpairs,
+                                    "tflops": tflops / (tms * 1e-3) / 1e12,
+                                    "frac": tflops / (tms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
+        log(f"kvpop future target S={S} B={B}: {tms:.3f} ms per layer, "
+            f"{prefill['future_target']['tflops']:.0f} TFLOP/s")
+        del plse, tgt
         del pq, pk_, pv_, pp, pout, ws
         torch.cuda.empty_cache()
 

@@ -253,6 +253,20 @@ int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const 
                          const uint16_t* v, const float* prio, uint16_t* out, float* lse, void* workspace,
                          size_t workspace_bytes);
 
+/* The training target of KVpop's scorer ("Resumen Técnico: KVpop" §2.2): for
+ * each key position t, the log of the attention mass that the future queries
+ * d >= t + w give it, summed over the query heads of its KV head,
+ *   target[t] = log sum_g sum_{d >= t + w} exp(scale * q[d, g] . k[t] - lse[d, g]),
+ * computed by the transposed pass the summary names: keys and queries swap
+ * roles in the MFMA and each query's normaliser lse is reused, so no
+ * attention map is formed. -inf where no query counts (t + w >= S).
+ *   q [B][Hq][S][d] fp16, k [B][Hkv][S][d] fp16,
+ *   lse [B][Hq][S] fp32 (for instance the one confkv_kvpop_prefill writes),
+ *   target [B][Hkv][S] fp32 (written).
+ * KVPOP only (w = protect_last); 1 <= S <= 131072. Only enqueues work. */
+int confkv_kvpop_future_target(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q, const uint16_t* k,
+                               const float* lse, float* target);
+
 /* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
  * ascending position order. Per segment i, rows 0..len[i]-1 of each
  * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max

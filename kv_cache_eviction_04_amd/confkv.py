@@ -58,6 +58,7 @@ def lib():
         "confkv_set_attend_splits": (c_int, [P, c_int32]),
         "confkv_kvpop_prefill_workspace": (c_size_t, [P, c_int32]),
         "confkv_kvpop_prefill": (c_int, [P, P, c_int32, P, P, P, P, P, P, P, c_size_t]),
+        "confkv_kvpop_future_target": (c_int, [P, P, c_int32, P, P, P, P]),
         "confkv_attend_splits": (c_int32, [P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "confkv_read_last_step": (c_int, [P, P, c_int32, c_int32, P, P, P, P]),
@@ -81,7 +82,7 @@ def lib():
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
             "confkv_attend", "confkv_evict", "confkv_sample", "confkv_set_attend_splits", "confkv_attend_splits",
-            "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill",
+            "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill", "confkv_kvpop_future_target",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
             "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
@@ -264,6 +265,21 @@ class Cache:
                                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel()),
                "confkv_kvpop_prefill")
         return out, lse, workspace
+
+    def kvpop_future_target(self, q, k, lse, out=None):
+        """Future-attention target [B][Hkv][S] from q [B][Hq][S][d], k [B][Hkv][S][d], lse [B][Hq][S]."""
+        c, dev = self.cfg, self.device
+        B, Hq, H, d = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        S = int(q.shape[2]) if q is not None and q.dim() == 4 else 0
+        _expect(q, (B, Hq, S, d), torch.float16, dev, "q")
+        _expect(k, (B, H, S, d), torch.float16, dev, "k")
+        _expect(lse, (B, Hq, S), torch.float32, dev, "lse")
+        if out is None:
+            out = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        _expect(out, (B, H, S), torch.float32, dev, "target")
+        _check(lib().confkv_kvpop_future_target(self.h, self._stream(), S, _ptr(q), _ptr(k), _ptr(lse), _ptr(out)),
+               "confkv_kvpop_future_target")
+        return out
 
     def kvpop_prefill_ranks(self, workspace, S):
         """(ranks, thresholds) [B*Hkv][S] int32 from a prefill's workspace (its documented layout)."""

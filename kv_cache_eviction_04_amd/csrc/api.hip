@@ -585,6 +585,34 @@ CONFKV_API int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_
   return CONFKV_OK;
 }
 
+CONFKV_API int confkv_kvpop_future_target(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
+                                         const uint16_t* k, const float* lse, float* target) {
+  if (!live(h)) return CONFKV_ESTATE;
+  if (h->poisoned) return CONFKV_ESTATE;
+  if (h->cfg.policy != CONFKV_POLICY_KVPOP) return CONFKV_EINVAL;
+  if (seq_len < 1 || seq_len > kPrefillMaxLen) return CONFKV_EINVAL;
+  if (!q || !k || !lse || !target) return CONFKV_EINVAL;
+  KvpopPrefillArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  pa.B = h->lay.B;
+  pa.Hq = h->lay.Hq;
+  pa.Hkv = h->lay.Hkv;
+  pa.G = h->lay.G;
+  pa.D = h->lay.D;
+  pa.S = seq_len;
+  pa.window = h->cfg.protect_last;
+  pa.scale = h->par.sm_scale;
+  pa.q = q;
+  pa.k = k;
+  pa.err = h->lay.err;
+  h->last_stream = (hipStream_t)stream;
+  if (launch_kvpop_target(pa, lse, target, stream) != 0) {
+    h->poisoned = 1;
+    return CONFKV_EHIP;
+  }
+  return CONFKV_OK;
+}
+
 CONFKV_API int confkv_read_cache(confkv_handle* h, void* stream, int32_t seg_first, int32_t seg_count, int32_t* len,
                                  int32_t* pos, float* ema, float* prio, uint16_t* k16, uint16_t* v16, int8_t* k8,
                                  int8_t* v8, float* k_scale, float* v_scale, uint8_t* is_int8) {

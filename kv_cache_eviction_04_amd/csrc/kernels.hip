@@ -2272,6 +2272,91 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
   }
 }
 
+// Future-attention target [KVpop summary §2.2], the transposed pass: for key
+// t of a segment, log sum over the group's query heads g and the queries
+// d >= t + w of exp(s[d, g, t] - LSE[d, g]), with the queries' normalisers
+// handed in, so no attention map is formed. One workgroup per 128 keys; wave
+// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles and streams
+// the Q rows of every later 16-query tile and head as B operands: the MFMA
+// gives S^T[key][query] and each lane accumulates the masked exponentials of
+// its keys.
+struct TargetBuf {
+  uint4 qc[4];
+  float lse;
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
+                                                                float* target) {
+  constexpr int KS = D / 32;
+  static_assert(KS <= 4, "head_dim up to 128");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, lj = lane & 15;
+  const int S = pa.S, w = pa.window;
+  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int t0 = 128 * blockIdx.x + 32 * wave;  // this wave's first key
+  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
+  const float scale = pa.scale;
+
+  half8 ka[2][KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int t = t0 + 16 * kb + lj;
+    const uint16_t* kr = kseg + (size_t)min(t, S - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
+      ka[kb][kk] = t < S ? as_h8(u) : half8{};
+    }
+  }
+  float acc[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[kb][r] = 0.0f;
+
+  // (query tile, head) pairs from the first tile holding a counted query
+  const int tile0 = min(t0 + w, S) >> 4;
+  const int ntile = (S + 15) >> 4;
+  pipelined<4, TargetBuf>(
+      tile0 * G, ntile * G,
+      [&](int x, TargetBuf& bf) {
+        const int tile = x / G, g = x - tile * G;
+        const int hq = h * G + g;
+        const int d = min(16 * tile + lj, S - 1);
+        const uint16_t* qr = pa.q + (((size_t)b * pa.Hq + hq) * S + d) * D;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) bf.qc[kk] = *reinterpret_cast<const uint4*>(qr + 8 * (lq + 4 * kk));
+        bf.lse = lse_in[((size_t)b * pa.Hq + hq) * S + d];
+      },
+      [&](int x, const TargetBuf& bf) {
+        const int tile = x / G;
+        const int d = 16 * tile + lj;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], as_h8(bf.qc[kk]), c);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * kb + 4 * lq + r;
+            const bool counted = d < S && d >= t + w;
+            acc[kb][r] += counted ? __expf(c[r] * scale - bf.lse) : 0.0f;
+          }
+        }
+      });
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = acc[kb][r];
+      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o, 64);
+      const int t = t0 + 16 * kb + 4 * lq + r;
+      if (lj == 0 && t < S) target[(size_t)seg * S + t] = a > 0.0f ? logf(a) : -INFINITY;
+    }
+  }
+}
+
 // ================================================================ init/ingest
 __global__ void zero_kernel(uint4* p, size_t n16) {
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -2579,6 +2664,27 @@ int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
   const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
   if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
   if (pa.D == 128) return launch_kvpop_attend_d<128>(pa, lds, s);
+  return -1;
+}
+
+template <int D>
+static int launch_target_d(const KvpopPrefillArgs& pa, const float* lse, float* target, hipStream_t s) {
+  const dim3 grid((pa.S + 127) / 128, pa.B * pa.Hkv);
+  switch (pa.G) {
+    case 1: hipLaunchKernelGGL((kvpop_target_kernel<D, 1>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 2: hipLaunchKernelGGL((kvpop_target_kernel<D, 2>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 4: hipLaunchKernelGGL((kvpop_target_kernel<D, 4>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 5: hipLaunchKernelGGL((kvpop_target_kernel<D, 5>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 8: hipLaunchKernelGGL((kvpop_target_kernel<D, 8>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    default: return -1;
+  }
+  return ok_or_err();
+}
+
+int launch_kvpop_target(const KvpopPrefillArgs& pa, const float* lse, float* target, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (pa.D == 64) return launch_target_d<64>(pa, lse, target, s);
+  if (pa.D == 128) return launch_target_d<128>(pa, lse, target, s);
   return -1;
 }
 

@@ -152,6 +152,7 @@ int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, i
                       float* ks, float* vs, uint8_t* is8, int32_t old_int8, void* stream);
 int launch_stats_total(const Layout& lay, int32_t reset, void* stream);
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream);
+int launch_kvpop_target(const KvpopPrefillArgs& pa, const float* lse, float* target, void* stream);
 int kvpop_prefill_attend_lds(int D, int list_cap);
 int fused_max_dynamic_lds();
 

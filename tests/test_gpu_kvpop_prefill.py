@@ -7,6 +7,10 @@ relative. Cases cover every compiled group size, head_dim 64 and 128, tied
 priorities, k = 0, k covering everything (plain causal attention), w = 0,
 no sinks, a sequence shorter than the sinks, ragged query tiles, and the
 Qwen3-8B shape at 16K positions checked on sampled query rows.
+
+The future-attention target (the transposed pass) is held to 1e-4 on its
+logarithm against the dense float64 oracle, with the prefill's own LSEs as
+normalisers, and on sampled keys at 16K positions.
 """
 
 import numpy as np
@@ -122,3 +126,57 @@ def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
                 l_or = m + np.log(e.sum())
                 assert abs(float(lse[0, h * G + g, qr]) - l_or) <= TOL_LSE_REL * max(1.0, abs(l_or))
     log(f"kvpop prefill Qwen3-8B 16K: {len(rows)} rows x 2 heads x {G}, worst out err {worst:.2e}")
+
+
+TOL_TARGET = 1e-4  # on the log: fp32 sums of exponentials, relative error well below 1e-4 at these lengths
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,S,w", [(4, 2, 64, 300, 16), (32, 8, 128, 333, 32), (10, 2, 128, 150, 0),
+                                          (16, 2, 64, 170, 12), (2, 2, 64, 40, 50)])
+def test_kvpop_future_target_matches_oracle(Hq, Hkv, d, S, w):
+    # normalisers from the masked prefill, as in training
+    B = 2
+    w_ = kvpop_cfg(Hq, Hkv, d, 2, w, 20, B)
+    gpu = confkv.Cache(w_)
+    q, kk, v, p = inputs(B, Hq, Hkv, S, d, seed=S + w)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    gpu.kvpop_prefill(q, kk, v, p, lse=lse)
+    tgt = gpu.kvpop_future_target(q, kk, lse).cpu().numpy()
+    assert gpu.status() == confkv.OK
+    qn, kn, ln = q.cpu().numpy(), kk.cpu().numpy(), lse.cpu().numpy().astype(np.float64)
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        want = KPP.future_attention_target(qn[b], kn[b], ln[b], w, scale)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(tgt[b]), fin)
+        err = float(np.abs(tgt[b][fin] - want[fin]).max(initial=0.0))
+        assert err <= TOL_TARGET, f"b{b}: target err {err}"
+    log(f"kvpop target G{Hq // Hkv} d{d} S{S} w{w}: ok")
+
+
+def test_kvpop_future_target_16k_sampled_keys():
+    B, Hq, Hkv, d, S = 1, 32, 8, 128, 16384
+    w_ = synth.workload("kvpop_qwen3_8b", num_layers=1, batch=B)
+    w = w_["protect_last"]
+    gpu = confkv.Cache(w_)
+    q, kk, v, p = inputs(B, Hq, Hkv, S, d, seed=8)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    gpu.kvpop_prefill(q, kk, v, p, lse=lse)
+    tgt = gpu.kvpop_future_target(q, kk, lse).cpu().numpy()
+    assert gpu.status() == confkv.OK
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d)
+    worst = 0.0
+    for h in (0, 7):
+        Q = q[0, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+        L = lse[0, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+        Kh = kk[0, h].cpu().numpy().astype(np.float64)
+        for t in (0, 1, 255, 256, 4000, 8191, 12000, S - w - 1, S - w, S - 1):
+            if t + w >= S:
+                assert tgt[0, h, t] == -np.inf
+                continue
+            m = sum(np.exp(Q[g, t + w:] @ Kh[t] * scale - L[g, t + w:]).sum() for g in range(G))
+            err = abs(float(tgt[0, h, t]) - np.log(m))
+            worst = max(worst, err)
+            assert err <= TOL_TARGET, f"h{h} t{t}: {err}"
+    log(f"kvpop target 16K: worst err {worst:.2e}")
