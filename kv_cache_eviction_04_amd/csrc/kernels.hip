@@ -2272,31 +2272,35 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
   }
 }
 
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+
 // Future-attention target [KVpop summary §2.2], the transposed pass: for key
 // t of a segment, log sum over the group's query heads g and the queries
 // d >= t + w of exp(s[d, g, t] - LSE[d, g]), with the queries' normalisers
 // handed in, so no attention map is formed. One workgroup per 128 keys; wave
-// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles and streams
-// the Q rows of every later 16-query tile and head as B operands: the MFMA
-// gives S^T[key][query] and each lane accumulates the masked exponentials of
-// its keys.
-struct TargetBuf {
-  uint4 qc[4];
-  float lse;
-};
-
+// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles. The later
+// queries stream through LDS in stages of four (16-query tile, head) pairs,
+// double-buffered and shared by the four waves; the MFMA gives
+// S^T[key][query] and each lane accumulates the masked exponentials.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
                                                                 float* target) {
   constexpr int KS = D / 32;
-  static_assert(KS <= 4, "head_dim up to 128");
+  constexpr int QSTR = D + 8;                 // staged row stride (halves)
+  constexpr int NP = 4;                       // (tile, head) pairs per stage
+  constexpr int RP = D / 8;                   // 16-byte pieces per row
+  constexpr int PPT = NP * 16 * RP / kThreads;
+  static_assert(PPT * kThreads == NP * 16 * RP, "stage pieces divide the block");
+  __shared__ __align__(16) uint16_t qs[2][NP][16][QSTR];
+  __shared__ float ls[2][NP][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, w = pa.window;
   const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int t0 = 128 * blockIdx.x + 32 * wave;  // this wave's first key
+  const int t0b = 128 * blockIdx.x;            // the workgroup's first key
+  const int t0 = t0b + 32 * wave;              // this wave's first key
   const uint16_t* kseg = pa.k + (size_t)seg * S * D;
-  const float scale = pa.scale;
+  const float sl2 = pa.scale * kLog2e;
 
   half8 ka[2][KS];
 #pragma unroll
@@ -2316,35 +2320,83 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
     for (int r = 0; r < 4; ++r) acc[kb][r] = 0.0f;
 
   // (query tile, head) pairs from the first tile holding a counted query
-  const int tile0 = min(t0 + w, S) >> 4;
-  const int ntile = (S + 15) >> 4;
-  pipelined<4, TargetBuf>(
-      tile0 * G, ntile * G,
-      [&](int x, TargetBuf& bf) {
+  const int x0 = (min(t0b + w, S) >> 4) * G, x1 = ((S + 15) >> 4) * G;
+  const int nst = (x1 - x0 + NP - 1) / NP;
+  uint4 pre[PPT];
+  float plse = 0.0f;
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
+      const int x = x0 + NP * st + pr;
+      if (x < x1) {
         const int tile = x / G, g = x - tile * G;
-        const int hq = h * G + g;
-        const int d = min(16 * tile + lj, S - 1);
-        const uint16_t* qr = pa.q + (((size_t)b * pa.Hq + hq) * S + d) * D;
+        const int d = min(16 * tile + row, S - 1);
+        pre[u] = *reinterpret_cast<const uint4*>(pa.q + (((size_t)b * pa.Hq + h * G + g) * S + d) * D + 8 * piece);
+      } else {
+        pre[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (tid < NP * 16) {
+      const int pr = tid >> 4, row = tid & 15;
+      const int x = x0 + NP * st + pr;
+      if (x < x1) {
+        const int tile = x / G, g = x - tile * G;
+        plse = lse_in[((size_t)b * pa.Hq + h * G + g) * S + min(16 * tile + row, S - 1)];
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) bf.qc[kk] = *reinterpret_cast<const uint4*>(qr + 8 * (lq + 4 * kk));
-        bf.lse = lse_in[((size_t)b * pa.Hq + hq) * S + d];
-      },
-      [&](int x, const TargetBuf& bf) {
-        const int tile = x / G;
-        const int d = 16 * tile + lj;
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
+      *reinterpret_cast<uint4*>(&qs[buf][pr][row][8 * piece]) = pre[u];
+    }
+    if (tid < NP * 16) ls[buf][tid >> 4][tid & 15] = plse;
+  };
+  if (nst > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int pr = 0; pr < NP; ++pr) {
+      const int x = x0 + NP * st + pr;
+      if (x >= x1) break;
+      const int d0 = 16 * (x / G), d = d0 + lj;
+      half8 qb[KS];
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], as_h8(bf.qc[kk]), c);
+      for (int kk = 0; kk < KS; ++kk) qb[kk] = as_h8(*reinterpret_cast<const uint4*>(&qs[buf][pr][lj][8 * (lq + 4 * kk)]));
+      // exp(s*scale - lse) = 2^(c*scale*log2(e) - lse*log2(e)): one FMA and one exp2
+      const float nl2 = -ls[buf][pr][lj] * kLog2e;
+      // every query of this tile counts for every key of this wave
+      const bool full = d0 >= t0 + 31 + w && d0 + 15 < S;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], qb[kk], c);
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[kb][r] += __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2));
+        } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = t0 + 16 * kb + 4 * lq + r;
             const bool counted = d < S && d >= t + w;
-            acc[kb][r] += counted ? __expf(c[r] * scale - bf.lse) : 0.0f;
+            acc[kb][r] += counted ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2)) : 0.0f;
           }
         }
-      });
+      }
+    }
+    if (st + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
