@@ -246,7 +246,7 @@ int confkv_sample(confkv_handle* h, void* stream, const float* logits, const flo
  *     ranks [B*Hkv][S] int32 (0 for the highest priority, -1 for sinks),
  *     thresholds [B*Hkv][S] int32 (the k-th smallest rank of C_q; S while
  *     |C_q| < k; -1 when k = 0).
- * 1 <= S <= 131072; EINVAL where one query tile's key list (s + k + w + 24
+ * 1 <= S <= 131072; EINVAL where one query tile's key list (s + k + w + 40
  * entries) would not fit on chip. Only enqueues work. */
 size_t confkv_kvpop_prefill_workspace(const confkv_handle* h, int32_t seq_len);
 int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q, const uint16_t* k,

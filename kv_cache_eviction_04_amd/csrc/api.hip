@@ -531,7 +531,7 @@ PrefillSizes prefill_sizes(const confkv_handle* h, int64_t S) {
 
 int prefill_list_cap(const confkv_handle* h, int64_t S) {
   const confkv_config& c = h->cfg;
-  return (int)(std::min<int64_t>(c.num_sink, S) + std::min<int64_t>(c.kvpop_k, S) + c.protect_last + 16 + 8);
+  return (int)(std::min<int64_t>(c.num_sink, S) + std::min<int64_t>(c.kvpop_k, S) + c.protect_last + 32 + 8);
 }
 }  // namespace
 

@@ -2006,7 +2006,10 @@ __global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
 // q; a bitmap over ranks holds the candidates. With n candidates, thr = S
 // (all pass) while n < k, the largest rank at n = k, and after that an
 // inserted rank below thr moves thr to the next candidate rank below it
-// (the old k-th is pushed out). k = 0 gives thr = -1 (none pass).
+// (the old k-th is pushed out). k = 0 gives thr = -1 (none pass). Once
+// n >= k a rank above thr is never the threshold again (thr only moves
+// down, and the search for the next rank runs below it), so it is not
+// entered in the bitmap.
 __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
   extern __shared__ uint32_t kbits[];  // ceil(N/32) words, then 1024 staged ranks
   const int tid = threadIdx.x, seg = blockIdx.x;
@@ -2028,12 +2031,13 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
       for (int i = 0; i < cnt; ++i) {
         const int r = stage[i];
         if (r >= 0 && k > 0) {
-          kbits[r >> 5] |= 1u << (r & 31);
           ++n;
-          if (n <= k) maxr = max(maxr, r);
-          if (n == k) {
-            t = maxr;
-          } else if (n > k && r < t) {
+          if (n <= k) {
+            kbits[r >> 5] |= 1u << (r & 31);
+            maxr = max(maxr, r);
+            if (n == k) t = maxr;
+          } else if (r < t) {
+            kbits[r >> 5] |= 1u << (r & 31);
             int wi = t >> 5;
             uint32_t word = kbits[wi] & ((1u << (t & 31)) - 1u);
             while (word == 0u) word = kbits[--wi];
@@ -2046,17 +2050,25 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
   }
 }
 
-// Masked prefill attention: one workgroup per 16 queries of a segment. The
-// key list holds the sinks, the long-range keys that pass the first query's
-// threshold (a superset for the later queries, whose thresholds are no
-// larger), and the contiguous run [q0 - w, q1). Per 32-key chunk the K rows
-// (row-major) and V rows (transposed) go through LDS; wave w takes query
-// heads w, w+4, ...: S = Q K^T on MFMA, the predicate per (query, key),
-// online softmax per query row, and PV with the weights as fp16 hi and lo
-// parts.
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
+
+// Masked prefill attention: one workgroup per 32 queries of a segment (16
+// when a wave serves two query heads). The key list holds the sinks, the
+// long-range keys that pass the first query's threshold (a superset for the
+// later queries, whose thresholds are no larger), and the contiguous run
+// [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
+// (transposed) go through LDS once for all the workgroup's queries; wave w
+// takes query heads w, w+4, ... for its 16-query blocks: S = Q K^T on MFMA,
+// the predicate per (query, key), online softmax per query row in the base-2
+// domain, and PV with the weights as fp16 hi and lo parts.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
-  constexpr int KS = D / 32, NCB = D / 16, HPW = (G + 3) / 4;
+__global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+  constexpr int KS = D / 32, NCB = D / 16;
+  constexpr int HPW = (G + 3) / 4;              // query heads per wave
+  constexpr int QT = HPW == 1 ? 2 : 1;          // 16-query blocks per head
+  constexpr int QB = 16 * QT;                   // queries per workgroup
+  constexpr int NR = HPW * QT;                  // 16-row blocks per wave
   constexpr int KSTR = D + 8;   // K tile row stride (halves)
   constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
   constexpr int PSTR = 40;      // P tile row stride (halves)
@@ -2069,13 +2081,12 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
   int32_t* lpos = reinterpret_cast<int32_t*>(Pw + 4 * 2 * 16 * PSTR);
   int32_t* lrank = lpos + pa.list_cap;
   __shared__ uint32_t red[4];
-  __shared__ int32_t sh_ng;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, s = pa.sinks, w = pa.window;
   const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int q0 = 16 * blockIdx.x, q1 = min(q0 + 16, S);
+  const int q0 = QB * blockIdx.x, q1 = min(q0 + QB, S);
   const int32_t* rank = pa.rank + (size_t)seg * S;
   const int32_t* thr = pa.thr + (size_t)seg * S;
   const uint16_t* kseg = pa.k + (size_t)seg * S * D;
@@ -2119,30 +2130,38 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
   __syncthreads();
   const int nkc = min(nk, pa.list_cap);
 
-  // ---- per-wave query heads: Q operands, thresholds of this lane's rows
-  half8 qa[HPW][KS];
-  float m[HPW][4], l[HPW][4];
-  floatx4 O[HPW][NCB];
-  int thr_r[4];
+  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT.
+  // Scores and maxima are kept in base-2 units (scale * log2(e) folded in).
+  const float sl2 = pa.scale * kLog2e;
+  half8 qa[NR][KS];
+  float m[NR][4], l[NR][4];
+  floatx4 O[NR][NCB];
+  int thr_r[QT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) thr_r[r] = q0 + 4 * lq + r < q1 ? thr[q0 + 4 * lq + r] : -1;
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-  for (int i = 0; i < HPW; ++i) {
-    const int g = wave + 4 * i;
+    for (int r = 0; r < 4; ++r) {
+      const int qr = q0 + 16 * qt + 4 * lq + r;
+      thr_r[qt][r] = qr < q1 ? thr[qr] : -1;
+    }
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const int g = wave + 4 * (rb / QT), qt = rb % QT;
     const int hq = h * G + (g < G ? g : 0);
-    const uint16_t* qrow = pa.q + (((size_t)b * pa.Hq + hq) * S + min(q0 + lj, S - 1)) * D;
+    const int qrow = q0 + 16 * qt + lj;
+    const uint16_t* qp = pa.q + (((size_t)b * pa.Hq + hq) * S + min(qrow, S - 1)) * D;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-      qa[i][kk] = (q0 + lj < q1) ? as_h8(u) : half8{};
+      const uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (lq + 4 * kk));
+      qa[rb][kk] = qrow < q1 ? as_h8(u) : half8{};
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m[i][r] = -INFINITY;
-      l[i][r] = 0.0f;
+      m[rb][r] = -INFINITY;
+      l[rb][r] = 0.0f;
     }
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) O[i][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int cb = 0; cb < NCB; ++cb) O[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
@@ -2193,8 +2212,9 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
       krank[kb] = kin[kb] ? lrank[li] : 0;
     }
 #pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      if (wave + 4 * i >= G) continue;
+    for (int rb = 0; rb < NR; ++rb) {
+      if (wave + 4 * (rb / QT) >= G) continue;
+      const int qt = rb % QT;
       floatx4 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -2202,32 +2222,33 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           const uint4 kv = *reinterpret_cast<const uint4*>(Kt + (16 * kb + lj) * KSTR + 8 * (lq + 4 * kk));
-          acc[kb] = mfma16(qa[i][kk], as_h8(kv), acc[kb]);
+          acc[kb] = mfma16(qa[rb][kk], as_h8(kv), acc[kb]);
         }
       }
       float p[2][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int qr = q0 + 4 * lq + r;
+        const int qr = q0 + 16 * qt + 4 * lq + r;
         float sc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int j = kpos[kb];
-          const bool ok = kin[kb] && qr < q1 && j <= qr && (j < s || j >= qr - w || krank[kb] <= thr_r[r]);
-          sc[kb] = ok ? acc[kb][r] * pa.scale : -INFINITY;
+          const bool ok = kin[kb] && qr < q1 && j <= qr && (j < s || j >= qr - w || krank[kb] <= thr_r[qt][r]);
+          sc[kb] = ok ? acc[kb][r] * sl2 : -INFINITY;
         }
         float mt = fmaxf(sc[0], sc[1]);
         for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
-        const float mn = fmaxf(m[i][r], mt);
-        const float alpha = m[i][r] == -INFINITY ? 0.0f : __expf(m[i][r] - mn);
-        p[0][r] = mn == -INFINITY ? 0.0f : __expf(sc[0] - mn);
-        p[1][r] = mn == -INFINITY ? 0.0f : __expf(sc[1] - mn);
+        const float mn = fmaxf(m[rb][r], mt);
+        const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
+        const float alpha = __builtin_amdgcn_exp2f(m[rb][r] - ms);
+        p[0][r] = __builtin_amdgcn_exp2f(sc[0] - ms);
+        p[1][r] = __builtin_amdgcn_exp2f(sc[1] - ms);
         float ls = p[0][r] + p[1][r];
         for (int o = 1; o < 16; o <<= 1) ls += __shfl_xor(ls, o, 64);
-        l[i][r] = l[i][r] * alpha + ls;
-        m[i][r] = mn;
+        l[rb][r] = l[rb][r] * alpha + ls;
+        m[rb][r] = mn;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) O[i][cb][r] *= alpha;
+        for (int cb = 0; cb < NCB; ++cb) O[rb][cb][r] *= alpha;
       }
       // weights to LDS as fp16 hi and lo parts, read back as PV A operands
 #pragma unroll
@@ -2245,34 +2266,33 @@ __global__ void __launch_bounds__(kThreads) kvpop_prefill_attend_kernel(KvpopPre
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const half8 bv = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
-        O[i][cb] = mfma16(ahi, bv, O[i][cb]);
-        O[i][cb] = mfma16(alo, bv, O[i][cb]);
+        O[rb][cb] = mfma16(ahi, bv, O[rb][cb]);
+        O[rb][cb] = mfma16(alo, bv, O[rb][cb]);
       }
       __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
   }
-  // ---- output rows and LSE
+  // ---- output rows and LSE (natural log: m * ln 2 + ln l)
 #pragma unroll
-  for (int i = 0; i < HPW; ++i) {
-    const int g = wave + 4 * i;
+  for (int rb = 0; rb < NR; ++rb) {
+    const int g = wave + 4 * (rb / QT), qt = rb % QT;
     if (g >= G) continue;
     const int hq = h * G + g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int qr = q0 + 4 * lq + r;
+      const int qr = q0 + 16 * qt + 4 * lq + r;
       if (qr < q1) {
-        const float il = 1.0f / l[i][r];
+        const float il = 1.0f / l[rb][r];
         uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) orow[16 * cb + lj] = f2h(O[i][cb][r] * il);
-        if (pa.lse && lj == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[i][r] + logf(l[i][r]);
+        for (int cb = 0; cb < NCB; ++cb) orow[16 * cb + lj] = f2h(O[rb][cb][r] * il);
+        if (pa.lse && lj == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[rb][r] * kLn2 + logf(l[rb][r]);
       }
     }
   }
 }
 
-constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 
 // Future-attention target [KVpop summary §2.2], the transposed pass: for key
 // t of a segment, log sum over the group's query heads g and the queries
@@ -2690,7 +2710,8 @@ int launch_attend_split(const Layout& lay, const Params& par, const StepArgs& a,
 
 template <int D>
 static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipStream_t s) {
-  const dim3 grid((pa.S + 15) / 16, pa.B * pa.Hkv);
+  const int qb = pa.G <= 4 ? 32 : 16;  // queries per workgroup (see the kernel)
+  const dim3 grid((pa.S + qb - 1) / qb, pa.B * pa.Hkv);
   switch (pa.G) {
     case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1>), grid, dim3(kThreads), lds_bytes, s, pa); break;
     case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2>), grid, dim3(kThreads), lds_bytes, s, pa); break;
