@@ -267,7 +267,7 @@ int attend_splits(const confkv_handle* h) {
   const int64_t segs = (int64_t)lay.B * lay.Hkv;
   const int64_t tiles = ((std::min<int64_t>(h->rows_bound, lay.cap) + 31) >> 5) + (lay.Wr32 >> 5);
   auto lds_ok = [&](int64_t ns) {
-    return ((tiles + ns - 1) / ns) * 32 * lay.G * 4 <= (int64_t)fused_max_dynamic_lds();
+    return ((tiles + ns - 1) / ns) * 32 * (lay.G + 1) * 4 <= (int64_t)fused_max_dynamic_lds();
   };
   int64_t ns;
   if (h->attend_splits == 1) return 1;
@@ -433,7 +433,7 @@ CONFKV_API int confkv_attend(confkv_handle* h, void* stream, int32_t layer, cons
     a.ns = ns;
     a.lds_rows = (int32_t)(((tiles + ns - 1) / ns) * 32);
     if (record_event(h, h->pa, s, true)) goto hip_fail;
-    rc = launch_attend_split(lay, h->par, a, a.lds_rows * lay.G * 4, stream);
+    rc = launch_attend_split(lay, h->par, a, a.lds_rows * (lay.G + 1) * 4, stream);  // planes + V scales
   } else {
     const Staging sg = staging(h, lay.planes);
     a.lds_rows = sg.lds_rows;

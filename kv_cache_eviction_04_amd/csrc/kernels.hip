@@ -1559,6 +1559,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
   if (cut) r1 = r0 + a.lds_rows;
   const int rs = a.lds_rows;
   auto st = [&](int g, int j) -> float& { return dyn_lds[g * rs + j]; };
+  float* svl = dyn_lds + G * rs;  // V scales of the run's old rows (from the QK loads)
 
   const int slot_new = t % Wr;
   const int i_new = n_old32 + slot_new;
@@ -1676,6 +1677,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
             const int row = 16 * tt + lj;
             const bool valid = row < n_old;
             if (valid) sv_max = fmaxf(sv_max, bf.sv);
+            if (lq == 0) svl[row - r0] = bf.sv;
             const float f = bf.sk * sm;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1714,6 +1716,25 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
           });
     }
   }
+  // ---- the first batch of this run's INT8 V tiles, loaded now so that the
+  // loads overlap the maxima barrier and the weight pass
+  const int pv_t0 = r0 >> 5, pv_t1 = oe > r0 ? oe >> 5 : pv_t0;
+  constexpr int NPRE = CONFKV_PV8_NPB;
+  PV8Buf vpre[NPRE];
+  auto load_pv8 = [&](int tt, PV8Buf& bf) {
+    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * (32 * tt + 8 * lq < n_old ? lane : lj);
+    if constexpr (CBW == 2) {
+      bf.v = ldnt4(tb + 1024 * wave);
+    } else {
+      const uint2 hh = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+      bf.v = make_uint4(hh.x, hh.y, 0u, 0u);
+    }
+  };
+  if (par.old_int8) {
+#pragma unroll
+    for (int u = 0; u < NPRE; ++u)
+      if (pv_t0 + u < pv_t1) load_pv8(pv_t0 + u, vpre[u]);
+  }
   // ---- this run's maxima per head and of the INT8 V scales
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -1746,7 +1767,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
   float* sco = lay.sk_s + (size_t)sl * G * lay.rows_max;
   for (int j = tid; j < r1 - r0; j += kThreads) {
     const int i = r0 + j;
-    const float sv = i < n_old ? ovs[i] : 0.0f;
+    const float sv = (i < n_old && par.old_int8) ? svl[j] : 0.0f;
     const float scf = ((i < n_old && par.old_int8 && sv > 0.0f) ? sv : 1.0f) * fscale;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -1818,28 +1839,21 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
   if (oe > r0) {
     const int t0 = r0 >> 5, t1 = oe >> 5;
     if (par.old_int8) {
-      pipelined<CONFKV_PV8_NPB, PV8Buf>(
-          t0, t1,
-          [&](int tt, PV8Buf& bf) {
-            const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * (32 * tt + 8 * lq < n_old ? lane : lj);
-            if constexpr (CBW == 2) {
-              bf.v = ldnt4(tb + 1024 * wave);
-            } else {
-              const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-              bf.v = make_uint4(h.x, h.y, 0u, 0u);
-            }
-          },
-          [&](int tt, const PV8Buf& bf) {
-            half8 ahi, alo, blo, bhi;
-            weights(32 * tt - r0 + 8 * lq, ahi, alo);
-            i8x16_to_h8(bf.v, blo, bhi);
-            O[0] = mfma16(ahi, blo, O[0]);
-            O[0] = mfma16(alo, blo, O[0]);
-            if constexpr (CBW == 2) {
-              O[1] = mfma16(ahi, bhi, O[1]);
-              O[1] = mfma16(alo, bhi, O[1]);
-            }
-          });
+      auto pv8 = [&](int tt, const PV8Buf& bf) {
+        half8 ahi, alo, blo, bhi;
+        weights(32 * tt - r0 + 8 * lq, ahi, alo);
+        i8x16_to_h8(bf.v, blo, bhi);
+        O[0] = mfma16(ahi, blo, O[0]);
+        O[0] = mfma16(alo, blo, O[0]);
+        if constexpr (CBW == 2) {
+          O[1] = mfma16(ahi, bhi, O[1]);
+          O[1] = mfma16(alo, bhi, O[1]);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u)
+        if (t0 + u < t1) pv8(t0 + u, vpre[u]);
+      pipelined<CONFKV_PV8_NPB, PV8Buf>(t0 + NPRE, t1, load_pv8, pv8);
     } else {
       pv16(reinterpret_cast<const uint16_t*>(ovt), 0, t0, t1, n_old);
     }
