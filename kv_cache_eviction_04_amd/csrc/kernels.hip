@@ -2073,11 +2073,11 @@ constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 // later queries, whose thresholds are no larger), and the contiguous run
 // [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
 // (transposed) go through LDS once for all the workgroup's queries; wave w
-// takes query heads w, w+4, ... for its 16-query blocks: S = Q K^T on MFMA,
-// the predicate per (query, key), online softmax per query row in the base-2
-// domain, and PV with the weights as fp16 hi and lo parts.
+// takes query heads w, w+4, ... for its 16-query blocks: S^T = K Q^T on
+// MFMA, the predicate per (key, query), online softmax per query in the
+// base-2 domain, and O^T = V^T P^T with the weights as fp16 hi and lo parts.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+__global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
   constexpr int KS = D / 32, NCB = D / 16;
   constexpr int HPW = (G + 3) / 4;              // query heads per wave
   constexpr int QT = HPW == 1 ? 2 : 1;          // 16-query blocks per head
@@ -2085,15 +2085,13 @@ __global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(Kvpop
   constexpr int NR = HPW * QT;                  // 16-row blocks per wave
   constexpr int KSTR = D + 8;   // K tile row stride (halves)
   constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
-  constexpr int PSTR = 40;      // P tile row stride (halves)
   constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
   constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
   extern __shared__ __align__(16) uint16_t plds[];
   uint16_t* Kt = plds;                        // [32][KSTR]
   uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
-  uint16_t* Pw = Vt + D * VSTR;               // [4 waves][2][16][PSTR]
-  int32_t* lpos = reinterpret_cast<int32_t*>(Pw + 4 * 2 * 16 * PSTR);
-  int32_t* lrank = lpos + pa.list_cap;
+  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + D * VSTR);
+  int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
   __shared__ uint32_t red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2144,20 +2142,17 @@ __global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(Kvpop
   __syncthreads();
   const int nkc = min(nk, pa.list_cap);
 
-  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT.
+  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT. The
+  // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
+  // that lane (lq, lj) receives query lj's scores against keys 8lq .. 8lq+7
+  // of the chunk: the softmax of a query stays in one lane group, and its
+  // eight weights are at once the lane's B operand of O^T = V^T P^T.
   // Scores and maxima are kept in base-2 units (scale * log2(e) folded in).
   const float sl2 = pa.scale * kLog2e;
-  half8 qa[NR][KS];
-  float m[NR][4], l[NR][4];
+  half8 qb[NR][KS];
+  float m[NR], l[NR];
+  int thr_q[NR];
   floatx4 O[NR][NCB];
-  int thr_r[QT][4];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qr = q0 + 16 * qt + 4 * lq + r;
-      thr_r[qt][r] = qr < q1 ? thr[qr] : -1;
-    }
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int g = wave + 4 * (rb / QT), qt = rb % QT;
@@ -2167,16 +2162,16 @@ __global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(Kvpop
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (lq + 4 * kk));
-      qa[rb][kk] = qrow < q1 ? as_h8(u) : half8{};
+      qb[rb][kk] = qrow < q1 ? as_h8(u) : half8{};
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m[rb][r] = -INFINITY;
-      l[rb][r] = 0.0f;
-    }
+    m[rb] = -INFINITY;
+    l[rb] = 0.0f;
+    thr_q[rb] = qrow < q1 ? thr[qrow] : -1;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) O[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  // row lj of permuted block kb holds key 8*(lj/4) + 4*kb + lj%4 of the chunk
+  const int kperm0 = 8 * (lj >> 2) + (lj & 3);
 
   // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
   uint4 rk[PPT], rv[PPT];
@@ -2208,101 +2203,98 @@ __global__ void __launch_bounds__(kThreads, 2) kvpop_prefill_attend_kernel(Kvpop
     }
   };
   const int nchunks = (nkc + 31) >> 5;
-  uint16_t* Phi = Pw + wave * 2 * 16 * PSTR;
-  uint16_t* Plo = Phi + 16 * PSTR;
   if (nchunks > 0) load_chunk(0);
   for (int c = 0; c < nchunks; ++c) {
     store_chunk();
     __syncthreads();
     if (c + 1 < nchunks) load_chunk(c + 1);
-    // this lane's two keys of the chunk
-    int kpos[2], krank[2];
-    bool kin[2];
+    // this lane's eight keys of the chunk: list entries 32c + 8lq .. +7
+    int kpos[8], krank[8];
+    {
+      const int li0 = 32 * c + 8 * lq;
+      const uint4 p0 = *reinterpret_cast<const uint4*>(lpos + li0);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(lpos + li0 + 4);
+      const uint4 r0v = *reinterpret_cast<const uint4*>(lrank + li0);
+      const uint4 r1v = *reinterpret_cast<const uint4*>(lrank + li0 + 4);
+      const int pp[8] = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+      const int rr[8] = {(int)r0v.x, (int)r0v.y, (int)r0v.z, (int)r0v.w,
+                         (int)r1v.x, (int)r1v.y, (int)r1v.z, (int)r1v.w};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int li = 32 * c + 16 * kb + lj;
-      kin[kb] = li < nkc;
-      kpos[kb] = kin[kb] ? lpos[li] : 0;
-      krank[kb] = kin[kb] ? lrank[li] : 0;
+      for (int e = 0; e < 8; ++e) {
+        const bool in = li0 + e < nkc;
+        kpos[e] = in ? pp[e] : INT32_MAX;  // out of the list: never <= a query
+        krank[e] = rr[e];
+      }
     }
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb) {
       if (wave + 4 * (rb / QT) >= G) continue;
-      const int qt = rb % QT;
+      const int qr = q0 + 16 * (rb % QT) + lj;
       floatx4 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         acc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t* kr = Kt + (kperm0 + 4 * kb) * KSTR;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(Kt + (16 * kb + lj) * KSTR + 8 * (lq + 4 * kk));
-          acc[kb] = mfma16(qa[rb][kk], as_h8(kv), acc[kb]);
-        }
+        for (int kk = 0; kk < KS; ++kk)
+          acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk))), qb[rb][kk], acc[kb]);
       }
-      float p[2][4];
+      float sc[8];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qr = q0 + 16 * qt + 4 * lq + r;
-        float sc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int j = kpos[kb];
-          const bool ok = kin[kb] && qr < q1 && j <= qr && (j < s || j >= qr - w || krank[kb] <= thr_r[qt][r]);
-          sc[kb] = ok ? acc[kb][r] * sl2 : -INFINITY;
-        }
-        float mt = fmaxf(sc[0], sc[1]);
-        for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
-        const float mn = fmaxf(m[rb][r], mt);
-        const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
-        const float alpha = __builtin_amdgcn_exp2f(m[rb][r] - ms);
-        p[0][r] = __builtin_amdgcn_exp2f(sc[0] - ms);
-        p[1][r] = __builtin_amdgcn_exp2f(sc[1] - ms);
-        float ls = p[0][r] + p[1][r];
-        for (int o = 1; o < 16; o <<= 1) ls += __shfl_xor(ls, o, 64);
-        l[rb][r] = l[rb][r] * alpha + ls;
-        m[rb][r] = mn;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) O[rb][cb][r] *= alpha;
+      for (int e = 0; e < 8; ++e) {
+        const int j = kpos[e];
+        const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
+        sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+        mt = fmaxf(mt, sc[e]);
       }
-      // weights to LDS as fp16 hi and lo parts, read back as PV A operands
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m[rb], mt);
+      const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
+      const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
+      float ls = 0.0f;
+      half8 phi, plo;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16 hi = (_Float16)p[kb][r];
-          const _Float16 lo = (_Float16)(p[kb][r] - (float)hi);
-          Phi[(4 * lq + r) * PSTR + 16 * kb + lj] = __builtin_bit_cast(uint16_t, hi);
-          Plo[(4 * lq + r) * PSTR + 16 * kb + lj] = __builtin_bit_cast(uint16_t, lo);
-        }
-      __builtin_amdgcn_wave_barrier();
-      const half8 ahi = as_h8(*reinterpret_cast<const uint4*>(Phi + lj * PSTR + 8 * lq));
-      const half8 alo = as_h8(*reinterpret_cast<const uint4*>(Plo + lj * PSTR + 8 * lq));
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sc[e] - ms);
+        ls += pe;
+        const _Float16 hi = (_Float16)pe;
+        phi[e] = hi;
+        plo[e] = (_Float16)(pe - (float)hi);
+      }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l[rb] = l[rb] * alpha + ls;
+      m[rb] = mn;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const half8 bv = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
-        O[rb][cb] = mfma16(ahi, bv, O[rb][cb]);
-        O[rb][cb] = mfma16(alo, bv, O[rb][cb]);
+        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
+        O[rb][cb] *= alpha;
+        O[rb][cb] = mfma16(av, phi, O[rb][cb]);
+        O[rb][cb] = mfma16(av, plo, O[rb][cb]);
       }
-      __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
   }
-  // ---- output rows and LSE (natural log: m * ln 2 + ln l)
+  // ---- output rows and LSE (natural log: m * ln 2 + ln l). Lane (lq, lj)
+  // holds O^T[column 16cb + 4lq + r][query lj].
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int g = wave + 4 * (rb / QT), qt = rb % QT;
     if (g >= G) continue;
     const int hq = h * G + g;
+    const int qr = q0 + 16 * qt + lj;
+    if (qr < q1) {
+      const float il = 1.0f / l[rb];
+      uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qr = q0 + 16 * qt + 4 * lq + r;
-      if (qr < q1) {
-        const float il = 1.0f / l[rb][r];
-        uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) orow[16 * cb + lj] = f2h(O[rb][cb][r] * il);
-        if (pa.lse && lj == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[rb][r] * kLn2 + logf(l[rb][r]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint32_t lo = (uint32_t)f2h(O[rb][cb][0] * il) | ((uint32_t)f2h(O[rb][cb][1] * il) << 16);
+        const uint32_t hi = (uint32_t)f2h(O[rb][cb][2] * il) | ((uint32_t)f2h(O[rb][cb][3] * il) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * lq) = make_uint2(lo, hi);
       }
+      if (pa.lse && lq == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[rb] * kLn2 + logf(l[rb]);
     }
   }
 }
@@ -2738,7 +2730,7 @@ static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipS
 }
 
 int kvpop_prefill_attend_lds(int D, int list_cap) {
-  return (32 * (D + 8) + D * 40 + 4 * 2 * 16 * 40) * 2 + list_cap * 8;
+  return (32 * (D + 8) + D * 40) * 2 + ((list_cap + 31) & ~31) * 8;
 }
 
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
