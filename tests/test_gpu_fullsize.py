@@ -9,6 +9,9 @@ checked in lockstep on a sample of segments the oracle can follow one by one.
   4096-step stream with checks spread over it.
 * KVpop on the Qwen3-8B shape: fill-up to the 2048-row budget, the first
   evictions, and the history-free closed form of the kept set.
+* The per-layer calls (attend per layer with automatic split-K, then evict)
+  on the Llama-3-8B shape at 32K: the first step splits 32769 rows per
+  segment 32 ways.
 """
 
 import pytest
@@ -85,3 +88,14 @@ def test_kvpop_qwen3_8b_full_size_fill_and_evict():
         n = int(ro["len"][0])
         assert ro["pos"][0, :n].tolist() == want, f"segment {seg}"
     log(f"kvpop full size: {total} steps, closed form holds at t {t}")
+
+
+def test_llama3_8b_32k_full_size_per_layer_calls():
+    w = synth.workload("llama3_8b_32k")
+    L, B, H = w["num_layers"], w["batch"], w["num_kv_heads"]
+    segs = segments(w, [(0, 0, 0), (L // 2, B - 1, 4), (L - 1, 7, 7)])
+    ls = Lockstep(w, 3, segs, split=0)
+    release_prefill(ls)
+    worst = drive(ls, 6, {0, 1, 5})
+    assert max(ls.splits_used) >= 2
+    log(f"llama3_8b_32k per-layer calls: splits used {sorted(ls.splits_used)}, worst out err {worst:.2e}")
