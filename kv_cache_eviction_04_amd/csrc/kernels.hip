@@ -578,7 +578,8 @@ typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 #define CONFKV_KB 6        // key-phase rows per thread loaded ahead
 #endif
 #ifndef CONFKV_OCC
-#define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 4)
+#define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 5; a few
+                           // spills at G = 5 cost less than a fourth of the occupancy)
 #endif
 // Streaming loads of K/V tiles: read once per step, so marked non-temporal.
 __device__ __forceinline__ uint4 ldnt4(const void* p) {
@@ -706,7 +707,7 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
 // One workgroup per segment. Stage-row index space: old rows [0, n_old32)
 // (rows >= n_old are padding), ring slots [n_old32, n_old32 + Wr32).
 template <int D, int G, bool kLds, int MODE>
-__global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) fused_step_kernel(Layout lay, Params par, StepArgs a) {
+__global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_step_kernel(Layout lay, Params par, StepArgs a) {
   constexpr bool kAtt = MODE != kModeEvict;  // append, attention, output (and the EMA update)
   constexpr bool kEv = MODE != kModeAttend;  // keys, selection, compaction, age-out
   constexpr int LPR = D / 16;          // lanes per row for row-wise work
