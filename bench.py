@@ -49,7 +49,7 @@ def kernel_source_hash():
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_eviction_04_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("kernels.hip", "layout.h"):
+    for name in ("kernels.hip", "device.h", "layout.h"):
         with open(os.path.join(root, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libconfkv.so")
-SOURCES = [os.path.join(HERE, "csrc", "kernels.hip"), os.path.join(HERE, "csrc", "api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n)
+           for n in ("kernels.hip", "split_attend.hip", "sample.hip", "kvpop_prefill.hip", "api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -3,211 +3,23 @@
 //
 // Kernels
 //   conf_reduce_kernel  logits -> (max, sum e, sum e*(z-m), top1, top2) per
-//                       chunk; the last chunk of a batch row to finish merges
-//                       them into the confidence c and the base budget.
+//                       chunk; each segment workgroup merges its row's
+//                       chunks into the confidence c and the base budget.
 //   fused_step_kernel   one workgroup per segment (layer, batch row, KV head):
 //                       append -> QK on MFMA -> max -> exp/sum -> PV on MFMA
 //                       -> out -> mass/EMA/score/key -> select -> compact ->
-//                       age-out.
+//                       age-out; also the attend-only and evict-only halves.
 //   init / ingest       zero the state and store the prefill.
 //   read_cache          logical (ascending position) read-out for checking.
+// The split-K attend, the next-token draw and the KVpop prefill live in
+// split_attend.hip, sample.hip and kvpop_prefill.hip.
 //
 // Sources: "Conf-KV" post (rcap.io), method paragraph and decoding-loop
 // pseudocode; CONF-KV abstract (chatpaper.ai); "Resumen Técnico: KVpop"
 // (gist.science) §2.1, §2.3, §2.4.
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
-#include "layout.h"
+#include "device.h"
 
 namespace confkv {
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ half8 as_h8(uint4 u) { return __builtin_bit_cast(half8, u); }
-__device__ __forceinline__ float half_lo(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[0]; }
-__device__ __forceinline__ float half_hi(uint32_t u) { return (float)__builtin_bit_cast(h2, u)[1]; }
-__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
-
-__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------- V tiles
-// Element offset of (row, col) in a segment's transposed V storage (see
-// layout.h): rows in tiles of 32, each tile 32*D elements.
-__device__ __forceinline__ size_t vt8(int row, int col, int D) {
-  const int r = row & 31, q = r >> 3, e = r & 7, cb = col >> 4, j = col & 15;
-  return (size_t)(row >> 5) * 32 * D + 1024 * (cb >> 1) + 16 * (16 * q + j) + 8 * (cb & 1) + e;
-}
-__device__ __forceinline__ size_t vt16(int row, int col, int D) {
-  const int r = row & 31, q = r >> 3, e = r & 7, cb = col >> 4, j = col & 15;
-  return (size_t)(row >> 5) * 32 * D + 512 * cb + 8 * (16 * q + j) + e;
-}
-
-// ---------------------------------------------------------------- lane groups
-// Row-wise work (quantization, moves) spreads a row of d elements over
-// LPR = d/16 consecutive lanes, 16 elements each. Group reductions use DPP:
-// quad_perm swaps (xor 1, xor 2) and, for 8-lane groups, the half-row mirror
-// (lane i <-> 7-i), which pairs the two quads.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-template <int LPR>
-__device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  if constexpr (LPR == 8) v = fmaxf(v, dpp<0x141>(v));
-  return v;
-}
-
-// Four signed INT8 codes -> two fp16 pairs, exactly: bias each byte to
-// unsigned (x + 128), splice it under the fp16 exponent of 1024 (0x64xx is
-// 1024 + xx), then subtract 1152.
-__device__ __forceinline__ void i8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
-  const uint32_t x = w ^ 0x80808080u;
-  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
-  hi = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
-}
-// 16 codes -> codes 0..7 and 8..15 as fp16 MFMA operands.
-__device__ __forceinline__ void i8x16_to_h8(uint4 w, half8& a, half8& b) {
-  h2 t0, t1, t2, t3, t4, t5, t6, t7;
-  i8x4_to_h2(w.x, t0, t1);
-  i8x4_to_h2(w.y, t2, t3);
-  i8x4_to_h2(w.z, t4, t5);
-  i8x4_to_h2(w.w, t6, t7);
-  a = half8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
-  b = half8{t4[0], t4[1], t5[0], t5[1], t6[0], t6[1], t7[0], t7[1]};
-}
-
-__device__ __forceinline__ uint32_t orderable(float f) {
-  if (f == 0.0f) f = 0.0f;  // -0 ranks as +0
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// Larger key = kept first: score descending, then position ascending.
-__device__ __forceinline__ uint64_t rank_key(float score, int32_t pos) {
-  return ((uint64_t)orderable(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
-}
-
-// Random ranks for the random-victim ranker: SplitMix64 (Steele, Lea and
-// Flood, OOPSLA 2014). out(k, n) is the n-th output of the generator started
-// from state k: the state advances by the golden-ratio increment and the
-// output function applies two xor-shift-multiply rounds and an xor-shift.
-__device__ __forceinline__ uint64_t splitmix64_out(uint64_t k, uint64_t n) {
-  uint64_t z = k + n * 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-// ------------------------------------------------------------ block helpers
-// 256 threads = 4 wavefronts of 64.
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o, 64);
-    v = w < v ? w : v;
-  }
-  return v;
-}
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
-  v = wave_sum_u32(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const uint32_t r = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
-  v = wave_min_u64(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint64_t r = red[0];
-  for (int w = 1; w < 4; ++w) r = red[w] < r ? red[w] : r;
-  __syncthreads();
-  return r;
-}
-// Exclusive prefix sum over the block in thread order; *total gets the sum.
-__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* red, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) red[wave] = inc;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += red[w];
-  *total = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return off + inc - v;
-}
-
-// ----------------------------------------------------------------- INT8 row
-// Absmax quantization of the 16 elements a lane holds; the group of LPR lanes
-// holds one row. scale = fl32(amax / 127) and code = rne(fl32(x / scale)),
-// clamped to [-127, 127]; amax == 0 gives scale 0 and zero codes. Both
-// quotients are formed in binary64 and rounded once to binary32, which is the
-// correctly rounded binary32 quotient (53 >= 2*24 + 2), independent of the
-// compiler's float-division mode. Returns the group's scale; codes[e] holds
-// the code of element e.
-template <int LPR>
-__device__ __forceinline__ float quantize16(const float (&x)[16], int8_t (&codes)[16]) {
-  float am = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(x[e]));
-  am = group_max<LPR>(am);
-  float scale = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) codes[e] = 0;
-  if (am > 0.0f) {
-    scale = (float)((double)am / 127.0);
-    const double sd = (double)scale;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float r = rintf((float)((double)x[e] / sd));
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      codes[e] = (int8_t)(int)r;
-    }
-  }
-  return scale;
-}
-__device__ __forceinline__ void load16h(const uint16_t* src, float (&x)[16]) {
-  const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(src)[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[2 * j] = half_lo(w[j]);
-    x[2 * j + 1] = half_hi(w[j]);
-  }
-}
-__device__ __forceinline__ uint4 pack16(const int8_t (&c)[16]) {
-  uint32_t p[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 16; ++e) p[e >> 2] |= ((uint32_t)(uint8_t)c[e]) << (8 * (e & 3));
-  return make_uint4(p[0], p[1], p[2], p[3]);
-}
 
 // ======================================================= logits -> confidence
 // [Conf-KV post, pseudocode] p = softmax(logits); c mixes the normalized
@@ -351,308 +163,6 @@ __device__ __forceinline__ void row_confidence(const Layout& lay, const Params& 
     c_out = cval;
   }
 }
-
-// ================================================================= sampling
-// [Conf-KV post, pseudocode] the step ends with x_t = sample(p), p the softmax
-// of the same logits. Greedy: the largest logit, lowest index among equal
-// maxima. Random: the smallest j with p_0 + ... + p_j > u for the caller's
-// uniform u of the row, the sums formed in binary64 from e_j = exp(z_j - M).
-// Pass 1 (one workgroup per 4096-logit chunk and row): the chunk's maximum,
-// its lowest index, and sum e^(z - m_c). Pass 2 (one workgroup per row): the
-// row's maximum and token for greedy; for a draw, the chunk where the scaled
-// running sum crosses u * total, then an ordered scan inside that chunk.
-__global__ void __launch_bounds__(256) sample_reduce_kernel(Layout lay, const float* logits, int32_t want_sum) {
-  __shared__ uint64_t s_k[4];
-  __shared__ double s_S[4];
-  const int b = blockIdx.y, ci = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int V = lay.V;
-  const float* z = logits + (size_t)b * V;
-  const int begin = ci * kChunk, end = min(V, begin + kChunk);
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) x[j] = z[min(begin + tid + 256 * j, end - 1)];
-  // key: (~orderable(z) << 32) | index — the smallest key is the largest
-  // logit at its lowest index; a non-finite logit forces the key 0
-  uint64_t key = ~0ull;
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int i = begin + tid + 256 * j;
-    if (i < end) {
-      bad |= !isfinite(x[j]);
-      const uint64_t k = ((uint64_t)(~orderable(x[j])) << 32) | (uint32_t)i;
-      key = k < key ? k : key;
-    }
-  }
-  if (bad) key = 0;
-  key = block_min_u64(key, s_k);
-  SamplePartial out;
-  out.idx = key == 0 ? -1 : (int32_t)(uint32_t)key;
-  out.m = key == 0 ? NAN : z[out.idx];
-  out.S = 0.0;
-  if (want_sum && key != 0) {
-    const double m = (double)out.m;
-    double S = 0.0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (begin + tid + 256 * j < end) S += exp((double)x[j] - m);
-    for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
-    if (lane == 0) s_S[wave] = S;
-    __syncthreads();
-    out.S = (s_S[0] + s_S[1]) + (s_S[2] + s_S[3]);
-  }
-  if (tid == 0) {
-    lay.spart[(size_t)b * lay.chunks + ci] = out;
-    if (key == 0) atomicOr(lay.err, kErrNonFinite);
-  }
-}
-
-// Exclusive prefix sum of doubles over the block in thread order.
-__device__ __forceinline__ double block_excl_scan_f64(double v, double* red, double* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) red[wave] = inc;
-  __syncthreads();
-  double off = 0.0;
-  for (int w = 0; w < wave; ++w) off += red[w];
-  *total = ((red[0] + red[1]) + red[2]) + red[3];
-  __syncthreads();
-  return off + inc - v;
-}
-
-__global__ void __launch_bounds__(256) sample_pick_kernel(Layout lay, const float* logits, const float* u,
-                                                          int32_t* token) {
-  __shared__ float s_m[4];
-  __shared__ int32_t s_i[4];
-  __shared__ double s_red[4];
-  __shared__ int32_t s_chunk, s_pick;
-  __shared__ double s_base, s_target;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int C = lay.chunks;
-  const SamplePartial* sp = lay.spart + (size_t)b * C;
-  // row maximum and its lowest index; any flagged chunk makes the row invalid
-  float m = -INFINITY;
-  int32_t idx = INT32_MAX;
-  bool bad = false;
-  for (int c = tid; c < C; c += 256) {
-    const SamplePartial p = sp[c];
-    if (p.idx < 0) {
-      bad = true;
-    } else if (p.m > m || (p.m == m && p.idx < idx)) {
-      m = p.m;
-      idx = p.idx;
-    }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(m, o, 64);
-    const int32_t oi = __shfl_xor(idx, o, 64);
-    if (om > m || (om == m && oi < idx)) {
-      m = om;
-      idx = oi;
-    }
-  }
-  bad = __any(bad);
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_i[wave] = bad ? -1 : idx;
-  }
-  __syncthreads();
-  float M = s_m[0];
-  int32_t I = s_i[0];
-  bool row_bad = s_i[0] < 0;
-  for (int w = 1; w < 4; ++w) {
-    row_bad |= s_i[w] < 0;
-    if (s_m[w] > M || (s_m[w] == M && s_i[w] < I)) {
-      M = s_m[w];
-      I = s_i[w];
-    }
-  }
-  if (row_bad) {
-    if (tid == 0) token[b] = -1;
-    return;
-  }
-  if (!u) {
-    if (tid == 0) token[b] = I;
-    return;
-  }
-  // the chunk where the running sum of e_j (in units of exp(-M)) passes u * total
-  if (tid == 0) {
-    const double Md = (double)M;
-    double total = 0.0;
-    for (int c = 0; c < C; ++c) total += sp[c].S * exp((double)sp[c].m - Md);
-    const double target = (double)u[b] * total;
-    double acc = 0.0;
-    int k = -1, last = 0;
-    for (int c = 0; c < C; ++c) {
-      const double wc = sp[c].S * exp((double)sp[c].m - Md);
-      if (wc > 0.0) last = c;
-      if (k < 0 && acc + wc > target && wc > 0.0) {
-        k = c;
-        break;
-      }
-      acc += wc;
-    }
-    if (k < 0) {  // u * total not reached through rounding: the last chunk with mass
-      k = last;
-      double a2 = 0.0;
-      for (int c = 0; c < k; ++c) a2 += sp[c].S * exp((double)sp[c].m - Md);
-      acc = a2;
-    }
-    s_chunk = k;
-    s_base = acc;
-    s_target = target;
-    s_pick = INT32_MAX;
-  }
-  __syncthreads();
-  const int k = s_chunk;
-  const double base = s_base, target = s_target, Md = (double)M;
-  const int V = lay.V;
-  const float* z = logits + (size_t)b * V;
-  const int begin = k * kChunk, end = min(V, begin + kChunk);
-  // thread tid scans 16 consecutive logits of the chunk, in index order
-  double e[16], loc = 0.0;
-  int lastpos = -1;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int i = begin + 16 * tid + j;
-    e[j] = i < end ? exp((double)z[i] - Md) : 0.0;
-    loc += e[j];
-    if (e[j] > 0.0) lastpos = i;
-  }
-  double chunk_total;
-  const double pre = base + block_excl_scan_f64(loc, s_red, &chunk_total);
-  if (pre <= target && pre + loc > target) {
-    // the crossing is in this thread's range; should the one-term-at-a-time
-    // sum stop short of it by rounding, the range's last token with mass
-    int pick = lastpos;
-    double run = pre;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      run += e[j];
-      if (run > target && e[j] > 0.0) {
-        pick = begin + 16 * tid + j;
-        break;
-      }
-    }
-    atomicMin(&s_pick, pick);
-  }
-  __syncthreads();
-  if (s_pick == INT32_MAX) {  // the chunk's own sum stops short of the target: its last token with mass
-    int lp = lastpos;
-    for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o, 64));
-    if (lane == 0) s_i[wave] = lp;
-    __syncthreads();
-    if (tid == 0) token[b] = max(max(s_i[0], s_i[1]), max(s_i[2], s_i[3]));
-    return;
-  }
-  if (tid == 0) token[b] = s_pick;
-}
-
-// ================================================== fused attend+evict step
-typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-// Tuning constants of the fused kernel (defaults measured on MI355X).
-#ifndef CONFKV_NT
-#define CONFKV_NT 0        // K/V tile loads marked non-temporal
-#endif
-#ifndef CONFKV_PIPE
-#define CONFKV_PIPE 0      // 0: load a batch, then compute it; 1: two-stage pipeline
-#endif
-#ifndef CONFKV_QK8_NPB
-#define CONFKV_QK8_NPB 4   // INT8 K tiles per batch
-#endif
-#ifndef CONFKV_QK16_NPB
-#define CONFKV_QK16_NPB 2  // FP16 K tiles per batch
-#endif
-#ifndef CONFKV_PV8_NPB
-#define CONFKV_PV8_NPB 8   // INT8 V tiles per batch
-#endif
-#ifndef CONFKV_PV16_NPB
-#define CONFKV_PV16_NPB 4  // FP16 V tiles per batch
-#endif
-#ifndef CONFKV_KB
-#define CONFKV_KB 6        // key-phase rows per thread loaded ahead
-#endif
-#ifndef CONFKV_OCC
-#define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 5; a few
-                           // spills at G = 5 cost less than a fourth of the occupancy)
-#endif
-// Streaming loads of K/V tiles: read once per step, so marked non-temporal.
-__device__ __forceinline__ uint4 ldnt4(const void* p) {
-#if CONFKV_NT
-  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
-}
-__device__ __forceinline__ uint2 ldnt2(const void* p) {
-#if CONFKV_NT
-  const u2v v = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(p));
-  return make_uint2(v[0], v[1]);
-#else
-  return *reinterpret_cast<const uint2*>(p);
-#endif
-}
-
-// Tile loop over [t0, t1) (uniform across the wavefront). Batched: issue the
-// loads of NPB tiles, then compute them. Two-stage: while one batch is
-// computed, the loads of the next are in flight (twice the registers).
-template <int NPB, class Buf, class LoadF, class CompF>
-__device__ __forceinline__ void pipelined(int t0, int t1, LoadF&& load, CompF&& comp) {
-  if (t0 >= t1) return;
-#if !CONFKV_PIPE
-  for (int base = t0; base < t1; base += NPB) {
-    Buf A[NPB];
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + u < t1) load(base + u, A[u]);
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + u < t1) comp(base + u, A[u]);
-  }
-  return;
-#endif
-  Buf A[NPB], B[NPB];
-#pragma unroll
-  for (int u = 0; u < NPB; ++u)
-    if (t0 + u < t1) load(t0 + u, A[u]);
-  for (int base = t0; base < t1; base += 2 * NPB) {
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + NPB + u < t1) load(base + NPB + u, B[u]);
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + u < t1) comp(base + u, A[u]);
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + 2 * NPB + u < t1) load(base + 2 * NPB + u, A[u]);
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + NPB + u < t1) comp(base + NPB + u, B[u]);
-  }
-}
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-struct QK8Buf {
-  uint4 k0, k1;
-  float sk, sv;
-};
-template <int KS>
-struct QK16Buf {
-  uint4 kc[KS];
-  int32_t pr;
-};
-struct PV8Buf {
-  uint4 v;
-};
-template <int CBW>
-struct PV16Buf {
-  uint4 v[CBW];
-};
 
 template <bool kLds>
 struct Stage {
@@ -1497,945 +1007,6 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   }
 }
 
-// ========================================================= split-K attend
-// One layer's attend with ns workgroups per segment, for launches whose
-// B*Hkv segments alone would leave most CUs idle. Split c of a segment takes
-// the run of 32-row stage tiles [c*T/ns, (c+1)*T/ns) (T tiles in all: the
-// old region, then the ring) and computes, per query head, its own maximum
-// m_c, sum l_c = sum exp(s - m_c) and unnormalised PV partial O_c, and
-// stores the raw scores s of its rows. The split holding the new row's slot
-// appends it. A second launch, one workgroup per segment, combines
-// [CONF-KV abstract: blockwise online-softmax attention]:
-//   M = max_c m_c, L = sum_c l_c e^(m_c - M), out = sum_c O_c e^(m_c - M) / L,
-//   LSE = M + log L,
-// and, under CONF, updates every live row's EMA from the stored scores with
-// mass = mean over the G heads of exp(s - LSE) [Conf-KV post: EMA of the
-// attention mass]. The launch boundary orders the two: a device-scope fence
-// per workgroup would write back and invalidate its XCD's whole L2.
-// Arithmetic per split is that of the whole-segment kernel.
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_split_kernel(Layout lay, Params par,
-                                                                                           StepArgs a) {
-  constexpr int KS = D / 32;           // MFMA k-steps over d
-  constexpr int NCB = D / 16;          // 16-column blocks of d
-  constexpr int CBW = NCB / 4;         // PV column blocks per wave
-  static_assert(G <= 16, "a GQA group fits one MFMA tile");
-
-  __shared__ float red_m[4][G], red_l[4][G];
-  __shared__ uint32_t red_u[4];
-  extern __shared__ float dyn_lds[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lq = lane >> 4, lj = lane & 15;
-  const int ns = a.ns;
-  const int sl = blockIdx.x / ns, c = blockIdx.x - sl * ns;  // local segment, split
-  const int seg = a.seg0 + sl;
-  const int t = a.t, Wr = lay.Wr, Wr32 = lay.Wr32;
-  const bool kvpop = par.policy == 1;
-
-  uint16_t* rk = lay.ring_k + (size_t)seg * Wr32 * D;
-  uint16_t* rvt = lay.ring_v + (size_t)seg * Wr32 * D;
-  const size_t obase = (size_t)seg * lay.cap32;
-  const uint8_t* okp = lay.old_k + obase * D * lay.old_bytes;
-  const uint8_t* ovt = lay.old_v + obase * D * lay.old_bytes;
-  const float* oks = lay.old_ks + obase;
-  const float* ovs = lay.old_vs + obase;
-  const size_t sbase = (size_t)seg * lay.rows_max;
-  int32_t* opos = lay.row_pos + sbase;
-  float* oema = lay.row_ema + sbase;
-  int32_t* rpos = opos + lay.cap32;
-  float* rema = oema + lay.cap32;
-  float* rprio = lay.row_prio + sbase + lay.cap32;
-
-  const int n_old = lay.seg_nold[seg];
-  const int n_old32 = (n_old + 31) & ~31;
-  const int rows = n_old32 + Wr32;
-  const int T = rows >> 5;
-  const int r0 = (int)(((long long)c * T) / ns) * 32;
-  int r1 = (int)(((long long)(c + 1) * T) / ns) * 32;
-  // The host sizes the LDS planes for the longest run a split can get;
-  // should a run be longer, it is cut (every access stays in bounds) and an
-  // internal error is raised.
-  const bool cut = r1 - r0 > a.lds_rows;
-  if (cut) r1 = r0 + a.lds_rows;
-  const int rs = a.lds_rows;
-  auto st = [&](int g, int j) -> float& { return dyn_lds[g * rs + j]; };
-  float* svl = dyn_lds + G * rs;  // V scales of the run's old rows (from the QK loads)
-
-  const int slot_new = t % Wr;
-  const int i_new = n_old32 + slot_new;
-  const bool owner = i_new >= r0 && i_new < r1;  // this split appends the new row
-  const int pos_prio = (kvpop && t - par.P >= par.s) ? t - par.P : -1;
-  const uint16_t* kn = a.k_new + (size_t)sl * D;
-
-  // ---- q as MFMA A operands (see the whole-segment kernel)
-  const uint16_t* qrow = a.q + ((size_t)sl * G + (lj < G ? lj : 0)) * D;
-  half8 qa8[KS], qa16[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-    qa16[kk] = lj < G ? as_h8(u16) : half8{};
-  }
-  uint4 kn4 = make_uint4(0u, 0u, 0u, 0u);
-  uint16_t vn1 = 0;
-  float prio_now = 0.0f;
-  int32_t pos_prio_slot = -1;
-  if (owner) {
-    kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
-    vn1 = a.v_new[(size_t)sl * D + tid % D];
-    if (pos_prio >= 0) {
-      prio_now = a.prio_new[sl];
-      pos_prio_slot = rpos[pos_prio % Wr];
-    }
-  }
-
-  const float sm = par.sm_scale;
-  float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float sv_max = 0.0f;
-  // ---- ring QK over this run's ring slots [ra, rb)
-  const int ra = max(r0, n_old32) - n_old32, rb = r1 - n_old32;
-  if (rb > ra) {
-    const int nt_ring = (Wr + 15) >> 4;
-    const int g0 = ra >> 4, g1 = min(rb >> 4, nt_ring);
-    const int n = max(g1 - g0, 0);
-    const int ta = g0 + ((wave * n) >> 2), tb = g0 + (((wave + 1) * n) >> 2);
-    pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
-        ta, tb,
-        [&](int tt, QK16Buf<KS>& bf) {
-          const int r = 16 * tt + lj;
-          // lanes past the last slot read the tile's first row (same lines, no traffic)
-          const uint16_t* kr = r == slot_new ? kn : rk + (size_t)(r < Wr ? r : 16 * tt) * D;
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
-          bf.pr = rpos[r];
-        },
-        [&](int tt, const QK16Buf<KS>& bf) {
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
-          const int r = 16 * tt + lj;
-          const bool valid = r < Wr && (bf.pr >= 0 || r == slot_new);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int g = 4 * lq + rr;
-            if (g < G) {
-              const float sc = valid ? acc[rr] * sm : -INFINITY;
-              st(g, n_old32 + r - r0) = sc;
-              mrun[rr] = fmaxf(mrun[rr], sc);
-            }
-          }
-        });
-    for (int r = max(ra, 16 * nt_ring) + tid; r < rb; r += kThreads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) st(g, n_old32 + r - r0) = -INFINITY;
-  }
-  // ---- append of the new row by the split that holds its slot (the slot's
-  // previous row left the window at the end of the last step)
-  if (owner) {
-    if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
-    if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
-    if (tid == 0) {
-      rpos[slot_new] = t;
-      rema[slot_new] = 0.0f;
-      rprio[slot_new] = 0.0f;
-      // [KVpop summary §2.3] delayed scoring
-      if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
-    }
-  }
-  // ---- old-region QK over this run's old rows [r0, oe)
-  const int oe = min(r1, n_old32);
-  if (oe > r0) {
-    const int n = (oe - r0) >> 4;
-    const int ta = (r0 >> 4) + ((wave * n) >> 2), tb = (r0 >> 4) + (((wave + 1) * n) >> 2);
-    if (par.old_int8) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
-        qa8[kk] = lj < G ? as_h8(u8) : half8{};
-      }
-      pipelined<CONFKV_QK8_NPB, QK8Buf>(
-          ta, tb,
-          [&](int tt, QK8Buf& bf) {
-            const int row = 16 * tt + lj, rl = row < n_old ? row : 16 * tt;
-            const uint8_t* kr = okp + (size_t)rl * D;
-            bf.k0 = ldnt4(kr + 16 * lq);
-            if constexpr (D == 128) bf.k1 = ldnt4(kr + 16 * (lq + 4));
-            bf.sk = oks[rl];
-            bf.sv = ovs[rl];
-          },
-          [&](int tt, const QK8Buf& bf) {
-            half8 b0, b1;
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            i8x16_to_h8(bf.k0, b0, b1);
-            acc = mfma16(qa8[0], b0, acc);
-            acc = mfma16(qa8[1], b1, acc);
-            if constexpr (D == 128) {
-              half8 b2, b3;
-              i8x16_to_h8(bf.k1, b2, b3);
-              acc = mfma16(qa8[2], b2, acc);
-              acc = mfma16(qa8[3], b3, acc);
-            }
-            const int row = 16 * tt + lj;
-            const bool valid = row < n_old;
-            if (valid) sv_max = fmaxf(sv_max, bf.sv);
-            if (lq == 0) svl[row - r0] = bf.sv;
-            const float f = bf.sk * sm;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int g = 4 * lq + r;
-              if (g < G) {
-                const float sc = valid ? acc[r] * f : -INFINITY;
-                st(g, row - r0) = sc;
-                mrun[r] = fmaxf(mrun[r], sc);
-              }
-            }
-          });
-    } else {
-      pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
-          ta, tb,
-          [&](int tt, QK16Buf<KS>& bf) {
-            const int row = 16 * tt + lj, rl = row < n_old ? row : 16 * tt;
-            const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)rl * D;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
-          },
-          [&](int tt, const QK16Buf<KS>& bf) {
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa16[kk], as_h8(bf.kc[kk]), acc);
-            const int row = 16 * tt + lj;
-            const bool valid = row < n_old;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int g = 4 * lq + r;
-              if (g < G) {
-                const float sc = valid ? acc[r] * sm : -INFINITY;
-                st(g, row - r0) = sc;
-                mrun[r] = fmaxf(mrun[r], sc);
-              }
-            }
-          });
-    }
-  }
-  // ---- the first batch of this run's INT8 V tiles, loaded now so that the
-  // loads overlap the maxima barrier and the weight pass
-  const int pv_t0 = r0 >> 5, pv_t1 = oe > r0 ? oe >> 5 : pv_t0;
-  constexpr int NPRE = CONFKV_PV8_NPB;
-  PV8Buf vpre[NPRE];
-  auto load_pv8 = [&](int tt, PV8Buf& bf) {
-    const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * (32 * tt + 8 * lq < n_old ? lane : lj);
-    if constexpr (CBW == 2) {
-      bf.v = ldnt4(tb + 1024 * wave);
-    } else {
-      const uint2 hh = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-      bf.v = make_uint4(hh.x, hh.y, 0u, 0u);
-    }
-  };
-  if (par.old_int8) {
-#pragma unroll
-    for (int u = 0; u < NPRE; ++u)
-      if (pv_t0 + u < pv_t1) load_pv8(pv_t0 + u, vpre[u]);
-  }
-  // ---- this run's maxima per head and of the INT8 V scales
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float m = mrun[r];
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const int g = 4 * lq + r;
-    if (lj == 0 && g < G) red_m[wave][g] = m;
-  }
-  sv_max = wave_max(sv_max);
-  if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
-  __syncthreads();
-  float Mc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) Mc[g] = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
-  float svm = 0.0f;
-  for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
-  int fexp = 10;
-  if (svm > 0.0f) {
-    int e2;
-    frexpf(svm, &e2);
-    fexp = min(10, max(-30, 14 - e2));
-  }
-  const float fscale = ldexpf(1.0f, fexp), finv = ldexpf(1.0f, -fexp);
-
-  // ---- weights: p = exp(s - m_c) (0 for a run without a valid row), the
-  // raw scores kept for the combine's EMA pass
-  float lpart[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
-  float* sco = lay.sk_s + (size_t)sl * G * lay.rows_max;
-  for (int j = tid; j < r1 - r0; j += kThreads) {
-    const int i = r0 + j;
-    const float sv = (i < n_old && par.old_int8) ? svl[j] : 0.0f;
-    const float scf = ((i < n_old && par.old_int8 && sv > 0.0f) ? sv : 1.0f) * fscale;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float s = st(g, j);
-      if (!kvpop) sco[(size_t)g * lay.rows_max + i] = s;
-      const float p = Mc[g] == -INFINITY ? 0.0f : __expf(s - Mc[g]);
-      lpart[g] += p;
-      const float wv = p * scf;
-      const _Float16 hi = (_Float16)wv, lo = (_Float16)(wv - (float)hi);
-      st(g, j) = __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                                                ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float v = wave_sum(lpart[g]);
-    if (lane == 0) red_l[wave][g] = v;
-  }
-  __syncthreads();
-
-  // ---- PV over this run's 32-row tiles (waves split the columns)
-  floatx4 O[CBW];
-#pragma unroll
-  for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto weights = [&](int j, half8& ahi, half8& alo) {  // local stage row j
-    if (lj < G) {
-      const float4 p0 = *reinterpret_cast<const float4*>(&st(lj, j));
-      const float4 p1 = *reinterpret_cast<const float4*>(&st(lj, j + 4));
-      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
-                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
-                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
-                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
-      uint4 h, lw;
-      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
-      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
-      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
-      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
-      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
-      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
-      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
-      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
-      ahi = as_h8(h);
-      alo = as_h8(lw);
-    } else {
-      ahi = half8{};
-      alo = half8{};
-    }
-  };
-  // tiles [t0, t1) of vbase, local stage row j0 + 32*(tt-t0); lanes whose 8
-  // rows lie past the region's nvalid rows read lane group 0's
-  auto pv16 = [&](const uint16_t* vbase, int j0, int t0, int t1, int nvalid) {
-    pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
-        t0, t1,
-        [&](int tt, PV16Buf<CBW>& bf) {
-          const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * (32 * tt + 8 * lq < nvalid ? lane : lj);
-#pragma unroll
-          for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
-        },
-        [&](int tt, const PV16Buf<CBW>& bf) {
-          half8 ahi, alo;
-          weights(j0 + 32 * (tt - t0) + 8 * lq, ahi, alo);
-#pragma unroll
-          for (int k = 0; k < CBW; ++k) {
-            O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
-            O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
-          }
-        });
-  };
-  if (oe > r0) {
-    const int t0 = r0 >> 5, t1 = oe >> 5;
-    if (par.old_int8) {
-      auto pv8 = [&](int tt, const PV8Buf& bf) {
-        half8 ahi, alo, blo, bhi;
-        weights(32 * tt - r0 + 8 * lq, ahi, alo);
-        i8x16_to_h8(bf.v, blo, bhi);
-        O[0] = mfma16(ahi, blo, O[0]);
-        O[0] = mfma16(alo, blo, O[0]);
-        if constexpr (CBW == 2) {
-          O[1] = mfma16(ahi, bhi, O[1]);
-          O[1] = mfma16(alo, bhi, O[1]);
-        }
-      };
-#pragma unroll
-      for (int u = 0; u < NPRE; ++u)
-        if (t0 + u < t1) pv8(t0 + u, vpre[u]);
-      pipelined<CONFKV_PV8_NPB, PV8Buf>(t0 + NPRE, t1, load_pv8, pv8);
-    } else {
-      pv16(reinterpret_cast<const uint16_t*>(ovt), 0, t0, t1, n_old);
-    }
-  }
-  if (rb > ra) pv16(rvt, max(r0, n_old32) - r0, ra >> 5, rb >> 5, Wr);
-
-  // ---- this split's partials: O_c (unnormalised, f removed), m_c, l_c
-  const size_t pbase = (size_t)sl * lay.ns_max + c;
-#pragma unroll
-  for (int k = 0; k < CBW; ++k) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int g = 4 * lq + r;
-      if (g < G) lay.sk_o[(pbase * G + g) * D + 16 * (CBW * wave + k) + lj] = O[k][r] * finv;
-    }
-  }
-  if (tid < G) {
-    const float l = red_l[0][tid] + red_l[1][tid] + red_l[2][tid] + red_l[3][tid];
-    lay.sk_ml[pbase * G + tid] = SplitML{Mc[tid], l};
-  }
-  if (tid == 0 && cut) atomicOr(lay.err, kErrInternal);
-}
-
-// The combine of a split-K attend: one workgroup per segment of the layer.
-// The splits' statistics go through LDS once; every load that follows is
-// issued in batches, so the combine costs a few load latencies.
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads) attend_combine_kernel(Layout lay, Params par, StepArgs a) {
-  constexpr int KMAX = 32;  // most splits per segment
-  __shared__ float sh_m[G][KMAX], sh_l[G][KMAX], sh_f[G][KMAX];
-  __shared__ float sh_lse[G];
-  const int tid = threadIdx.x;
-  const int ns = a.ns;
-  const int sl = blockIdx.x, seg = a.seg0 + sl;
-  const int t = a.t, Wr = lay.Wr;
-  const bool kvpop = par.policy == 1;
-  const size_t pbase = (size_t)sl * lay.ns_max;
-  if (tid < G * ns) {
-    const int k = tid / G, g = tid - k * G;
-    const SplitML ml = lay.sk_ml[(pbase + k) * G + g];
-    sh_m[g][k] = ml.m;
-    sh_l[g][k] = ml.l;
-  }
-  __syncthreads();
-  // per head: M = max m_k, L = sum l_k e^(m_k - M); weights e^(m_k - M) / L
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, sh_m[tid][k]);
-    float L = 0.0f;
-    for (int k = 0; k < ns; ++k) L += sh_m[tid][k] == -INFINITY ? 0.0f : sh_l[tid][k] * __expf(sh_m[tid][k] - M);
-    const float il = 1.0f / L;
-    for (int k = 0; k < ns; ++k) sh_f[tid][k] = sh_m[tid][k] == -INFINITY ? 0.0f : __expf(sh_m[tid][k] - M) * il;
-    sh_lse[tid] = M + logf(L);
-  }
-  __syncthreads();
-  // out = sum_k O_k * e^(m_k - M) / L, eight splits' loads at a time
-  const float* po = lay.sk_o + pbase * G * D;
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int g = e / D;
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < ns; k0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = k0 + u < ns ? po[(size_t)(k0 + u) * G * D + e] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += k0 + u < ns ? v[u] * sh_f[g][k0 + u] : 0.0f;
-    }
-    a.out[(size_t)sl * G * D + e] = f2h(acc);
-  }
-  if (par.record && tid < G) lay.rec_lse[(size_t)seg * G + tid] = sh_lse[tid];
-  if (kvpop) return;
-  // ---- EMA of every live row from the stored scores, four rows per thread
-  // per batch with every load of the batch issued first
-  const size_t sbase = (size_t)seg * lay.rows_max;
-  const int32_t* opos = lay.row_pos + sbase;
-  float* oema = lay.row_ema + sbase;
-  const int n_old = lay.seg_nold[seg];
-  const int n_old32 = (n_old + 31) & ~31;
-  const int rows = n_old32 + lay.Wr32;
-  const int slot_new = t % Wr;
-  const float* sco = lay.sk_s + (size_t)sl * G * lay.rows_max;
-  float lse[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) lse[g] = sh_lse[g];
-  constexpr int RB = 4;
-  for (int i0 = tid; i0 < rows; i0 += kThreads * RB) {
-    int32_t p[RB];
-    float ev[RB], sc[RB][G];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = min(i0 + kThreads * u, rows - 1);
-      const int r = i - n_old32;
-      const int ix = r < 0 ? i : lay.cap32 + min(r, lay.Wr32 - 1);
-      p[u] = opos[ix];
-      ev[u] = oema[ix];
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[u][g] = sco[(size_t)g * lay.rows_max + i];
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = i0 + kThreads * u;
-      if (i >= rows) continue;
-      const int r = i - n_old32;
-      const bool is_old = i < n_old, is_ring = r >= 0 && r < Wr;
-      const bool is_new = is_ring && r == slot_new;
-      if (!(is_old || (is_ring && (is_new || p[u] >= 0)))) continue;
-      float mass = 0.0f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) mass += __expf(sc[u][g] - lse[g]);
-      mass *= 1.0f / (float)G;
-      oema[is_old ? i : lay.cap32 + r] = par.beta * (is_new ? 0.0f : ev[u]) + (1.0f - par.beta) * mass;
-    }
-  }
-}
-
-// ==================================================== KVpop prefill mask
-// [KVpop summary §2.4] The k long-range slots follow a running threshold over
-// static priorities, so the sparse mask of a prefill over S known priorities
-// is generated inside the attention kernel, never stored as S x S. Query q
-// may see key j iff
-//   j <= q and (j < s or j >= q - w or rank(j) <= thr(q)),
-// where rank orders positions >= s by (priority descending, position
-// ascending) and thr(q) is the k-th smallest rank among [s, q-1-w]: the rows
-// a decode step at q attends to. Per segment (batch row, KV head): a sort
-// gives the ranks, one pass over q moves the threshold, and the attention
-// kernel evaluates the predicate per (query, key).
-
-// Ranks: keys (orderable priority << 32 | ~position) sorted descending by a
-// bitonic network in the workspace, then rank[position] = sorted index
-// (-1 for sinks).
-__global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
-  const int tid = threadIdx.x, seg = blockIdx.x;
-  const int S = pa.S, s = pa.sinks, N = pa.N;
-  const float* pr = pa.prio + (size_t)seg * S;
-  uint64_t* A = pa.sort + (size_t)seg * N;
-  int32_t* rank = pa.rank + (size_t)seg * S;
-  for (int i = tid; i < N; i += 1024) {
-    const int j = s + i;
-    A[i] = j < S ? rank_key(pr[j], j) : 0ull;  // padding sorts last
-    if (j < S && !isfinite(pr[j])) atomicOr(pa.err, kErrNonFinite);
-  }
-  for (int j = tid; j < min(s, S); j += 1024) rank[j] = -1;
-  __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < N; i += 1024) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const uint64_t a = A[i], b = A[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            A[i] = b;
-            A[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < S - s; i += 1024) rank[0xFFFFFFFFu - (uint32_t)A[i]] = i;
-}
-
-// Thresholds: one pass over q. Position q-1-w joins the candidates at query
-// q; a bitmap over ranks holds the candidates. With n candidates, thr = S
-// (all pass) while n < k, the largest rank at n = k, and after that an
-// inserted rank below thr moves thr to the next candidate rank below it
-// (the old k-th is pushed out). k = 0 gives thr = -1 (none pass). Once
-// n >= k a rank above thr is never the threshold again (thr only moves
-// down, and the search for the next rank runs below it), so it is not
-// entered in the bitmap.
-__global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
-  extern __shared__ uint32_t kbits[];  // ceil(N/32) words, then 1024 staged ranks
-  const int tid = threadIdx.x, seg = blockIdx.x;
-  const int S = pa.S, s = pa.sinks, w = pa.window, k = pa.topk, nw = (pa.N + 31) >> 5;
-  int32_t* stage = reinterpret_cast<int32_t*>(kbits + nw);
-  const int32_t* rank = pa.rank + (size_t)seg * S;
-  int32_t* thr = pa.thr + (size_t)seg * S;
-  for (int i = tid; i < nw; i += 64) kbits[i] = 0u;
-  int n = 0, t = k > 0 ? S : -1, maxr = -1;
-  for (int q0 = 0; q0 < S; q0 += 1024) {
-    __syncthreads();
-    for (int i = tid; i < 1024; i += 64) {
-      const int p = q0 + i - 1 - w;
-      stage[i] = (q0 + i < S && p >= s) ? rank[p] : -2;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      const int cnt = min(1024, S - q0);
-      for (int i = 0; i < cnt; ++i) {
-        const int r = stage[i];
-        if (r >= 0 && k > 0) {
-          ++n;
-          if (n <= k) {
-            kbits[r >> 5] |= 1u << (r & 31);
-            maxr = max(maxr, r);
-            if (n == k) t = maxr;
-          } else if (r < t) {
-            kbits[r >> 5] |= 1u << (r & 31);
-            int wi = t >> 5;
-            uint32_t word = kbits[wi] & ((1u << (t & 31)) - 1u);
-            while (word == 0u) word = kbits[--wi];
-            t = (wi << 5) + 31 - __clz((int)word);
-          }
-        }
-        thr[q0 + i] = t;
-      }
-    }
-  }
-}
-
-constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
-constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
-
-// Masked prefill attention: one workgroup per 32 queries of a segment (16
-// when a wave serves two query heads). The key list holds the sinks, the
-// long-range keys that pass the first query's threshold (a superset for the
-// later queries, whose thresholds are no larger), and the contiguous run
-// [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
-// (transposed) go through LDS once for all the workgroup's queries; wave w
-// takes query heads w, w+4, ... for its 16-query blocks: S^T = K Q^T on
-// MFMA, the predicate per (key, query), online softmax per query in the
-// base-2 domain, and O^T = V^T P^T with the weights as fp16 hi and lo parts.
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
-  constexpr int KS = D / 32, NCB = D / 16;
-  constexpr int HPW = (G + 3) / 4;              // query heads per wave
-  constexpr int QT = HPW == 1 ? 2 : 1;          // 16-query blocks per head
-  constexpr int QB = 16 * QT;                   // queries per workgroup
-  constexpr int NR = HPW * QT;                  // 16-row blocks per wave
-  constexpr int KSTR = D + 8;   // K tile row stride (halves)
-  constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
-  constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
-  constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
-  extern __shared__ __align__(16) uint16_t plds[];
-  uint16_t* Kt = plds;                        // [32][KSTR]
-  uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
-  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + D * VSTR);
-  int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
-  __shared__ uint32_t red[4];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lq = lane >> 4, lj = lane & 15;
-  const int S = pa.S, s = pa.sinks, w = pa.window;
-  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int q0 = QB * blockIdx.x, q1 = min(q0 + QB, S);
-  const int32_t* rank = pa.rank + (size_t)seg * S;
-  const int32_t* thr = pa.thr + (size_t)seg * S;
-  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
-  const uint16_t* vseg = pa.v + (size_t)seg * S * D;
-
-  // ---- key list: sinks, long-range keys passing thr(q0), contiguous run
-  const int n_sink = min(s, q1);
-  const int g_end = max(s, q0 - w);            // long-range positions [s, g_end)
-  const int thr0 = thr[q0];
-  const int glen = g_end - s;
-  const int per = (glen + kThreads - 1) / kThreads;
-  const int ga = s + min(glen, tid * per), gb = s + min(glen, tid * per + per);
-  uint32_t cnt = 0;
-  for (int j = ga; j < gb; ++j) cnt += rank[j] <= thr0 ? 1u : 0u;
-  uint32_t ng;
-  uint32_t off = block_excl_scan_u32(cnt, red, &ng);
-  for (int j = ga; j < gb; ++j) {
-    const int r = rank[j];
-    if (r <= thr0) {
-      if (n_sink + (int)off < pa.list_cap) {
-        lpos[n_sink + off] = j;
-        lrank[n_sink + off] = r;
-      }
-      ++off;
-    }
-  }
-  const int c0 = g_end;
-  const int n_cont = max(0, q1 - c0);
-  const int nk = n_sink + (int)ng + n_cont;
-  for (int i = tid; i < n_sink; i += kThreads) {
-    lpos[i] = i;
-    lrank[i] = -1;
-  }
-  for (int i = tid; i < n_cont; i += kThreads) {
-    if (n_sink + (int)ng + i < pa.list_cap) {
-      lpos[n_sink + ng + i] = c0 + i;
-      lrank[n_sink + ng + i] = rank[c0 + i];
-    }
-  }
-  if (tid == 0 && nk > pa.list_cap) atomicOr(pa.err, kErrInternal);  // cannot happen: host bound
-  __syncthreads();
-  const int nkc = min(nk, pa.list_cap);
-
-  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT. The
-  // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
-  // that lane (lq, lj) receives query lj's scores against keys 8lq .. 8lq+7
-  // of the chunk: the softmax of a query stays in one lane group, and its
-  // eight weights are at once the lane's B operand of O^T = V^T P^T.
-  // Scores and maxima are kept in base-2 units (scale * log2(e) folded in).
-  const float sl2 = pa.scale * kLog2e;
-  half8 qb[NR][KS];
-  float m[NR], l[NR];
-  int thr_q[NR];
-  floatx4 O[NR][NCB];
-#pragma unroll
-  for (int rb = 0; rb < NR; ++rb) {
-    const int g = wave + 4 * (rb / QT), qt = rb % QT;
-    const int hq = h * G + (g < G ? g : 0);
-    const int qrow = q0 + 16 * qt + lj;
-    const uint16_t* qp = pa.q + (((size_t)b * pa.Hq + hq) * S + min(qrow, S - 1)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (lq + 4 * kk));
-      qb[rb][kk] = qrow < q1 ? as_h8(u) : half8{};
-    }
-    m[rb] = -INFINITY;
-    l[rb] = 0.0f;
-    thr_q[rb] = qrow < q1 ? thr[qrow] : -1;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) O[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  // row lj of permuted block kb holds key 8*(lj/4) + 4*kb + lj%4 of the chunk
-  const int kperm0 = 8 * (lj >> 2) + (lj & 3);
-
-  // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
-  uint4 rk[PPT], rv[PPT];
-  auto load_chunk = [&](int c) {
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      if (e < PIECES) {
-        const int key = e / (D / 8), piece = e - key * (D / 8);
-        const int li = 32 * c + key;
-        const int pos = li < nkc ? lpos[li] : 0;
-        rk[u] = *reinterpret_cast<const uint4*>(kseg + (size_t)pos * D + 8 * piece);
-        rv[u] = *reinterpret_cast<const uint4*>(vseg + (size_t)pos * D + 8 * piece);
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      if (e < PIECES) {
-        const int key = e / (D / 8), piece = e - key * (D / 8);
-        *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
-        const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          Vt[(8 * piece + x) * VSTR + key] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
-      }
-    }
-  };
-  const int nchunks = (nkc + 31) >> 5;
-  if (nchunks > 0) load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    store_chunk();
-    __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
-    // this lane's eight keys of the chunk: list entries 32c + 8lq .. +7
-    int kpos[8], krank[8];
-    {
-      const int li0 = 32 * c + 8 * lq;
-      const uint4 p0 = *reinterpret_cast<const uint4*>(lpos + li0);
-      const uint4 p1 = *reinterpret_cast<const uint4*>(lpos + li0 + 4);
-      const uint4 r0v = *reinterpret_cast<const uint4*>(lrank + li0);
-      const uint4 r1v = *reinterpret_cast<const uint4*>(lrank + li0 + 4);
-      const int pp[8] = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-      const int rr[8] = {(int)r0v.x, (int)r0v.y, (int)r0v.z, (int)r0v.w,
-                         (int)r1v.x, (int)r1v.y, (int)r1v.z, (int)r1v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool in = li0 + e < nkc;
-        kpos[e] = in ? pp[e] : INT32_MAX;  // out of the list: never <= a query
-        krank[e] = rr[e];
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < NR; ++rb) {
-      if (wave + 4 * (rb / QT) >= G) continue;
-      const int qr = q0 + 16 * (rb % QT) + lj;
-      floatx4 acc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t* kr = Kt + (kperm0 + 4 * kb) * KSTR;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk))), qb[rb][kk], acc[kb]);
-      }
-      float sc[8];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = kpos[e];
-        const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
-        sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
-        mt = fmaxf(mt, sc[e]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[rb], mt);
-      const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
-      const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
-      float ls = 0.0f;
-      half8 phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sc[e] - ms);
-        ls += pe;
-        const _Float16 hi = (_Float16)pe;
-        phi[e] = hi;
-        plo[e] = (_Float16)(pe - (float)hi);
-      }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      l[rb] = l[rb] * alpha + ls;
-      m[rb] = mn;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
-        O[rb][cb] *= alpha;
-        O[rb][cb] = mfma16(av, phi, O[rb][cb]);
-        O[rb][cb] = mfma16(av, plo, O[rb][cb]);
-      }
-    }
-    __syncthreads();
-  }
-  // ---- output rows and LSE (natural log: m * ln 2 + ln l). Lane (lq, lj)
-  // holds O^T[column 16cb + 4lq + r][query lj].
-#pragma unroll
-  for (int rb = 0; rb < NR; ++rb) {
-    const int g = wave + 4 * (rb / QT), qt = rb % QT;
-    if (g >= G) continue;
-    const int hq = h * G + g;
-    const int qr = q0 + 16 * qt + lj;
-    if (qr < q1) {
-      const float il = 1.0f / l[rb];
-      uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint32_t lo = (uint32_t)f2h(O[rb][cb][0] * il) | ((uint32_t)f2h(O[rb][cb][1] * il) << 16);
-        const uint32_t hi = (uint32_t)f2h(O[rb][cb][2] * il) | ((uint32_t)f2h(O[rb][cb][3] * il) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * lq) = make_uint2(lo, hi);
-      }
-      if (pa.lse && lq == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[rb] * kLn2 + logf(l[rb]);
-    }
-  }
-}
-
-
-// Future-attention target [KVpop summary §2.2], the transposed pass: for key
-// t of a segment, log sum over the group's query heads g and the queries
-// d >= t + w of exp(s[d, g, t] - LSE[d, g]), with the queries' normalisers
-// handed in, so no attention map is formed. One workgroup per 128 keys; wave
-// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles. The later
-// queries stream through LDS in stages of four (16-query tile, head) pairs,
-// double-buffered and shared by the four waves; the MFMA gives
-// S^T[key][query] and each lane accumulates the masked exponentials.
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
-                                                                float* target) {
-  constexpr int KS = D / 32;
-  constexpr int QSTR = D + 8;                 // staged row stride (halves)
-  constexpr int NP = 4;                       // (tile, head) pairs per stage
-  constexpr int RP = D / 8;                   // 16-byte pieces per row
-  constexpr int PPT = NP * 16 * RP / kThreads;
-  static_assert(PPT * kThreads == NP * 16 * RP, "stage pieces divide the block");
-  __shared__ __align__(16) uint16_t qs[2][NP][16][QSTR];
-  __shared__ float ls[2][NP][16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lq = lane >> 4, lj = lane & 15;
-  const int S = pa.S, w = pa.window;
-  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int t0b = 128 * blockIdx.x;            // the workgroup's first key
-  const int t0 = t0b + 32 * wave;              // this wave's first key
-  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
-  const float sl2 = pa.scale * kLog2e;
-
-  half8 ka[2][KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int t = t0 + 16 * kb + lj;
-    const uint16_t* kr = kseg + (size_t)min(t, S - 1) * D;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
-      ka[kb][kk] = t < S ? as_h8(u) : half8{};
-    }
-  }
-  float acc[2][4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[kb][r] = 0.0f;
-
-  // (query tile, head) pairs from the first tile holding a counted query
-  const int x0 = (min(t0b + w, S) >> 4) * G, x1 = ((S + 15) >> 4) * G;
-  const int nst = (x1 - x0 + NP - 1) / NP;
-  uint4 pre[PPT];
-  float plse = 0.0f;
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
-      const int x = x0 + NP * st + pr;
-      if (x < x1) {
-        const int tile = x / G, g = x - tile * G;
-        const int d = min(16 * tile + row, S - 1);
-        pre[u] = *reinterpret_cast<const uint4*>(pa.q + (((size_t)b * pa.Hq + h * G + g) * S + d) * D + 8 * piece);
-      } else {
-        pre[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    if (tid < NP * 16) {
-      const int pr = tid >> 4, row = tid & 15;
-      const int x = x0 + NP * st + pr;
-      if (x < x1) {
-        const int tile = x / G, g = x - tile * G;
-        plse = lse_in[((size_t)b * pa.Hq + h * G + g) * S + min(16 * tile + row, S - 1)];
-      }
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
-      *reinterpret_cast<uint4*>(&qs[buf][pr][row][8 * piece]) = pre[u];
-    }
-    if (tid < NP * 16) ls[buf][tid >> 4][tid & 15] = plse;
-  };
-  if (nst > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) load_stage(st + 1);
-#pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-      const int x = x0 + NP * st + pr;
-      if (x >= x1) break;
-      const int d0 = 16 * (x / G), d = d0 + lj;
-      half8 qb[KS];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) qb[kk] = as_h8(*reinterpret_cast<const uint4*>(&qs[buf][pr][lj][8 * (lq + 4 * kk)]));
-      // exp(s*scale - lse) = 2^(c*scale*log2(e) - lse*log2(e)): one FMA and one exp2
-      const float nl2 = -ls[buf][pr][lj] * kLog2e;
-      // every query of this tile counts for every key of this wave
-      const bool full = d0 >= t0 + 31 + w && d0 + 15 < S;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], qb[kk], c);
-        if (full) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[kb][r] += __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 16 * kb + 4 * lq + r;
-            const bool counted = d < S && d >= t + w;
-            acc[kb][r] += counted ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2)) : 0.0f;
-          }
-        }
-      }
-    }
-    if (st + 1 < nst) store_stage(buf ^ 1);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float a = acc[kb][r];
-      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o, 64);
-      const int t = t0 + 16 * kb + 4 * lq + r;
-      if (lj == 0 && t < S) target[(size_t)seg * S + t] = a > 0.0f ? logf(a) : -INFINITY;
-    }
-  }
-}
-
 // ================================================================ init/ingest
 __global__ void zero_kernel(uint4* p, size_t n16) {
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -2616,8 +1187,6 @@ __global__ void __launch_bounds__(256) stats_total_kernel(Layout lay, int32_t re
 }
 
 // ================================================================ launchers
-static inline int ok_or_err() { return hipGetLastError() == hipSuccess ? 0 : -3; }
-
 int launch_init(const Layout& lay, const Params& par, void* state, size_t state_bytes, const uint16_t* pk,
                 const uint16_t* pv, int32_t P0, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -2634,15 +1203,6 @@ int launch_init(const Layout& lay, const Params& par, void* state, size_t state_
     else
       hipLaunchKernelGGL(ingest_kernel<128>, grid, dim3(256), 0, s, lay, par, pk, pv, P0);
   }
-  return ok_or_err();
-}
-
-int launch_sample(const Layout& lay, const float* logits, const float* u, int32_t* token, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(sample_reduce_kernel, dim3(lay.chunks, lay.B), dim3(256), 0, s, lay, logits,
-                     (int32_t)(u != nullptr));
-  if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL(sample_pick_kernel, dim3(lay.B), dim3(256), 0, s, lay, logits, u, token);
   return ok_or_err();
 }
 
@@ -2683,88 +1243,6 @@ static int launch_mode(const Layout& lay, const Params& par, const StepArgs& a, 
                        hipStream_t s) {
   if (lay.D == 64) return launch_fused_d<64, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
   if (lay.D == 128) return launch_fused_d<128, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
-  return -1;
-}
-
-template <int D, int G>
-static int launch_split_dg(const Layout& lay, const Params& par, const StepArgs& a, int lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL((attend_split_kernel<D, G>), dim3(lay.B * lay.Hkv * a.ns), dim3(kThreads), lds_bytes, s, lay,
-                     par, a);
-  if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL((attend_combine_kernel<D, G>), dim3(lay.B * lay.Hkv), dim3(kThreads), 0, s, lay, par, a);
-  return ok_or_err();
-}
-
-template <int D>
-static int launch_split_d(const Layout& lay, const Params& par, const StepArgs& a, int lds_bytes, hipStream_t s) {
-  switch (lay.G) {
-    case 1: return launch_split_dg<D, 1>(lay, par, a, lds_bytes, s);
-    case 2: return launch_split_dg<D, 2>(lay, par, a, lds_bytes, s);
-    case 4: return launch_split_dg<D, 4>(lay, par, a, lds_bytes, s);
-    case 5: return launch_split_dg<D, 5>(lay, par, a, lds_bytes, s);
-    case 8: return launch_split_dg<D, 8>(lay, par, a, lds_bytes, s);
-    default: return -1;
-  }
-}
-
-int launch_attend_split(const Layout& lay, const Params& par, const StepArgs& a, int lds_bytes, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (a.ns < 2 || a.ns > lay.ns_max) return -1;
-  if (lay.D == 64) return launch_split_d<64>(lay, par, a, lds_bytes, s);
-  if (lay.D == 128) return launch_split_d<128>(lay, par, a, lds_bytes, s);
-  return -1;
-}
-
-template <int D>
-static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipStream_t s) {
-  const int qb = pa.G <= 4 ? 32 : 16;  // queries per workgroup (see the kernel)
-  const dim3 grid((pa.S + qb - 1) / qb, pa.B * pa.Hkv);
-  switch (pa.G) {
-    case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 4: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 4>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 5: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 5>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 8: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 8>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    default: return -1;
-  }
-  return ok_or_err();
-}
-
-int kvpop_prefill_attend_lds(int D, int list_cap) {
-  return (32 * (D + 8) + D * 40) * 2 + ((list_cap + 31) & ~31) * 8;
-}
-
-int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  const int segs = pa.B * pa.Hkv;
-  hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), 0, s, pa);
-  if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4 + 1024 * 4, s, pa);
-  if (hipGetLastError() != hipSuccess) return -3;
-  const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
-  if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
-  if (pa.D == 128) return launch_kvpop_attend_d<128>(pa, lds, s);
-  return -1;
-}
-
-template <int D>
-static int launch_target_d(const KvpopPrefillArgs& pa, const float* lse, float* target, hipStream_t s) {
-  const dim3 grid((pa.S + 127) / 128, pa.B * pa.Hkv);
-  switch (pa.G) {
-    case 1: hipLaunchKernelGGL((kvpop_target_kernel<D, 1>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
-    case 2: hipLaunchKernelGGL((kvpop_target_kernel<D, 2>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
-    case 4: hipLaunchKernelGGL((kvpop_target_kernel<D, 4>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
-    case 5: hipLaunchKernelGGL((kvpop_target_kernel<D, 5>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
-    case 8: hipLaunchKernelGGL((kvpop_target_kernel<D, 8>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
-    default: return -1;
-  }
-  return ok_or_err();
-}
-
-int launch_kvpop_target(const KvpopPrefillArgs& pa, const float* lse, float* target, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (pa.D == 64) return launch_target_d<64>(pa, lse, target, s);
-  if (pa.D == 128) return launch_target_d<128>(pa, lse, target, s);
   return -1;
 }
 

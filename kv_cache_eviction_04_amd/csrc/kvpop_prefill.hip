@@ -1,0 +1,529 @@
+// HIP kernels for gfx950 (MI355X): KVpop's prefill over S tokens with known
+// priorities under the multi-query sink + window + top-k mask, and the
+// scorer's future-attention training target.
+//
+// Source: "Resumen Técnico: KVpop" (gist.science) §2.1, §2.2, §2.4.
+#include "device.h"
+
+namespace confkv {
+
+// ==================================================== KVpop prefill mask
+// [KVpop summary §2.4] The k long-range slots follow a running threshold over
+// static priorities, so the sparse mask of a prefill over S known priorities
+// is generated inside the attention kernel, never stored as S x S. Query q
+// may see key j iff
+//   j <= q and (j < s or j >= q - w or rank(j) <= thr(q)),
+// where rank orders positions >= s by (priority descending, position
+// ascending) and thr(q) is the k-th smallest rank among [s, q-1-w]: the rows
+// a decode step at q attends to. Per segment (batch row, KV head): a sort
+// gives the ranks, one pass over q moves the threshold, and the attention
+// kernel evaluates the predicate per (query, key).
+
+// Ranks: keys (orderable priority << 32 | ~position) sorted descending by a
+// bitonic network in the workspace, then rank[position] = sorted index
+// (-1 for sinks).
+__global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
+  const int tid = threadIdx.x, seg = blockIdx.x;
+  const int S = pa.S, s = pa.sinks, N = pa.N;
+  const float* pr = pa.prio + (size_t)seg * S;
+  uint64_t* A = pa.sort + (size_t)seg * N;
+  int32_t* rank = pa.rank + (size_t)seg * S;
+  for (int i = tid; i < N; i += 1024) {
+    const int j = s + i;
+    A[i] = j < S ? rank_key(pr[j], j) : 0ull;  // padding sorts last
+    if (j < S && !isfinite(pr[j])) atomicOr(pa.err, kErrNonFinite);
+  }
+  for (int j = tid; j < min(s, S); j += 1024) rank[j] = -1;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < N; i += 1024) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const uint64_t a = A[i], b = A[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            A[i] = b;
+            A[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < S - s; i += 1024) rank[0xFFFFFFFFu - (uint32_t)A[i]] = i;
+}
+
+// Thresholds: one pass over q. Position q-1-w joins the candidates at query
+// q; a bitmap over ranks holds the candidates. With n candidates, thr = S
+// (all pass) while n < k, the largest rank at n = k, and after that an
+// inserted rank below thr moves thr to the next candidate rank below it
+// (the old k-th is pushed out). k = 0 gives thr = -1 (none pass). Once
+// n >= k a rank above thr is never the threshold again (thr only moves
+// down, and the search for the next rank runs below it), so it is not
+// entered in the bitmap.
+__global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
+  extern __shared__ uint32_t kbits[];  // ceil(N/32) words, then 1024 staged ranks
+  const int tid = threadIdx.x, seg = blockIdx.x;
+  const int S = pa.S, s = pa.sinks, w = pa.window, k = pa.topk, nw = (pa.N + 31) >> 5;
+  int32_t* stage = reinterpret_cast<int32_t*>(kbits + nw);
+  const int32_t* rank = pa.rank + (size_t)seg * S;
+  int32_t* thr = pa.thr + (size_t)seg * S;
+  for (int i = tid; i < nw; i += 64) kbits[i] = 0u;
+  int n = 0, t = k > 0 ? S : -1, maxr = -1;
+  for (int q0 = 0; q0 < S; q0 += 1024) {
+    __syncthreads();
+    for (int i = tid; i < 1024; i += 64) {
+      const int p = q0 + i - 1 - w;
+      stage[i] = (q0 + i < S && p >= s) ? rank[p] : -2;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const int cnt = min(1024, S - q0);
+      for (int i = 0; i < cnt; ++i) {
+        const int r = stage[i];
+        if (r >= 0 && k > 0) {
+          ++n;
+          if (n <= k) {
+            kbits[r >> 5] |= 1u << (r & 31);
+            maxr = max(maxr, r);
+            if (n == k) t = maxr;
+          } else if (r < t) {
+            kbits[r >> 5] |= 1u << (r & 31);
+            int wi = t >> 5;
+            uint32_t word = kbits[wi] & ((1u << (t & 31)) - 1u);
+            while (word == 0u) word = kbits[--wi];
+            t = (wi << 5) + 31 - __clz((int)word);
+          }
+        }
+        thr[q0 + i] = t;
+      }
+    }
+  }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
+
+// Masked prefill attention: one workgroup per 32 queries of a segment (16
+// when a wave serves two query heads). The key list holds the sinks, the
+// long-range keys that pass the first query's threshold (a superset for the
+// later queries, whose thresholds are no larger), and the contiguous run
+// [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
+// (transposed) go through LDS once for all the workgroup's queries; wave w
+// takes query heads w, w+4, ... for its 16-query blocks: S^T = K Q^T on
+// MFMA, the predicate per (key, query), online softmax per query in the
+// base-2 domain, and O^T = V^T P^T with the weights as fp16 hi and lo parts.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+  constexpr int KS = D / 32, NCB = D / 16;
+  constexpr int HPW = (G + 3) / 4;              // query heads per wave
+  constexpr int QT = HPW == 1 ? 2 : 1;          // 16-query blocks per head
+  constexpr int QB = 16 * QT;                   // queries per workgroup
+  constexpr int NR = HPW * QT;                  // 16-row blocks per wave
+  constexpr int KSTR = D + 8;   // K tile row stride (halves)
+  constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
+  constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
+  constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
+  extern __shared__ __align__(16) uint16_t plds[];
+  uint16_t* Kt = plds;                        // [32][KSTR]
+  uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
+  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + D * VSTR);
+  int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
+  __shared__ uint32_t red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, lj = lane & 15;
+  const int S = pa.S, s = pa.sinks, w = pa.window;
+  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int q0 = QB * blockIdx.x, q1 = min(q0 + QB, S);
+  const int32_t* rank = pa.rank + (size_t)seg * S;
+  const int32_t* thr = pa.thr + (size_t)seg * S;
+  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
+  const uint16_t* vseg = pa.v + (size_t)seg * S * D;
+
+  // ---- key list: sinks, long-range keys passing thr(q0), contiguous run
+  const int n_sink = min(s, q1);
+  const int g_end = max(s, q0 - w);            // long-range positions [s, g_end)
+  const int thr0 = thr[q0];
+  const int glen = g_end - s;
+  const int per = (glen + kThreads - 1) / kThreads;
+  const int ga = s + min(glen, tid * per), gb = s + min(glen, tid * per + per);
+  uint32_t cnt = 0;
+  for (int j = ga; j < gb; ++j) cnt += rank[j] <= thr0 ? 1u : 0u;
+  uint32_t ng;
+  uint32_t off = block_excl_scan_u32(cnt, red, &ng);
+  for (int j = ga; j < gb; ++j) {
+    const int r = rank[j];
+    if (r <= thr0) {
+      if (n_sink + (int)off < pa.list_cap) {
+        lpos[n_sink + off] = j;
+        lrank[n_sink + off] = r;
+      }
+      ++off;
+    }
+  }
+  const int c0 = g_end;
+  const int n_cont = max(0, q1 - c0);
+  const int nk = n_sink + (int)ng + n_cont;
+  for (int i = tid; i < n_sink; i += kThreads) {
+    lpos[i] = i;
+    lrank[i] = -1;
+  }
+  for (int i = tid; i < n_cont; i += kThreads) {
+    if (n_sink + (int)ng + i < pa.list_cap) {
+      lpos[n_sink + ng + i] = c0 + i;
+      lrank[n_sink + ng + i] = rank[c0 + i];
+    }
+  }
+  if (tid == 0 && nk > pa.list_cap) atomicOr(pa.err, kErrInternal);  // cannot happen: host bound
+  __syncthreads();
+  const int nkc = min(nk, pa.list_cap);
+
+  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT. The
+  // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
+  // that lane (lq, lj) receives query lj's scores against keys 8lq .. 8lq+7
+  // of the chunk: the softmax of a query stays in one lane group, and its
+  // eight weights are at once the lane's B operand of O^T = V^T P^T.
+  // Scores and maxima are kept in base-2 units (scale * log2(e) folded in).
+  const float sl2 = pa.scale * kLog2e;
+  half8 qb[NR][KS];
+  float m[NR], l[NR];
+  int thr_q[NR];
+  floatx4 O[NR][NCB];
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const int g = wave + 4 * (rb / QT), qt = rb % QT;
+    const int hq = h * G + (g < G ? g : 0);
+    const int qrow = q0 + 16 * qt + lj;
+    const uint16_t* qp = pa.q + (((size_t)b * pa.Hq + hq) * S + min(qrow, S - 1)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (lq + 4 * kk));
+      qb[rb][kk] = qrow < q1 ? as_h8(u) : half8{};
+    }
+    m[rb] = -INFINITY;
+    l[rb] = 0.0f;
+    thr_q[rb] = qrow < q1 ? thr[qrow] : -1;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) O[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // row lj of permuted block kb holds key 8*(lj/4) + 4*kb + lj%4 of the chunk
+  const int kperm0 = 8 * (lj >> 2) + (lj & 3);
+
+  // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
+  uint4 rk[PPT], rv[PPT];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      if (e < PIECES) {
+        const int key = e / (D / 8), piece = e - key * (D / 8);
+        const int li = 32 * c + key;
+        const int pos = li < nkc ? lpos[li] : 0;
+        rk[u] = *reinterpret_cast<const uint4*>(kseg + (size_t)pos * D + 8 * piece);
+        rv[u] = *reinterpret_cast<const uint4*>(vseg + (size_t)pos * D + 8 * piece);
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      if (e < PIECES) {
+        const int key = e / (D / 8), piece = e - key * (D / 8);
+        *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
+        const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          Vt[(8 * piece + x) * VSTR + key] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
+      }
+    }
+  };
+  const int nchunks = (nkc + 31) >> 5;
+  if (nchunks > 0) load_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    store_chunk();
+    __syncthreads();
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    // this lane's eight keys of the chunk: list entries 32c + 8lq .. +7
+    int kpos[8], krank[8];
+    {
+      const int li0 = 32 * c + 8 * lq;
+      const uint4 p0 = *reinterpret_cast<const uint4*>(lpos + li0);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(lpos + li0 + 4);
+      const uint4 r0v = *reinterpret_cast<const uint4*>(lrank + li0);
+      const uint4 r1v = *reinterpret_cast<const uint4*>(lrank + li0 + 4);
+      const int pp[8] = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+      const int rr[8] = {(int)r0v.x, (int)r0v.y, (int)r0v.z, (int)r0v.w,
+                         (int)r1v.x, (int)r1v.y, (int)r1v.z, (int)r1v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = li0 + e < nkc;
+        kpos[e] = in ? pp[e] : INT32_MAX;  // out of the list: never <= a query
+        krank[e] = rr[e];
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb) {
+      if (wave + 4 * (rb / QT) >= G) continue;
+      const int qr = q0 + 16 * (rb % QT) + lj;
+      floatx4 acc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        acc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t* kr = Kt + (kperm0 + 4 * kb) * KSTR;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk))), qb[rb][kk], acc[kb]);
+      }
+      float sc[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = kpos[e];
+        const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
+        sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+        mt = fmaxf(mt, sc[e]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m[rb], mt);
+      const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
+      const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
+      float ls = 0.0f;
+      half8 phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sc[e] - ms);
+        ls += pe;
+        const _Float16 hi = (_Float16)pe;
+        phi[e] = hi;
+        plo[e] = (_Float16)(pe - (float)hi);
+      }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l[rb] = l[rb] * alpha + ls;
+      m[rb] = mn;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
+        O[rb][cb] *= alpha;
+        O[rb][cb] = mfma16(av, phi, O[rb][cb]);
+        O[rb][cb] = mfma16(av, plo, O[rb][cb]);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- output rows and LSE (natural log: m * ln 2 + ln l). Lane (lq, lj)
+  // holds O^T[column 16cb + 4lq + r][query lj].
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const int g = wave + 4 * (rb / QT), qt = rb % QT;
+    if (g >= G) continue;
+    const int hq = h * G + g;
+    const int qr = q0 + 16 * qt + lj;
+    if (qr < q1) {
+      const float il = 1.0f / l[rb];
+      uint16_t* orow = pa.out + (((size_t)b * pa.Hq + hq) * S + qr) * D;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint32_t lo = (uint32_t)f2h(O[rb][cb][0] * il) | ((uint32_t)f2h(O[rb][cb][1] * il) << 16);
+        const uint32_t hi = (uint32_t)f2h(O[rb][cb][2] * il) | ((uint32_t)f2h(O[rb][cb][3] * il) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * cb + 4 * lq) = make_uint2(lo, hi);
+      }
+      if (pa.lse && lq == 0) pa.lse[((size_t)b * pa.Hq + hq) * S + qr] = m[rb] * kLn2 + logf(l[rb]);
+    }
+  }
+}
+
+
+// Future-attention target [KVpop summary §2.2], the transposed pass: for key
+// t of a segment, log sum over the group's query heads g and the queries
+// d >= t + w of exp(s[d, g, t] - LSE[d, g]), with the queries' normalisers
+// handed in, so no attention map is formed. One workgroup per 128 keys; wave
+// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles. The later
+// queries stream through LDS in stages of four (16-query tile, head) pairs,
+// double-buffered and shared by the four waves; the MFMA gives
+// S^T[key][query] and each lane accumulates the masked exponentials.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
+                                                                float* target) {
+  constexpr int KS = D / 32;
+  constexpr int QSTR = D + 8;                 // staged row stride (halves)
+  constexpr int NP = 4;                       // (tile, head) pairs per stage
+  constexpr int RP = D / 8;                   // 16-byte pieces per row
+  constexpr int PPT = NP * 16 * RP / kThreads;
+  static_assert(PPT * kThreads == NP * 16 * RP, "stage pieces divide the block");
+  __shared__ __align__(16) uint16_t qs[2][NP][16][QSTR];
+  __shared__ float ls[2][NP][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, lj = lane & 15;
+  const int S = pa.S, w = pa.window;
+  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int t0b = 128 * blockIdx.x;            // the workgroup's first key
+  const int t0 = t0b + 32 * wave;              // this wave's first key
+  const uint16_t* kseg = pa.k + (size_t)seg * S * D;
+  const float sl2 = pa.scale * kLog2e;
+
+  half8 ka[2][KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int t = t0 + 16 * kb + lj;
+    const uint16_t* kr = kseg + (size_t)min(t, S - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = *reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk));
+      ka[kb][kk] = t < S ? as_h8(u) : half8{};
+    }
+  }
+  float acc[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[kb][r] = 0.0f;
+
+  // (query tile, head) pairs from the first tile holding a counted query
+  const int x0 = (min(t0b + w, S) >> 4) * G, x1 = ((S + 15) >> 4) * G;
+  const int nst = (x1 - x0 + NP - 1) / NP;
+  uint4 pre[PPT];
+  float plse = 0.0f;
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
+      const int x = x0 + NP * st + pr;
+      if (x < x1) {
+        const int tile = x / G, g = x - tile * G;
+        const int d = min(16 * tile + row, S - 1);
+        pre[u] = *reinterpret_cast<const uint4*>(pa.q + (((size_t)b * pa.Hq + h * G + g) * S + d) * D + 8 * piece);
+      } else {
+        pre[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (tid < NP * 16) {
+      const int pr = tid >> 4, row = tid & 15;
+      const int x = x0 + NP * st + pr;
+      if (x < x1) {
+        const int tile = x / G, g = x - tile * G;
+        plse = lse_in[((size_t)b * pa.Hq + h * G + g) * S + min(16 * tile + row, S - 1)];
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + kThreads * u;
+      const int pr = e / (16 * RP), rem = e - pr * 16 * RP, row = rem / RP, piece = rem - row * RP;
+      *reinterpret_cast<uint4*>(&qs[buf][pr][row][8 * piece]) = pre[u];
+    }
+    if (tid < NP * 16) ls[buf][tid >> 4][tid & 15] = plse;
+  };
+  if (nst > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      const int x = x0 + NP * st + pr;
+      if (x >= x1) break;
+      const int d0 = 16 * (x / G), d = d0 + lj;
+      half8 qb[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) qb[kk] = as_h8(*reinterpret_cast<const uint4*>(&qs[buf][pr][lj][8 * (lq + 4 * kk)]));
+      // exp(s*scale - lse) = 2^(c*scale*log2(e) - lse*log2(e)): one FMA and one exp2
+      const float nl2 = -ls[buf][pr][lj] * kLog2e;
+      // every query of this tile counts for every key of this wave
+      const bool full = d0 >= t0 + 31 + w && d0 + 15 < S;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], qb[kk], c);
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[kb][r] += __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * kb + 4 * lq + r;
+            const bool counted = d < S && d >= t + w;
+            acc[kb][r] += counted ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2)) : 0.0f;
+          }
+        }
+      }
+    }
+    if (st + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = acc[kb][r];
+      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o, 64);
+      const int t = t0 + 16 * kb + 4 * lq + r;
+      if (lj == 0 && t < S) target[(size_t)seg * S + t] = a > 0.0f ? logf(a) : -INFINITY;
+    }
+  }
+}
+
+template <int D>
+static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipStream_t s) {
+  const int qb = pa.G <= 4 ? 32 : 16;  // queries per workgroup (see the kernel)
+  const dim3 grid((pa.S + qb - 1) / qb, pa.B * pa.Hkv);
+  switch (pa.G) {
+    case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 4: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 4>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 5: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 5>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    case 8: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 8>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+    default: return -1;
+  }
+  return ok_or_err();
+}
+
+int kvpop_prefill_attend_lds(int D, int list_cap) {
+  return (32 * (D + 8) + D * 40) * 2 + ((list_cap + 31) & ~31) * 8;
+}
+
+int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int segs = pa.B * pa.Hkv;
+  hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), 0, s, pa);
+  if (hipGetLastError() != hipSuccess) return -3;
+  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4 + 1024 * 4, s, pa);
+  if (hipGetLastError() != hipSuccess) return -3;
+  const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
+  if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
+  if (pa.D == 128) return launch_kvpop_attend_d<128>(pa, lds, s);
+  return -1;
+}
+
+template <int D>
+static int launch_target_d(const KvpopPrefillArgs& pa, const float* lse, float* target, hipStream_t s) {
+  const dim3 grid((pa.S + 127) / 128, pa.B * pa.Hkv);
+  switch (pa.G) {
+    case 1: hipLaunchKernelGGL((kvpop_target_kernel<D, 1>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 2: hipLaunchKernelGGL((kvpop_target_kernel<D, 2>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 4: hipLaunchKernelGGL((kvpop_target_kernel<D, 4>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 5: hipLaunchKernelGGL((kvpop_target_kernel<D, 5>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    case 8: hipLaunchKernelGGL((kvpop_target_kernel<D, 8>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
+    default: return -1;
+  }
+  return ok_or_err();
+}
+
+int launch_kvpop_target(const KvpopPrefillArgs& pa, const float* lse, float* target, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (pa.D == 64) return launch_target_d<64>(pa, lse, target, s);
+  if (pa.D == 128) return launch_target_d<128>(pa, lse, target, s);
+  return -1;
+}
+
+}  // namespace confkv
