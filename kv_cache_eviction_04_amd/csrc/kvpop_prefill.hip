@@ -62,43 +62,110 @@ __global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
 // n >= k a rank above thr is never the threshold again (thr only moves
 // down, and the search for the next rank runs below it), so it is not
 // entered in the bitmap.
+// One wave per segment walks the queries in batches of 64: lane i loads the
+// rank that joins at query q0 + i (four batches at a time, loaded a group
+// ahead), and lane i keeps the threshold of query q0 + i until the batch is
+// stored. A batch that leaves n below k only enters its ranks; the batch in
+// which n reaches k is stepped through query by query (readlane). After
+// that only the ranks below the batch's starting thr can move it, so a
+// ballot picks them and they are taken in query order. The bitmap word that
+// holds thr is also kept in a register, so a move of thr within that word
+// needs no LDS access; inserts are LDS atomic ORs whose result is not
+// waited for.
+__device__ __forceinline__ int wave_max_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
 __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
-  extern __shared__ uint32_t kbits[];  // ceil(N/32) words, then 1024 staged ranks
-  const int tid = threadIdx.x, seg = blockIdx.x;
+  extern __shared__ uint32_t kbits[];  // ceil(N/32) words
+  const int lane = threadIdx.x, seg = blockIdx.x;
   const int S = pa.S, s = pa.sinks, w = pa.window, k = pa.topk, nw = (pa.N + 31) >> 5;
-  int32_t* stage = reinterpret_cast<int32_t*>(kbits + nw);
   const int32_t* rank = pa.rank + (size_t)seg * S;
   int32_t* thr = pa.thr + (size_t)seg * S;
-  for (int i = tid; i < nw; i += 64) kbits[i] = 0u;
+  for (int i = lane; i < nw; i += 64) kbits[i] = 0u;
+  __syncthreads();
   int n = 0, t = k > 0 ? S : -1, maxr = -1;
-  for (int q0 = 0; q0 < S; q0 += 1024) {
-    __syncthreads();
-    for (int i = tid; i < 1024; i += 64) {
-      const int p = q0 + i - 1 - w;
-      stage[i] = (q0 + i < S && p >= s) ? rank[p] : -2;
+  int wt = 0;        // the bitmap word holding thr once n >= k,
+  uint32_t ct = 0u;  // and a copy of it kept up to date
+  // insert rank r below thr and move thr to the next candidate rank below it
+  auto move = [&](int r) {
+    const uint32_t bit = 1u << (r & 31);
+    if (lane == 0) atomicOr(&kbits[r >> 5], bit);  // LDS operations of a wave complete in order
+    if ((r >> 5) == wt) ct |= bit;
+    int wi = wt;
+    uint32_t word = ct & ((1u << (t & 31)) - 1u);
+    if (word == 0u) {
+      do word = kbits[--wi];
+      while (word == 0u);
+      wt = wi;
+      ct = word;
     }
-    __syncthreads();
-    if (tid == 0) {
-      const int cnt = min(1024, S - q0);
-      for (int i = 0; i < cnt; ++i) {
-        const int r = stage[i];
-        if (r >= 0 && k > 0) {
-          ++n;
-          if (n <= k) {
-            kbits[r >> 5] |= 1u << (r & 31);
-            maxr = max(maxr, r);
-            if (n == k) t = maxr;
-          } else if (r < t) {
-            kbits[r >> 5] |= 1u << (r & 31);
-            int wi = t >> 5;
-            uint32_t word = kbits[wi] & ((1u << (t & 31)) - 1u);
-            while (word == 0u) word = kbits[--wi];
-            t = (wi << 5) + 31 - __clz((int)word);
+    t = (wi << 5) + 31 - __clz((int)word);
+  };
+  auto rank_at = [&](int q0) {
+    const int q = q0 + lane, p = q - 1 - w;
+    return (q < S && p >= s) ? rank[p] : -2;
+  };
+  constexpr int NB = 4;  // batches whose ranks are loaded together
+  int rv[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) rv[j] = rank_at(64 * j);
+  for (int g0 = 0; g0 < S; g0 += 64 * NB) {
+    int rn[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) rn[j] = g0 + 64 * (NB + j) < S ? rank_at(g0 + 64 * (NB + j)) : -2;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int q0 = g0 + 64 * j, q = q0 + lane;
+      if (q0 >= S) break;
+      const int r_l = rv[j];
+      int tv = t;
+      const uint64_t valid = __ballot(r_l >= 0);
+      const int nv = __popcll(valid);
+      if (k > 0 && n >= k) {
+        // thr only moves down, so only ranks below the batch's starting thr
+        // can move it; the others change nothing
+        n += nv;
+        uint64_t cand = __ballot(r_l >= 0 && r_l < t);
+        while (cand) {
+          const int i = __builtin_ctzll(cand);
+          cand &= cand - 1;
+          const int r = __builtin_amdgcn_readlane(r_l, i);
+          if (r < t) {
+            move(r);
+            tv = lane >= i ? t : tv;
           }
         }
-        thr[q0 + i] = t;
+      } else if (k > 0 && n + nv < k) {
+        // every rank of the batch is entered and thr stays S
+        if (r_l >= 0) atomicOr(&kbits[r_l >> 5], 1u << (r_l & 31));
+        maxr = max(maxr, wave_max_i32(r_l));
+        n += nv;
+      } else {
+        const int cnt = min(64, S - q0);
+        for (int i = 0; i < cnt; ++i) {
+          const int r = __builtin_amdgcn_readlane(r_l, i);
+          if (r >= 0 && k > 0) {
+            ++n;
+            if (n <= k) {
+              if (lane == 0) atomicOr(&kbits[r >> 5], 1u << (r & 31));
+              maxr = max(maxr, r);
+              if (n == k) {
+                t = maxr;
+                wt = t >> 5;
+                ct = kbits[wt];
+              }
+            } else if (r < t) {
+              move(r);
+            }
+          }
+          tv = lane == i ? t : tv;
+        }
       }
+      if (q < S) thr[q] = tv;
     }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) rv[j] = rn[j];
   }
 }
 
@@ -497,7 +564,7 @@ int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
   const int segs = pa.B * pa.Hkv;
   hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), 0, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4 + 1024 * 4, s, pa);
+  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
   const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
   if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);

@@ -13,6 +13,8 @@ logarithm against the dense float64 oracle, with the prefill's own LSEs as
 normalisers, and on sampled keys at 16K positions.
 """
 
+import bisect
+
 import numpy as np
 import pytest
 import torch
@@ -83,6 +85,42 @@ def test_kvpop_prefill_matches_oracle(Hq, Hkv, d, S, s, w, k, ties):
     log(f"kvpop prefill G{G} d{d} S{S} s{s} w{w} k{k}: worst out err {worst:.2e}")
 
 
+def kth_smallest_prefix(rank, S, s, w, k):
+    """thr(q) by its definition: the k-th smallest rank over positions
+    [s, q-1-w], S while fewer than k, -1 for k = 0 (a sorted prefix)."""
+    out = np.empty(S, dtype=np.int64)
+    pref = []
+    for q in range(S):
+        p = q - 1 - w
+        if p >= s:
+            bisect.insort(pref, int(rank[p]))
+        out[q] = -1 if k == 0 else (pref[k - 1] if len(pref) >= k else S)
+    return out
+
+
+@pytest.mark.parametrize("S,s,w,k,ties", [
+    (64, 0, 0, 1, False), (65, 1, 3, 61, True), (257, 2, 5, 63, False), (300, 0, 40, 200, True),
+    (513, 3, 0, 129, False), (256, 0, 0, 256, False), (700, 0, 2, 5, True),
+])
+def test_kvpop_thresholds_at_batch_edges(S, s, w, k, ties):
+    # the threshold pass walks queries in batches of 64 (groups of 256): the
+    # fill-up ends (n reaches k) at different offsets inside a batch, and S
+    # ends partial batches and groups
+    B, Hq, Hkv, d = 1, 2, 2, 64
+    w_ = kvpop_cfg(Hq, Hkv, d, s, w, k, B)
+    gpu = confkv.Cache(w_)
+    q, kk, v, p = inputs(B, Hq, Hkv, S, d, seed=3 * S + k, ties=ties)
+    _, _, ws = gpu.kvpop_prefill(q, kk, v, p)
+    ranks, thr = gpu.kvpop_prefill_ranks(ws, S)
+    assert gpu.status() == confkv.OK
+    for h in range(Hkv):
+        r_or = KPP.descending_ranks(p[0, h].cpu().numpy(), s)
+        assert np.array_equal(ranks[h].cpu().numpy(), r_or), f"ranks h{h}"
+        t_or = KPP.running_thresholds(r_or, S, s, w, k)
+        assert np.array_equal(thr[h].cpu().numpy(), t_or), f"thresholds h{h}"
+        assert np.array_equal(t_or, kth_smallest_prefix(r_or, S, s, w, k))
+
+
 def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
     # the Qwen3-8B shape at the pages' 16384-token training length, budget
     # s + w + k = 4 + 256 + 1788; rows checked one by one against top-k per row
@@ -99,7 +137,7 @@ def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
     scale = 1.0 / np.sqrt(d)
     rows = [0, 3, 4, 259, 260, 261, 2047, 2048, 2049, 5000, 9999, S - 17, S - 1]
     worst = 0.0
-    for h in (0, 5):
+    for h in range(Hkv):
         pn = p[0, h].cpu().numpy()
         kn = kk[0, h].cpu().numpy().astype(np.float64)
         vn = v[0, h].cpu().numpy().astype(np.float64)
@@ -108,6 +146,7 @@ def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
         r_or[s + order] = np.arange(S - s)
         assert np.array_equal(ranks[h].cpu().numpy(), r_or), f"ranks h{h}"
         thr_h = thr[h].cpu().numpy()
+        assert np.array_equal(thr_h, kth_smallest_prefix(r_or, S, s, w, k)), f"all thresholds h{h}"
         for qr in rows:
             cand = np.arange(s, max(s, qr - w))
             top = cand[np.argsort(r_or[cand], kind="stable")[:k]]
