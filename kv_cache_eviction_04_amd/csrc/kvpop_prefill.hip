@@ -169,6 +169,22 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
   }
 }
 
+// Work item of a workgroup of a (tiles x segments) grid, XCD-aware. The
+// dispatcher deals workgroups out round-robin over the 8 XCDs, each with its
+// own L2, so XCD x = lin % 8 is given the contiguous run of work items that
+// starts at x * (n / 8) + min(x, n % 8), in order; work items run tile-fastest
+// within a segment. Neighbouring tiles of a segment share most of their keys
+// (prefill) or their later query rows (target), and so meet in one L2. The
+// map is a bijection on [0, n) whatever the dispatch order.
+__device__ __forceinline__ void xcd_tile_seg(int& tile, int& seg) {
+  const int n = gridDim.x * gridDim.y;
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+  const int x = lin & 7;
+  const int work = x * (n >> 3) + min(x, n & 7) + (lin >> 3);
+  seg = work / gridDim.x;
+  tile = work - seg * gridDim.x;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 
@@ -202,8 +218,10 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, s = pa.sinks, w = pa.window;
-  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int q0 = QB * blockIdx.x, q1 = min(q0 + QB, S);
+  int tile, seg;
+  xcd_tile_seg(tile, seg);
+  const int b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int q0 = QB * tile, q1 = min(q0 + QB, S);
   const int32_t* rank = pa.rank + (size_t)seg * S;
   const int32_t* thr = pa.thr + (size_t)seg * S;
   const uint16_t* kseg = pa.k + (size_t)seg * S * D;
@@ -427,8 +445,10 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, w = pa.window;
-  const int seg = blockIdx.y, b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int t0b = 128 * blockIdx.x;            // the workgroup's first key
+  int tile, seg;
+  xcd_tile_seg(tile, seg);
+  const int b = seg / pa.Hkv, h = seg - b * pa.Hkv;
+  const int t0b = 128 * tile;                  // the workgroup's first key
   const int t0 = t0b + 32 * wave;              // this wave's first key
   const uint16_t* kseg = pa.k + (size_t)seg * S * D;
   const float sl2 = pa.scale * kLog2e;
