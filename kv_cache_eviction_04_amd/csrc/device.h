@@ -117,6 +117,18 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
   }
   return v;
 }
+// The wave's smallest key and the index held with it (keys are unique, so the
+// index is that of the one lane holding the minimum).
+__device__ __forceinline__ void wave_argmin_u64(uint64_t& k, int32_t& i) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(k, o, 64);
+    const int32_t j = __shfl_xor(i, o, 64);
+    if (w < k) {
+      k = w;
+      i = j;
+    }
+  }
+}
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
   v = wave_sum_u32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -253,9 +265,15 @@ __device__ __forceinline__ void pipelined(int t0, int t1, LoadF&& load, CompF&& 
 #if !CONFKV_PIPE
   for (int base = t0; base < t1; base += NPB) {
     Buf A[NPB];
+    // Every slot of the batch is loaded, those past the range with the range's
+    // last tile (same lines, in flight already: no extra HBM traffic). With no
+    // branch between the loads, each tile's compute waits for that tile's
+    // loads only, not for the whole batch.
 #pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      if (base + u < t1) load(base + u, A[u]);
+    for (int u = 0; u < NPB; ++u) {
+      load(min(base + u, t1 - 1), A[u]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads in tile order
+    }
 #pragma unroll
     for (int u = 0; u < NPB; ++u)
       if (base + u < t1) comp(base + u, A[u]);

@@ -240,6 +240,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   __shared__ uint32_t hist[256];
   __shared__ int32_t sh[8];
   __shared__ int32_t sh_out_live, sh_base;
+  __shared__ uint32_t sel_cnt[4][2];  // per wave: live rows, eligible rows
+  __shared__ uint64_t sel_key[4];     // per wave: smallest key
+  __shared__ int32_t sel_row[4];      // per wave: its stage row
   extern __shared__ float dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -451,7 +454,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
               }
               const int row = 16 * tt + lj;
               const bool valid = row < n_old;
-              if (valid) sv_max = fmaxf(sv_max, bf.sv);
+              sv_max = fmaxf(sv_max, valid ? bf.sv : 0.0f);
               const float f = bf.sk * sm;
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -709,6 +712,8 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   // planes 0/1 of the row just read (same thread). An attend launch stops at
   // the EMA; an evict launch takes the EMA the attend launches stored.
   uint32_t n_live = 0, n_elig = 0;
+  uint64_t kmin = ~0ull;  // this thread's smallest key and its stage row
+  int32_t imin = -1;
   const float inv_t1 = 1.0f / (float)(t + 1);  // recency (pos+1)/(t+1) as a product, within an ulp
   // random ranker: this step's and segment's generator state; a row's rank
   // is the top 24 bits of out(k2, pos + 1) times 2^-24
@@ -758,6 +763,10 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
             } else if (elig) {
               key = rank_key(score, pos);
               ++n_elig;
+              if (key < kmin) {
+                kmin = key;
+                imin = i;
+              }
             }
             if (pos == pos_out && i >= n_old32) sh_out_live = 1;
           }
@@ -788,8 +797,31 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       }
     }
   }
-  n_live = block_sum_u32(n_live, red_u);
-  n_elig = block_sum_u32(n_elig, red_u);
+  // One block reduction gives the live and eligible counts and the smallest
+  // key with its row. With one victim (the steady state) that is the whole
+  // selection; more victims continue from it.
+  {
+    n_live = wave_sum_u32(n_live);
+    n_elig = wave_sum_u32(n_elig);
+    wave_argmin_u64(kmin, imin);
+    if (lane == 0) {
+      sel_cnt[wave][0] = n_live;
+      sel_cnt[wave][1] = n_elig;
+      sel_key[wave] = kmin;
+      sel_row[wave] = imin;
+    }
+    __syncthreads();
+    n_live = sel_cnt[0][0] + sel_cnt[1][0] + sel_cnt[2][0] + sel_cnt[3][0];
+    n_elig = sel_cnt[0][1] + sel_cnt[1][1] + sel_cnt[2][1] + sel_cnt[3][1];
+    kmin = sel_key[0];
+    imin = sel_row[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (sel_key[w] < kmin) {
+        kmin = sel_key[w];
+        imin = sel_row[w];
+      }
+  }
 
   // ---- budget and selection of the e lowest keys among the eligible rows.
   int budget;
@@ -803,9 +835,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   }
   uint32_t e = 0;
   if ((int)n_live > budget) e = min((uint32_t)((int)n_live - budget), n_elig);
-  uint64_t T = 0;  // victims: key <= T (no key is 0)
-  if (e > 0 && e <= 8) {
-    for (uint32_t r = 0; r < e; ++r) {
+  uint64_t T = e > 0 ? kmin : 0;  // victims: key <= T (no key is 0); the first is the smallest key
+  if (e > 1 && e <= 8) {
+    for (uint32_t r = 1; r < e; ++r) {
       uint64_t mk = ~0ull;
       for (int i = tid; i < rows; i += kThreads) {
         const uint64_t k = st.key(i);
@@ -825,7 +857,12 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   const bool age = pos_out >= 0 && sh_out_live && st.key(n_old32 + slot_out) > T;
   uint32_t ev_old = 0;
   int vmin = n_old, vmax = -1;
-  if (e > 0) {
+  if (e == 1) {
+    if (imin < n_old) {  // the one victim is an old row
+      ev_old = 1;
+      vmin = vmax = imin;
+    }
+  } else if (e > 1) {
     for (int i = tid; i < n_old; i += kThreads)
       if (st.key(i) <= T) {
         ++ev_old;
@@ -927,9 +964,12 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       }
     }
   }
-  if (e > 0)
+  if (e == 1) {
+    if (tid == 0 && imin >= n_old32) rpos[imin - n_old32] = -1;
+  } else if (e > 1) {
     for (int r = tid; r < Wr; r += kThreads)
       if (st.key(n_old32 + r) <= T) rpos[r] = -1;
+  }
 
   // ---- age-out: the row at t - W leaves the FP16 window; if it survived it
   // is stored in the old region (quantized when old rows are INT8), in the
