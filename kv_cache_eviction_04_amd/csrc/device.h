@@ -98,36 +98,85 @@ __device__ __forceinline__ uint64_t splitmix64_out(uint64_t k, uint64_t n) {
 
 // ------------------------------------------------------------ block helpers
 // 256 threads = 4 wavefronts of 64.
+//
+// Wave reductions run inside each row of 16 lanes by DPP moves (quad
+// permutes for lane distances 1 and 2, then the half-row and row mirrors),
+// with no LDS round trip, and then combine the four rows' results read from
+// lanes 0, 16, 32 and 48. After the quad steps every lane of a quad holds the
+// same value, so pairing by mirror gives the same operands as pairing by XOR.
+// They must be called with every lane of the wave active; the result is the
+// same in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+  v = op(v, dpp_f32<kDppXor1>(v));
+  v = op(v, dpp_f32<kDppXor2>(v));
+  v = op(v, dpp_f32<kDppHalfMirror>(v));
+  return op(v, dpp_f32<kDppMirror>(v));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = row16_reduce(v, [](float x, float y) { return x + y; });
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_u32<kDppXor1>(v);
+  v += dpp_u32<kDppXor2>(v);
+  v += dpp_u32<kDppHalfMirror>(v);
+  v += dpp_u32<kDppMirror>(v);
+  return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) + __builtin_amdgcn_readlane((int)v, 16) +
+                    __builtin_amdgcn_readlane((int)v, 32) + __builtin_amdgcn_readlane((int)v, 48));
 }
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o, 64);
-    v = w < v ? w : v;
+// The wave's smallest 64-bit key and the index held with it (the index of
+// the lane holding the minimum when keys are unique).
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(uint64_t& k, int32_t& i) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)k), hi = dpp_u32<CTRL>((uint32_t)(k >> 32));
+  const int32_t j = (int32_t)dpp_u32<CTRL>((uint32_t)i);
+  const uint64_t w = ((uint64_t)hi << 32) | lo;
+  if (w < k) {
+    k = w;
+    i = j;
   }
-  return v;
 }
-// The wave's smallest key and the index held with it (keys are unique, so the
-// index is that of the one lane holding the minimum).
 __device__ __forceinline__ void wave_argmin_u64(uint64_t& k, int32_t& i) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(k, o, 64);
-    const int32_t j = __shfl_xor(i, o, 64);
-    if (w < k) {
-      k = w;
-      i = j;
+  argmin_step<kDppXor1>(k, i);
+  argmin_step<kDppXor2>(k, i);
+  argmin_step<kDppHalfMirror>(k, i);
+  argmin_step<kDppMirror>(k, i);
+  uint64_t best = ~0ull;
+  int32_t bi = -1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t w = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * r);
+    const int32_t j = __builtin_amdgcn_readlane(i, 16 * r);
+    if (r == 0 || w < best) {
+      best = w;
+      bi = j;
     }
   }
+  k = best;
+  i = bi;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  int32_t unused = 0;
+  wave_argmin_u64(v, unused);
+  return v;
 }
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
   v = wave_sum_u32(v);

@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float m = mrun[r];
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = row16_reduce(m, [](float x, float y) { return fmaxf(x, y); });
     const int g = 4 * lq + r;
     if (lj == 0 && g < G) red_m[wave][g] = m;
   }
