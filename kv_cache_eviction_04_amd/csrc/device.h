@@ -281,7 +281,10 @@ typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 #define CONFKV_PV16_NPB 4  // FP16 V tiles per batch
 #endif
 #ifndef CONFKV_KB
-#define CONFKV_KB 6        // key-phase rows per thread loaded ahead
+#define CONFKV_KB 10       // key-phase rows per thread loaded ahead, groups of up to 4
+#endif                     // query heads (2560 staged rows in one round)
+#ifndef CONFKV_KB_WIDE
+#define CONFKV_KB_WIDE 6   // the same for larger groups, which have fewer registers left
 #endif
 #ifndef CONFKV_OCC
 #define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 5; a few

@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   constexpr int NP16 = 2;              // 16-row FP16 K tiles in flight per wave
   constexpr int NV8 = 8;               // 32-row INT8 V tiles in flight per wave
   constexpr int NV16 = 4;              // 32-row FP16 V tiles in flight per wave
-  constexpr int KB = CONFKV_KB;        // rows per thread in flight in the key phase
+  constexpr int KB = G <= 4 ? CONFKV_KB : CONFKV_KB_WIDE;  // rows per thread in flight in the key phase
   static_assert(LPR == 4 || LPR == 8, "head_dim 64 or 128");
   static_assert(G <= 16, "a GQA group fits one MFMA tile");
 
@@ -302,11 +302,14 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   // Row state of stage row i sits at one index of the unified row arrays
   // (old row i, or ring slot i - n_old32 at cap32 + slot), so every row issues
   // the same three loads with no branch between them; padding rows read valid
-  // padding entries and are masked after.
+  // padding entries and are masked after. Slots in which no row of the wave
+  // is below the stage-row count are not loaded (nothing reads them).
   const float* uev = kvpop ? oprio : oema;
   auto load_rows = [&](int i0) {
+    const int wrow0 = i0 - tid + 64 * wave;  // the wave's first row of slot 0
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
+      if (wrow0 + kThreads * u >= rows) break;  // no row of the wave in this slot or later ones
       const int i = i0 + kThreads * u;
       const int r = i - n_old32;
       const int ix = r < 0 ? i : lay.cap32 + min(r, Wr32 - 1);
