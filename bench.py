@@ -224,7 +224,9 @@ def main():
     inputs = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(args.steps)]
     torch.cuda.synchronize()
     gpu.stats(reset=True)
-    gpu.profile(True)
+    # Event pairs around the fused kernel only: each record costs stream time,
+    # so the reducer is timed in a pass of its own after the timed region.
+    gpu.profile(True, kernels=("step",))
     gpu.profile_read(reset=True)
 
     torch.cuda.synchronize()
@@ -247,7 +249,18 @@ def main():
     kv_per_step, alg_per_launch = algorithmic_bytes(w, st, args.steps, S)
     kv_gbps = kv_per_step / (ms_per_step * 1e-3) / 1e9
     fused_avg_ms = prof["fused_ms"] / max(prof["fused_launches"], 1)
-    reduce_avg_ms = prof["reduce_ms"] / prof["reduce_launches"] if prof["reduce_launches"] else None
+    reduce_avg_ms = None
+    if w["policy"] != "kvpop":  # the reducer's duration, over a few more steps
+        red_inputs = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(20)]
+        torch.cuda.synchronize()
+        gpu.profile(True, kernels=("reduce",))
+        for x in red_inputs:
+            run_step(x)
+        gpu.profile(False)
+        red = gpu.profile_read(reset=True)
+        step_i += len(red_inputs)
+        gpu.stats(reset=True)
+        reduce_avg_ms = red["reduce_ms"] / max(red["reduce_launches"], 1)
     achieved = alg_per_launch / (fused_avg_ms * 1e-3) / 1e9
     log(f"{steps_per_s:.1f} steps/s ({ms_per_step:.4f} ms/step), KV {kv_gbps:.0f} GB/s; fused kernel "
         f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic"

@@ -297,14 +297,22 @@ int confkv_read_last_step(confkv_handle* h, void* stream, int32_t seg_first, int
 int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, int32_t reset);
 
 /* Profiling of the step's kernels with HIP events on the step's stream.
- * confkv_profile(h, 1) starts recording an event pair around each launch of
- * the fused attend+evict kernel of confkv_step, of the logits reducer (of
- * confkv_step and confkv_evict), and of the kernels of confkv_attend and
- * confkv_evict; confkv_profile_read synchronizes and writes HOST values: total
- * milliseconds and launch counts of the fused kernel and of the reducer, then
- * (if reset) clears them. confkv_profile_kernel does the same for one kernel:
- * 0 fused step, 1 logits reducer, 2 attend, 3 evict (EINVAL otherwise). */
-int confkv_profile(confkv_handle* h, int32_t enable);
+ * confkv_profile(h, mask) records an event pair around each launch of the
+ * kernels in mask (0 stops recording; EINVAL outside 0 .. CONFKV_PROFILE_ALL):
+ * the fused attend+evict kernel of confkv_step, the logits reducer (of
+ * confkv_step and confkv_evict), the kernels of confkv_attend and the kernel
+ * of confkv_evict. Each event record costs a few microseconds of stream time,
+ * so a throughput measurement times only the kernels it needs.
+ * confkv_profile_read synchronizes and writes HOST values: total milliseconds
+ * and launch counts of the fused kernel and of the reducer, then (if reset)
+ * clears them. confkv_profile_kernel does the same for one kernel: 0 fused
+ * step, 1 logits reducer, 2 attend, 3 evict (EINVAL otherwise). */
+#define CONFKV_PROFILE_STEP 1
+#define CONFKV_PROFILE_REDUCE 2
+#define CONFKV_PROFILE_ATTEND 4
+#define CONFKV_PROFILE_EVICT 8
+#define CONFKV_PROFILE_ALL 15
+int confkv_profile(confkv_handle* h, int32_t mask);
 int confkv_profile_read(confkv_handle* h, double* fused_ms, int64_t* fused_launches, double* reduce_ms,
                         int64_t* reduce_launches, int32_t reset);
 int confkv_profile_kernel(confkv_handle* h, int32_t kernel, double* ms, int64_t* launches, int32_t reset);

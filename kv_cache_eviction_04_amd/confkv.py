@@ -326,8 +326,15 @@ class Cache:
         _check(lib().confkv_stats(self.h, self._stream(), arr, int(reset)), "confkv_stats")
         return dict(kv_bytes=int(arr[0]), rows_attended=int(arr[1]), rows_moved=int(arr[2]), rows_evicted=int(arr[3]))
 
-    def profile(self, enable=True):
-        _check(lib().confkv_profile(self.h, int(enable)), "confkv_profile")
+    def profile(self, enable=True, kernels=None):
+        """Record event pairs around launches of the named kernels (default: all four of KERNELS),
+        or stop recording (enable False)."""
+        mask = 0
+        if enable:
+            names = self.KERNELS if kernels is None else kernels
+            for k in names:
+                mask |= 1 << self.KERNELS.index(k)
+        _check(lib().confkv_profile(self.h, mask), "confkv_profile")
 
     def profile_read(self, reset=True):
         fm, rm = c_double(), c_double()

@@ -30,6 +30,7 @@ constexpr int kSplitTarget = 1024;   // workgroups an automatic split-K attend a
 constexpr int kSplitMinTiles = 4;    // 32-row tiles per split at least, when splitting for occupancy
 
 struct EventPool {
+  int bit = 0;                 // this kernel's bit in the profiling mask
   std::vector<hipEvent_t> ev;  // pairs: start, stop
   size_t used = 0;             // pairs recorded since the last read
   double ms = 0.0;
@@ -50,7 +51,7 @@ struct confkv_handle {
   int64_t keep_max;    // no segment keeps more rows than this after an eviction
   int poisoned;
   hipStream_t last_stream;
-  int prof;
+  int prof;  // mask of the kernels whose launches get an event pair
   EventPool pf, pr;    // fused kernel, logits reducer
   EventPool pa, pe;    // attend kernel, evict kernel
   std::vector<uint8_t> attended;  // per layer: attended at position t by confkv_attend
@@ -213,7 +214,7 @@ bool live(const confkv_handle* h) {
 }
 
 int record_event(confkv_handle* h, EventPool& pool, hipStream_t s, bool start) {
-  if (!h->prof) return 0;
+  if (!(h->prof & pool.bit)) return 0;
   const size_t idx = 2 * pool.used + (start ? 0 : 1);
   if (pool.used >= (size_t)kMaxProfilePairs) return 0;
   while (pool.ev.size() <= idx) {
@@ -344,6 +345,10 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   h->poisoned = 0;
   h->last_stream = (hipStream_t)stream;
   h->prof = 0;
+  h->pf.bit = CONFKV_PROFILE_STEP;
+  h->pr.bit = CONFKV_PROFILE_REDUCE;
+  h->pa.bit = CONFKV_PROFILE_ATTEND;
+  h->pe.bit = CONFKV_PROFILE_EVICT;
   h->attended.assign((size_t)cfg->num_layers, 0);
   h->n_attended = 0;
   h->attend_splits = 0;
@@ -671,7 +676,8 @@ CONFKV_API int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, in
 
 CONFKV_API int confkv_profile(confkv_handle* h, int32_t enable) {
   if (!live(h)) return CONFKV_ESTATE;
-  h->prof = enable ? 1 : 0;
+  if (enable < 0 || enable > CONFKV_PROFILE_ALL) return CONFKV_EINVAL;
+  h->prof = enable;
   return CONFKV_OK;
 }
 
