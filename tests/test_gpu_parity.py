@@ -24,7 +24,9 @@ def wl(name, **over):
     return w
 
 
-def run(w, steps, segs=None, seed=0, check_every=1, capacity=None):
+def run(w, steps, segs=None, seed=0, check_every=1, capacity=None, victims=None):
+    """Lockstep over `steps` steps; `victims`, if a list, receives the number
+    of rows each checked segment evicted at each checked step."""
     S = w["num_layers"] * w["batch"] * w["num_kv_heads"]
     ls = Lockstep(w, seed, range(S) if segs is None else segs, capacity=capacity)
     worst = 0.0
@@ -32,6 +34,8 @@ def run(w, steps, segs=None, seed=0, check_every=1, capacity=None):
         r = ls.step(check=(i % check_every == 0 or i == steps - 1))
         if r:
             worst = max(worst, r["worst_out"])
+            if victims is not None:
+                victims.extend(len(sr.victims) for sr in r["orc"].seg.values())
     log(f"{w['name']}: {steps} steps, worst out err {worst:.2e}")
     assert ls.gpu.status() == confkv.OK
     return ls
@@ -122,6 +126,18 @@ def test_ranker_variants_of_the_matched_rate_ablation():
 def test_ragged_tails_and_many_evictions():
     # prefill not a multiple of any tile; budget drops force multi-row evictions
     run(wl("toy", prefill=331, n_low=37, n_high=77, protect_last=5, fp16_window=13), 40, seed=12)
+
+
+def test_every_selection_path_bit_exact():
+    # The kernel settles one victim from the block's smallest key, 2..8 victims
+    # by arg-min rounds after it, and more by radix select. Each step's victims
+    # are checked bit-exactly by the lockstep; this run (chosen with the oracle:
+    # the first step evicts the prefill down to the budget, uncertain runs of
+    # a few steps are followed by budget drops) takes every path.
+    e = []
+    run(wl("toy", prefill=150, n_low=37, n_high=77, protect_last=5, fp16_window=13), 40, seed=12, victims=e)
+    e = np.array(e)
+    assert (e == 1).sum() > 0 and ((e >= 2) & (e <= 8)).sum() > 0 and (e > 8).sum() > 0, np.bincount(e)
 
 
 def test_kvpop_variant_closed_form():
