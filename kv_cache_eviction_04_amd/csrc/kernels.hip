@@ -183,10 +183,12 @@ struct Stage {
 };
 
 // The e-th smallest key (e >= 1) over keys [0, rows): an 8-bit-digit radix
-// select from the most significant digit down.
+// select from the most significant digit down. Keys are unique, so once the
+// selected digit's bin holds a single key, that key is the answer and one
+// minimum pass over the keys under the prefix finds it.
 template <bool kLds>
 __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, uint32_t* hist, uint32_t* red,
-                                 int32_t* sh) {
+                                 int32_t* sh, uint64_t* red64) {
   uint64_t prefix = 0, mask = 0;
   const int tid = threadIdx.x;
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -203,13 +205,23 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
     if (excl < e && e <= excl + cnt) {
       sh[0] = tid;
       sh[1] = (int32_t)excl;
+      sh[2] = (int32_t)cnt;
     }
     __syncthreads();
     const uint32_t bin = (uint32_t)sh[0];
     e -= (uint32_t)sh[1];
     prefix |= (uint64_t)bin << shift;
     mask |= (uint64_t)0xFFu << shift;
+    const bool single = sh[2] == 1;
     __syncthreads();
+    if (single && shift > 0) {
+      uint64_t mk = ~0ull;
+      for (int i = tid; i < rows; i += kThreads) {
+        const uint64_t k = st.key(i);
+        if ((k & mask) == prefix && k < mk) mk = k;
+      }
+      return block_min_u64(mk, red64);
+    }
   }
   return prefix;
 }
@@ -849,7 +861,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       T = block_min_u64(mk, red_k);
     }
   } else if (e > 8) {
-    T = radix_select(st, rows, e, hist, red_u, sh);
+    T = radix_select(st, rows, e, hist, red_u, sh, red_k);
   }
 
   // ---- compaction of the old region. The row leaving the FP16 window (if it
