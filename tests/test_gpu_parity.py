@@ -168,3 +168,34 @@ def test_nonfinite_logits_reported():
     assert gpu.status() == confkv.ENONFINITE
     with pytest.raises(confkv.ConfKVError):
         gpu.step(x["logits"], x["q"], x["k"], x["v"])
+
+
+def test_profile_mask_times_only_the_selected_kernels():
+    # confkv_profile takes a mask of kernels: an event pair is recorded around
+    # each launch of a selected kernel and around nothing else
+    w = wl("toy")
+    gpu = confkv.Cache(w)
+    step_i = 0
+
+    def steps(n):
+        nonlocal step_i
+        for _ in range(n):
+            x = synth.step_inputs(w, 0, step_i, DEV)
+            gpu.step(x["logits"], x["q"], x["k"], x["v"])
+            step_i += 1
+
+    gpu.profile(True, kernels=("step",))
+    steps(3)
+    p = gpu.profile_read(reset=True)
+    assert p["fused_launches"] == 3 and p["reduce_launches"] == 0 and p["fused_ms"] > 0.0
+    gpu.profile(True, kernels=("reduce",))
+    steps(2)
+    p = gpu.profile_read(reset=True)
+    assert p["fused_launches"] == 0 and p["reduce_launches"] == 2
+    gpu.profile(False)
+    steps(1)
+    p = gpu.profile_read(reset=True)
+    assert p["fused_launches"] == 0 and p["reduce_launches"] == 0
+    assert confkv.lib().confkv_profile(gpu.h, 16) == confkv.EINVAL
+    assert confkv.lib().confkv_profile(gpu.h, -1) == confkv.EINVAL
+    assert gpu.status() == confkv.OK
