@@ -295,19 +295,27 @@ class Cache:
         thr = workspace[o_thr:o_thr + segs * S * 4].view(torch.int32).view(segs, S)
         return ranks, thr
 
-    def read_cache(self, seg_first=0, seg_count=None):
+    READ_FIELDS = ("len", "pos", "ema", "prio", "k16", "v16", "k8", "v8", "k_scale", "v_scale", "is_int8")
+
+    def read_cache(self, seg_first=0, seg_count=None, fields=None):
         """Logical contents (ascending position) of a segment range, as torch
-        tensors on the device; rows >= len[i] are zero."""
+        tensors on the device; rows >= len[i] are zero. ``fields`` names the
+        outputs wanted (default: all); ``len`` is always returned and the
+        library is handed NULL for the others."""
         n = self.S - seg_first if seg_count is None else seg_count
         R, d, dev = self.rows_max, self.cfg.head_dim, self.device
-        z = lambda *s, dt: torch.zeros(s, dtype=dt, device=dev)  # noqa: E731
-        o = dict(len=z(n, dt=torch.int32), pos=z(n, R, dt=torch.int32), ema=z(n, R, dt=torch.float32),
-                 prio=z(n, R, dt=torch.float32), k16=z(n, R, d, dt=torch.float16), v16=z(n, R, d, dt=torch.float16),
-                 k8=z(n, R, d, dt=torch.int8), v8=z(n, R, d, dt=torch.int8), k_scale=z(n, R, dt=torch.float32),
-                 v_scale=z(n, R, dt=torch.float32), is_int8=z(n, R, dt=torch.uint8))
-        _check(lib().confkv_read_cache(self.h, self._stream(), seg_first, n, *[_ptr(o[k]) for k in (
-            "len", "pos", "ema", "prio", "k16", "v16", "k8", "v8", "k_scale", "v_scale", "is_int8")]),
-            "confkv_read_cache")
+        want = set(self.READ_FIELDS if fields is None else fields) | {"len"}
+        unknown = want - set(self.READ_FIELDS)
+        if unknown:
+            raise ValueError(f"unknown read_cache fields {sorted(unknown)}")
+        shapes = dict(len=((n,), torch.int32), pos=((n, R), torch.int32), ema=((n, R), torch.float32),
+                      prio=((n, R), torch.float32), k16=((n, R, d), torch.float16), v16=((n, R, d), torch.float16),
+                      k8=((n, R, d), torch.int8), v8=((n, R, d), torch.int8), k_scale=((n, R), torch.float32),
+                      v_scale=((n, R), torch.float32), is_int8=((n, R), torch.uint8))
+        o = {k: torch.zeros(shapes[k][0], dtype=shapes[k][1], device=dev) for k in self.READ_FIELDS if k in want}
+        _check(lib().confkv_read_cache(self.h, self._stream(), seg_first, n, *[_ptr(o.get(k)) for k in
+                                                                              self.READ_FIELDS]),
+               "confkv_read_cache")
         return o
 
     def read_last_step(self, seg_first=0, seg_count=None):

@@ -158,7 +158,7 @@ class SegmentRecord:
     lse: np.ndarray            # [G]
     pos: np.ndarray            # positions present during attention (ascending)
     mass: np.ndarray           # per present row (CONF-KV)
-    score32: np.ndarray        # ranking value per present row, float32
+    score32: np.ndarray        # the oracle's own ranking value per present row, float32 (never an override)
     budget: int
     victims: np.ndarray        # evicted positions
 
@@ -203,13 +203,14 @@ def kvpop_segment_step(seg: Segment, t, qg, k_new, v_new, prio_leaving, cfg: Con
     leaving = np.nonzero(seg.pos == t - w)[0]
     if leaving.size and t - w >= cfg.num_sink:
         seg.prio[leaving[0]] = np.float32(prio_leaving)
-    rank_by = seg.prio.copy() if prio_override is None else np.asarray(prio_override, np.float32)
+    own = seg.prio.copy()
+    rank_by = own if prio_override is None else np.asarray(prio_override, np.float32)
     present = seg.pos.copy()
     victims = kvpop.long_range_victims(seg.pos, rank_by, t, cfg.num_sink, w, cfg.kvpop_k)
     seg.remove(victims)
     if cfg.old_int8:
         seg.store_int8_upto(t - cfg.window)
-    return SegmentRecord(o, lse, present, np.zeros(0), rank_by, kvpop.budget(cfg.num_sink, w, cfg.kvpop_k),
+    return SegmentRecord(o, lse, present, np.zeros(0), own, kvpop.budget(cfg.num_sink, w, cfg.kvpop_k),
                          present[victims])
 
 

@@ -8,8 +8,13 @@ state on device-to-host copies of the same inputs, and compare:
   dequantized values); LSE within 1e-5 relative;
 * confidence within 1e-5; base budget exact unless |c - tau| < 1e-5;
 * the rows present during attention: exact;
+* ranking values: the GPU's float32 score of every present row against the
+  oracle's own (float64 EMA and recency, rounded once), within 1e-6; random
+  ranks and KVpop priorities bit-exact;
 * eviction: the oracle's rule applied to the GPU's own float32 ranking values
-  must give exactly the GPU's victims (bit-exact selection);
+  must give exactly the GPU's victims (bit-exact selection); and the oracle's
+  rule on its own ranking values may pick other victims only across a score
+  gap of at most 1e-5 (random ranks and priorities: never);
 * post-step state: positions exact, FP16 rows and INT8 codes/scales
   bit-exact (the aged-out row re-quantized by the oracle), EMA within 1e-6.
 """
@@ -21,11 +26,15 @@ import torch
 
 from kv_cache_eviction_04_amd import confkv, synth
 from oracle import cache as OC
+from oracle import kvpop as KP
+from oracle import policy as OP
 
 TOL_OUT = 2e-3
 TOL_CONF = 1e-5
 TOL_EMA = 1e-6
 TOL_LSE_REL = 1e-5
+TOL_SCORE = 1e-6       # GPU fp32 score vs the oracle's (EMA within 1e-6, halved by alpha, plus fp32 rounding)
+TOL_SCORE_GAP = 1e-5   # a victim may differ from the oracle's own choice only across a gap this small
 
 DEV = torch.device("cuda", 0)
 
@@ -54,6 +63,50 @@ def segment_from_readout(ro, i, d):
     return seg
 
 
+def own_victims(cfg, sr, t):
+    """Positions the oracle evicts when it ranks by its own values (sr.score32)."""
+    if cfg.policy == "kvpop":
+        idx = KP.long_range_victims(sr.pos, sr.score32, t, cfg.num_sink, cfg.protect_last, cfg.kvpop_k)
+    else:
+        idx = OP.select_victims(sr.pos, sr.score32, t, sr.budget, cfg.num_sink, cfg.protect_last)
+    return set(sr.pos[np.asarray(idx, dtype=np.int64)].tolist())
+
+
+def victim_gap(sr, gpu_victims, own):
+    """0 when the GPU evicted exactly the oracle's own victims. Otherwise the
+    largest difference, in the oracle's own ranking values, between a row only
+    the GPU evicted (the oracle ranks it higher) and a row only the oracle
+    evicted; inf if the counts differ."""
+    only_gpu, only_or = set(gpu_victims) - own, own - set(gpu_victims)
+    if not only_gpu and not only_or:
+        return 0.0
+    if len(only_gpu) != len(only_or):
+        return float("inf")
+    sc = dict(zip(sr.pos.tolist(), sr.score32.astype(np.float64).tolist()))
+    return max(sc[p] for p in only_gpu) - min(sc[p] for p in only_or)
+
+
+def gap_tolerance(cfg):
+    """Float scores may tie within rounding; counter-based ranks and static
+    priorities are the same numbers on both sides, so their selection is exact."""
+    return TOL_SCORE_GAP if cfg.policy == "conf" and cfg.ranker == "score" else 0.0
+
+
+def check_ranking_values(cfg, sr, gpu_vals, t, s):
+    """The GPU's recorded ranking value of each present row against the oracle's own."""
+    if cfg.policy == "conf" and cfg.ranker == "score":
+        d = np.abs(gpu_vals.astype(np.float64) - sr.score32.astype(np.float64))
+        assert d.max(initial=0.0) <= TOL_SCORE, f"step {t} seg {s}: score err {d.max()}"
+        return float(d.max(initial=0.0))
+    if cfg.policy == "kvpop":  # rows holding a priority: the long-range candidates
+        m = (sr.pos >= cfg.num_sink) & (sr.pos <= t - cfg.protect_last)
+    else:
+        m = np.ones(sr.pos.size, dtype=bool)
+    assert np.array_equal(gpu_vals[m].view(np.uint32), sr.score32[m].view(np.uint32)), \
+        f"step {t} seg {s}: ranking values differ"
+    return 0.0
+
+
 class Lockstep:
     """split: None drives confkv_step; an int drives confkv_attend per layer
     (with that many workgroups per segment, 0 = automatic) and confkv_evict."""
@@ -71,6 +124,8 @@ class Lockstep:
             self.gpu.set_attend_splits(split)
         self.splits_used = set()
         self.step_i = 0
+        self.worst_score = 0.0     # largest |GPU score - oracle score| seen
+        self.own_flips = []        # (t, seg, gap) where the oracle's own choice differed
         self.d = w["head_dim"]
         self.G = self.gpu.G
 
@@ -153,9 +208,11 @@ class Lockstep:
             assert gpu_victims == set(sr.victims.tolist()), \
                 f"step {t} seg {s}: victims gpu {sorted(gpu_victims)[:10]} oracle {sorted(sr.victims.tolist())[:10]}"
             assert int(meta[3]) == len(sr.victims)
-            if cfg.policy == "conf" and cfg.ranker == "random":  # counter-based ranks: bit-exact
-                assert np.array_equal(overrides[s].view(np.uint32), sr.score32.view(np.uint32)), \
-                    f"step {t} seg {s}: random ranks differ"
+            self.worst_score = max(self.worst_score, check_ranking_values(cfg, sr, overrides[s], t, s))
+            gap = victim_gap(sr, gpu_victims, own_victims(cfg, sr, t))
+            assert gap <= gap_tolerance(cfg), f"step {t} seg {s}: own-score victims differ across a gap of {gap}"
+            if gap > 0.0:
+                self.own_flips.append((t, s, gap))
 
             self.compare_state(s, oc.segs[s], post[s], t)
         return dict(t=t, worst_out=worst, orc=orc, post=post)

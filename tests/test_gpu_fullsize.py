@@ -37,6 +37,7 @@ def drive(ls, total, checked):
             worst = max(worst, r["worst_out"])
             log(f"{ls.w['name']}: step {i} (t {r['t']}) checked, out err {r['worst_out']:.2e}")
     assert ls.gpu.status() == confkv.OK
+    log(f"{ls.w['name']}: worst score err {ls.worst_score:.2e}, own-score victim flips {ls.own_flips}")
     return worst
 
 

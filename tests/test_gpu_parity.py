@@ -36,7 +36,8 @@ def run(w, steps, segs=None, seed=0, check_every=1, capacity=None, victims=None)
             worst = max(worst, r["worst_out"])
             if victims is not None:
                 victims.extend(len(sr.victims) for sr in r["orc"].seg.values())
-    log(f"{w['name']}: {steps} steps, worst out err {worst:.2e}")
+    log(f"{w['name']}: {steps} steps, worst out err {worst:.2e}, worst score err {ls.worst_score:.2e}, "
+        f"own-score victim flips {ls.own_flips}")
     assert ls.gpu.status() == confkv.OK
     return ls
 
@@ -44,34 +45,6 @@ def run(w, steps, segs=None, seed=0, check_every=1, capacity=None, victims=None)
 def test_toy_shape_lockstep():
     # 1 layer, 4 MHA heads, d 64, V 1000: window fill, steady eviction, age-out.
     run(wl("toy"), 200)
-
-
-def test_toy_free_running_retained_sets():
-    # Independent GPU and oracle runs over the whole 512-step toy stream.
-    w = wl("toy")
-    gpu = confkv.Cache(w)
-    cfg = OC.Config.from_dict(w)
-    oc = OC.OracleCache(cfg)
-    oc.init(0)
-    agree = total = 0
-    worst = 0.0
-    for i in range(w["steps"]):
-        x = synth.step_inputs(w, 3, i, DEV)
-        out = gpu.step(x["logits"], x["q"], x["k"], x["v"]).float().cpu().numpy()
-        rec = oc.step(logits=x["logits"].cpu().numpy(), q=x["q"].cpu().numpy(), k_new=x["k"].cpu().numpy(),
-                      v_new=x["v"].cpu().numpy())
-        ro = gpu.read_cache(0, 4)
-        for s in range(4):
-            n = int(ro["len"][s])
-            g = set(ro["pos"][s, :n].tolist())
-            o = set(oc.segs[s].pos.tolist())
-            agree += len(g & o)
-            total += len(g | o)
-            if g == o:
-                worst = max(worst, float(np.abs(out[0, 0, s] - rec.seg[s].out[0]).max()))
-    log(f"toy free-running: retained agreement {agree / total:.6f}, worst out err {worst:.2e}")
-    assert agree / total >= 0.999
-    assert worst <= 2e-3
 
 
 def test_gpt2_shape_pyramid_prefill():
