@@ -253,6 +253,27 @@ int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const 
                          const uint16_t* v, const float* prio, uint16_t* out, float* lse, void* workspace,
                          size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * masked prefill as confkv_kvpop_prefill, same arguments and results, with
+ * no workspace argument. Its sort keys, ranks and thresholds live in a
+ * library-owned device array of CONFKV_NOALLOC_SCRATCH_BYTES (16 MiB), one
+ * copy per GPU, taken when the library's code is loaded on that GPU and held
+ * until the process ends. The call allocates and frees nothing.
+ * - ECAPACITY, with nothing enqueued, when the workspace this S needs
+ *   (confkv_kvpop_prefill_workspace(h, S)) exceeds that size; for instance
+ *   B*Hkv = 64 with S = 16384 needs exactly 16 MiB.
+ * - Every call on one GPU uses that GPU's single array: calls that overlap on
+ *   one GPU (several streams, or several host threads) race and give wrong
+ *   results; calls in one stream's order do not. Each call rewrites every
+ *   byte it reads, so nothing carries over from an earlier call.
+ * - The ranks and thresholds are not handed back (use confkv_kvpop_prefill
+ *   for them). Other errors as confkv_kvpop_prefill. Only enqueues work. */
+#define CONFKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int confkv_kvpop_prefill_noalloc(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const float* prio, uint16_t* out,
+                                 float* lse);
+
 /* The training target of KVpop's scorer ("Resumen Técnico: KVpop" §2.2): for
  * each key position t, the log of the attention mass that the future queries
  * d >= t + w give it, summed over the query heads of its KV head,

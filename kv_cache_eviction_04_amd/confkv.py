@@ -58,6 +58,7 @@ def lib():
         "confkv_set_attend_splits": (c_int, [P, c_int32]),
         "confkv_kvpop_prefill_workspace": (c_size_t, [P, c_int32]),
         "confkv_kvpop_prefill": (c_int, [P, P, c_int32, P, P, P, P, P, P, P, c_size_t]),
+        "confkv_kvpop_prefill_noalloc": (c_int, [P, P, c_int32, P, P, P, P, P, P]),
         "confkv_kvpop_future_target": (c_int, [P, P, c_int32, P, P, P, P]),
         "confkv_attend_splits": (c_int32, [P]),
         "confkv_read_cache": (c_int, [P, P, c_int32, c_int32, P, P, P, P, P, P, P, P, P, P, P]),
@@ -82,7 +83,8 @@ def lib():
 
 EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_init", "confkv_step",
             "confkv_attend", "confkv_evict", "confkv_sample", "confkv_set_attend_splits", "confkv_attend_splits",
-            "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill", "confkv_kvpop_future_target",
+            "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill", "confkv_kvpop_prefill_noalloc",
+            "confkv_kvpop_future_target",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
             "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
 
@@ -265,6 +267,24 @@ class Cache:
                                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel()),
                "confkv_kvpop_prefill")
         return out, lse, workspace
+
+    def kvpop_prefill_noalloc(self, q, k, v, prio, out, lse=None):
+        """The masked prefill of ``kvpop_prefill`` with the library's static
+        per-GPU workspace: the call allocates nothing, so ``out`` (and ``lse``,
+        if wanted) must be passed in. Returns (out, lse)."""
+        c, dev = self.cfg, self.device
+        B, Hq, H, d = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        S = int(q.shape[2]) if q is not None and q.dim() == 4 else 0
+        _expect(q, (B, Hq, S, d), torch.float16, dev, "q")
+        _expect(k, (B, H, S, d), torch.float16, dev, "k")
+        _expect(v, (B, H, S, d), torch.float16, dev, "v")
+        _expect(prio, (B, H, S), torch.float32, dev, "prio")
+        _expect(out, (B, Hq, S, d), torch.float16, dev, "out")
+        if lse is not None:
+            _expect(lse, (B, Hq, S), torch.float32, dev, "lse")
+        _check(lib().confkv_kvpop_prefill_noalloc(self.h, self._stream(), S, _ptr(q), _ptr(k), _ptr(v), _ptr(prio),
+                                                  _ptr(out), _ptr(lse)), "confkv_kvpop_prefill_noalloc")
+        return out, lse
 
     def kvpop_future_target(self, q, k, lse, out=None):
         """Future-attention target [B][Hkv][S] from q [B][Hq][S][d], k [B][Hkv][S][d], lse [B][Hq][S]."""

@@ -20,6 +20,12 @@
 
 using namespace confkv;
 
+// Workspace of confkv_kvpop_prefill_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. Host code never passes its name
+// to a kernel or a copy (on the host it is only a stand-in for the symbol);
+// it uses the device address taken by hipGetSymbolAddress for each device.
+static __device__ __align__(256) uint8_t scratch[CONFKV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr uint32_t kMagic = 0xC0F4B1E5u;
@@ -202,6 +208,31 @@ Params make_params(const confkv_config* c) {
   return p;
 }
 
+// Device address of `scratch` per device id, taken once per device with that
+// device current (at confkv_init, or at the first no-allocation call there).
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return CONFKV_EHIP;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return CONFKV_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CONFKV_OK;
+}
+
 // Handles handed out and not yet destroyed; a destroyed or foreign pointer is
 // never dereferenced.
 std::mutex g_mu;
@@ -331,6 +362,8 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   if (state_bytes < carve(cfg, nullptr, nullptr)) return CONFKV_ECAPACITY;
   if (prefill_len > 0 && (!prefill_k || !prefill_v)) return CONFKV_EINVAL;
   if (prefill_len == 0 && (prefill_k || prefill_v)) return CONFKV_EINVAL;
+  void* scratch_ptr = nullptr;
+  if (scratch_on_current_device(&scratch_ptr) != CONFKV_OK) return CONFKV_EHIP;
   confkv_handle* h = new (std::nothrow) confkv_handle();
   if (!h) return CONFKV_EHIP;
   h->magic = kMagic;
@@ -545,16 +578,23 @@ CONFKV_API size_t confkv_kvpop_prefill_workspace(const confkv_handle* h, int32_t
   return (size_t)prefill_sizes(h, seq_len).total;
 }
 
-CONFKV_API int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
-                                    const uint16_t* k, const uint16_t* v, const float* prio, uint16_t* out,
-                                    float* lse, void* workspace, size_t workspace_bytes) {
+namespace {
+// Checks shared by the two prefill entry points (the workspace aside).
+int prefill_args_ok(const confkv_handle* h, int32_t seq_len, const uint16_t* q, const uint16_t* k,
+                    const uint16_t* v, const float* prio, const uint16_t* out) {
   if (!live(h)) return CONFKV_ESTATE;
   if (h->poisoned) return CONFKV_ESTATE;
   if (h->cfg.policy != CONFKV_POLICY_KVPOP) return CONFKV_EINVAL;
   if (seq_len < 1 || seq_len > kPrefillMaxLen) return CONFKV_EINVAL;
-  if (!q || !k || !v || !prio || !out || !workspace || ((uintptr_t)workspace & 255)) return CONFKV_EINVAL;
+  if (!q || !k || !v || !prio || !out) return CONFKV_EINVAL;
+  return CONFKV_OK;
+}
+
+// Enqueue the rank, threshold and masked attention kernels with the given
+// workspace (sort keys, ranks, thresholds; every byte rewritten per call).
+int kvpop_prefill_enqueue(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const float* prio, uint16_t* out, float* lse, void* workspace) {
   const PrefillSizes z = prefill_sizes(h, seq_len);
-  if (workspace_bytes < (size_t)z.total) return CONFKV_ECAPACITY;
   const int cap = prefill_list_cap(h, seq_len);
   if (kvpop_prefill_attend_lds(h->lay.D, cap) > fused_max_dynamic_lds()) return CONFKV_EINVAL;
   KvpopPrefillArgs pa;
@@ -588,6 +628,28 @@ CONFKV_API int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_
     return CONFKV_EHIP;
   }
   return CONFKV_OK;
+}
+}  // namespace
+
+CONFKV_API int confkv_kvpop_prefill(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* v, const float* prio, uint16_t* out,
+                                    float* lse, void* workspace, size_t workspace_bytes) {
+  const int rc = prefill_args_ok(h, seq_len, q, k, v, prio, out);
+  if (rc != CONFKV_OK) return rc;
+  if (!workspace || ((uintptr_t)workspace & 255)) return CONFKV_EINVAL;
+  if (workspace_bytes < (size_t)prefill_sizes(h, seq_len).total) return CONFKV_ECAPACITY;
+  return kvpop_prefill_enqueue(h, stream, seq_len, q, k, v, prio, out, lse, workspace);
+}
+
+CONFKV_API int confkv_kvpop_prefill_noalloc(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
+                                            const uint16_t* k, const uint16_t* v, const float* prio, uint16_t* out,
+                                            float* lse) {
+  const int rc = prefill_args_ok(h, seq_len, q, k, v, prio, out);
+  if (rc != CONFKV_OK) return rc;
+  if ((size_t)prefill_sizes(h, seq_len).total > (size_t)CONFKV_NOALLOC_SCRATCH_BYTES) return CONFKV_ECAPACITY;
+  void* ws = nullptr;
+  if (scratch_on_current_device(&ws) != CONFKV_OK) return CONFKV_EHIP;
+  return kvpop_prefill_enqueue(h, stream, seq_len, q, k, v, prio, out, lse, ws);
 }
 
 CONFKV_API int confkv_kvpop_future_target(confkv_handle* h, void* stream, int32_t seq_len, const uint16_t* q,
