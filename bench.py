@@ -76,23 +76,72 @@ def stored_traffic(workload):
         return None
 
 
+def _oracle_rows_worker(args):
+    """Confidence and base budget of (row, step) tasks: the oracle as it stands."""
+    from oracle import confidence as OCONF
+    cfg, tasks = args
+    t0 = time.perf_counter()
+    out = {}
+    for key, z in tasks:
+        c = OCONF.confidence(z, cfg.w_entropy, cfg.w_margin, cfg.w_pmax)
+        out[key] = OCONF.gate(c, cfg.tau, cfg.n_low, cfg.n_high, cfg.gate_literal)
+    return out, time.perf_counter() - t0
+
+
+def _oracle_segments_worker(args):
+    """Steps of a group of segments, from their read-back state, with the base
+    budgets of the confidence phase: the oracle's own per-segment step, as
+    OracleCache.step calls it."""
+    from oracle import cache as OC
+    from oracle import confidence as OCONF
+    cfg, t0_pos, states, steps = args
+    L, B, H, G = cfg.num_layers, cfg.batch, cfg.num_kv_heads, cfg.group
+    t0 = time.perf_counter()
+    for i, x in enumerate(steps):
+        t = t0_pos + i
+        for s, seg in states.items():
+            l, b, h = s // (B * H), (s // H) % B, s % H
+            qg, kn, vn = x["q"][l][b][h * G:(h + 1) * G], x["k"][l][b][h], x["v"][l][b][h]
+            if cfg.policy == "conf":
+                bud = OCONF.layer_budget(x["base"][b], l, L, cfg.pyramid)
+                OC.conf_segment_step(seg, t, qg, kn, vn, bud, cfg, segment_id=s)
+            else:
+                OC.kvpop_segment_step(seg, t, qg, kn, vn, float(x["prio"][l][b][h]), cfg)
+    return time.perf_counter() - t0
+
+
+def host_cores():
+    """Host cores this process may use: its CPU affinity, capped by the
+    OMP_NUM_THREADS share when the environment sets one."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
 def cpu_baseline(w, gpu, seed, first_input_step, budget_s):
     """Time the CPU oracle (as it stands) on a bounded, exact sample of the same
-    workload: a subset of segments continued from the GPU's current state."""
+    workload: a subset of segments continued from the GPU's current state, on
+    every host core through a process pool (segments are independent given
+    their row's budget). The pool first computes the sampled rows' confidence
+    for every sampled step, then runs the segments in groups."""
+    import copy
+    import multiprocessing as mp
+
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
 
     from kv_cache_eviction_04_amd import synth
     from oracle import cache as OC
-    from oracle import confidence as OCONF
 
     L, B, H = w["num_layers"], w["batch"], w["num_kv_heads"]
     rows = sorted({0, B - 1})
     layers = sorted({0, L // 2, L - 1})
     segs = [(l * B + b) * H + h for l in layers for b in rows for h in range(H)]
     cfg = OC.Config.from_dict(w)
-    oc = OC.OracleCache(cfg, segs)
+    cores = host_cores()
+    states = {}
     for s in segs:
         ro = {k: v.cpu().numpy() for k, v in gpu.read_cache(s, 1).items()}
         seg = OC.Segment(w["head_dim"])
@@ -104,44 +153,129 @@ def cpu_baseline(w, gpu, seed, first_input_step, budget_s):
         seg.ks, seg.vs = ro["k_scale"][0, :n].copy(), ro["v_scale"][0, :n].copy()
         seg.ema = ro["ema"][0, :n].astype(np.float64)
         seg.prio = ro["prio"][0, :n].copy()
-        oc.segs[s] = seg
-    oc.t = gpu.position
+        states[s] = seg
+    t_pos = gpu.position
+    # the sample: enough steps for about budget_s seconds of single-core work
+    # (the per-segment step cost is measured on one step first)
     dev = torch.device("cuda", 0)
-    t_seg = t_conf = 0.0
-    n_steps = 0
-    with threadpool_limits(limits=1):
-        while t_seg + t_conf < budget_s:
-            x = synth.step_inputs(w, seed, first_input_step + n_steps, dev)
-            xs = {k: (None if v is None else v.cpu().numpy()) for k, v in x.items()}
-            base = None
-            if cfg.policy == "conf":
-                t0 = time.perf_counter()
-                base = {}
-                for b in rows:
-                    c = OCONF.confidence(xs["logits"][b], cfg.w_entropy, cfg.w_margin, cfg.w_pmax)
-                    base[b] = OCONF.gate(c, cfg.tau, cfg.n_low, cfg.n_high, cfg.gate_literal)
-                t_conf += time.perf_counter() - t0
-            t0 = time.perf_counter()
-            oc.step(logits=xs["logits"] if cfg.policy == "conf" else None, q=xs["q"], k_new=xs["k"],
-                    v_new=xs["v"], prio=xs["prio"], base_override=base)
-            t_seg += time.perf_counter() - t0
-            n_steps += 1
+    lbs = sorted({(l, b) for l in layers for b in rows})
+
+    def host_step(i):
+        x = synth.step_inputs(w, seed, first_input_step + i, dev)
+        li = torch.tensor([l for l, _ in lbs], device=dev)
+        bi = torch.tensor([b for _, b in lbs], device=dev)
+        q, k, v = (x[n][li, bi].cpu().numpy() for n in ("q", "k", "v"))
+        pr = x["prio"][li, bi].cpu().numpy() if x["prio"] is not None else None
+        nest = {n: {l: {} for l, _ in lbs} for n in ("q", "k", "v", "prio")}
+        for j, (l, b) in enumerate(lbs):
+            nest["q"][l][b], nest["k"][l][b], nest["v"][l][b] = q[j], k[j], v[j]
+            if pr is not None:
+                nest["prio"][l][b] = pr[j]
+        logits = None if x["logits"] is None else {b: x["logits"][b].cpu().numpy() for b in rows}
+        return dict(q=nest["q"], k=nest["k"], v=nest["v"], prio=nest["prio"] if pr is not None else None,
+                    logits=logits)
+
+    probe = host_step(0)
+    t0 = time.perf_counter()
+    base_probe = None
+    if cfg.policy == "conf":
+        base_probe, _ = _oracle_rows_worker((cfg, [((b, 0), probe["logits"][b]) for b in rows]))
+    t_conf1 = time.perf_counter() - t0
+    one = dict(probe, base={b: base_probe[(b, 0)] for b in rows} if base_probe else None)
+    probe_states = {s: states[s] for s in segs[:4]}
+    t_seg1 = _oracle_segments_worker((cfg, t_pos, copy.deepcopy(probe_states), [one])) / 4
+    per_step_serial = t_seg1 * len(segs) + t_conf1
+    n_steps = max(2, min(100, int(budget_s / max(per_step_serial, 1e-6))))
+    steps = [probe] + [host_step(i) for i in range(1, n_steps)]
+
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_rows_worker, [(cfg, [])] * cores)  # start the workers before timing
+        t0 = time.perf_counter()
+        bases = {}
+        if cfg.policy == "conf":
+            tasks = [((b, i), st["logits"][b]) for i, st in enumerate(steps) for b in rows]
+            chunks = [tasks[j::cores] for j in range(cores)]
+            for out, _ in pool.map(_oracle_rows_worker, [(cfg, c) for c in chunks if c]):
+                bases.update(out)
+        t_conf = time.perf_counter() - t0
+        for i, st in enumerate(steps):
+            st["base"] = {b: bases[(b, i)] for b in rows} if bases else None
+            st["logits"] = None
+        groups = [segs[j::cores] for j in range(cores) if segs[j::cores]]
+        t0 = time.perf_counter()
+        pool.map(_oracle_segments_worker, [(cfg, t_pos, {s: states[s] for s in g}, steps) for g in groups])
+        t_seg = time.perf_counter() - t0
     S = L * B * H
-    # oc.step computes the confidence of its rows itself; t_conf times that same work on its own, so
-    # the segment part is (t_seg - t_conf) and the confidence part scales with the batch rows.
-    per_step = ((t_seg - t_conf) / n_steps) * (S / len(segs)) + (t_conf / n_steps) * (B / len(rows))
+    # wall time per step on `cores` processes, extrapolated from the sampled
+    # segments (and rows) to every segment (and row) of the workload
+    per_step = (t_seg / n_steps) * (S / len(segs)) + (t_conf / n_steps) * (B / len(rows))
     return {
         "value": 1.0 / per_step,
         "unit": "steps/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{n_steps} steady steps of {len(segs)} of {S} segments (batch rows {rows}, layers {layers}, "
                    f"all {H} KV heads) continued from the GPU state, plus confidence for {len(rows)} of {B} rows; "
-                   f"per-step time extrapolated x{S}/{len(segs)} (segments) and x{B}/{len(rows)} (rows); "
-                   f"float64 NumPy, one thread"),
+                   f"float64 NumPy oracle in {cores} worker processes (segments and (row, step) confidences "
+                   f"spread over them); per-step wall time extrapolated x{S}/{len(segs)} (segments) and "
+                   f"x{B}/{len(rows)} (rows)"),
         "seconds": t_seg + t_conf,
         "steps_timed": n_steps,
     }
+
+
+def hbm_ceiling(dev, nbytes=3 << 29, reps=10):
+    """The HBM bandwidth plain streaming kernels attain on this part, beside
+    its peak: the library's probe kernel reading (and copying) nbytes, and
+    torch's device copy of the same buffer, each timed with events."""
+    import torch
+
+    from kv_cache_eviction_04_amd import confkv
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    read_ms = timed(lambda: confkv.bandwidth_probe(src, sink, copy=False))
+    copy_ms = timed(lambda: confkv.bandwidth_probe(src, dst, copy=True))
+    torch_ms = timed(lambda: dst.copy_(src))
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "read_ms": read_ms, "read_gbps": nbytes / (read_ms * 1e-3) / 1e9,
+            "copy_ms": copy_ms, "copy_gbps": 2 * nbytes / (copy_ms * 1e-3) / 1e9,
+            "torch_copy_gbps": 2 * nbytes / (torch_ms * 1e-3) / 1e9,
+            "kernels": "confkv_bandwidth_probe read and copy (16-byte loads, 8 in flight per lane); torch copy_; "
+                       "copies count bytes read + written"}
+
+
+def kv_footprint(gpu, w):
+    """Bytes of K/V rows the cache retains now: 4d per FP16 row, 2d + 8 per
+    INT8 row (codes and two fp32 scales), summed over every segment."""
+    import torch
+    d = w["head_dim"]
+    total = rows = 0
+    chunk = max(1, (64 << 20) // max(gpu.rows_max, 1))
+    for first in range(0, gpu.S, chunk):
+        n = min(chunk, gpu.S - first)
+        ro = gpu.read_cache(first, n, fields=("is_int8",))
+        live = torch.arange(gpu.rows_max, device=ro["len"].device)[None, :] < ro["len"][:, None]
+        is8 = (ro["is_int8"] != 0) & live
+        n8 = int(is8.sum())
+        n_all = int(live.sum())
+        total += n8 * (2 * d + 8) + (n_all - n8) * 4 * d
+        rows += n_all
+    return {"bytes": total, "gb": total / 1e9, "rows": rows, "position": gpu.position}
 
 
 def main():
@@ -160,6 +294,15 @@ def main():
                          "fused steps; 0 skips it")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for HBM counter scaling)")
+    ap.add_argument("--spread-steps", type=int, default=200,
+                    help="steps timed one by one (an event at every step boundary) for p10/p50/p90; 0 skips it")
+    ap.add_argument("--graph-steps", type=int, default=None,
+                    help="steps captured into one hipGraph and replayed (default: 512 for the launch-bound toy "
+                         "and GPT-2 shapes, 0 for the others)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-copy HBM ceiling measurement")
+    ap.add_argument("--run-to", type=int, default=0,
+                    help="after the measurements, keep decoding (untimed) until this many tokens have been "
+                         "generated after the prefill, then report the retained K/V footprint there")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -184,6 +327,12 @@ def main():
         torch.cuda.synchronize()
         log("calibration kernel (neg): 1 GiB read + 1 GiB written")
         del src, dst
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = hbm_ceiling(dev)
+        log(f"streaming over {ceiling['bytes'] / 2**30:.2f} GiB: read {ceiling['read_gbps']:.0f} GB/s, copy "
+            f"{ceiling['copy_gbps']:.0f} GB/s (read + write; torch copy {ceiling['torch_copy_gbps']:.0f} GB/s)")
 
     log(f"workload {args.workload}: L{L} B{B} Hq{Hq} Hkv{H} d{d} prefill {w['prefill']}")
     t0 = time.perf_counter()
@@ -261,6 +410,72 @@ def main():
         step_i += len(red_inputs)
         gpu.stats(reset=True)
         reduce_avg_ms = red["reduce_ms"] / max(red["reduce_launches"], 1)
+    # The distribution of step times: one event at every step boundary on the
+    # stream the steps run on (each record costs a little stream time, so this
+    # is a pass of its own after the timed region).
+    spread = None
+    if args.spread_steps > 0:
+        sp_in = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(args.spread_steps)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.spread_steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i, x in enumerate(sp_in):
+            run_step(x)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        step_i += args.spread_steps
+        gpu.stats(reset=True)
+        ts = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.spread_steps))
+        q = lambda f: ts[min(len(ts) - 1, int(f * (len(ts) - 1) + 0.5))]  # noqa: E731
+        spread = {"steps": len(ts), "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9),
+                  "mean_ms": sum(ts) / len(ts), "min_ms": ts[0], "max_ms": ts[-1]}
+        log(f"step time p10/p50/p90 {spread['p10_ms']:.4f}/{spread['p50_ms']:.4f}/{spread['p90_ms']:.4f} ms "
+            f"over {len(ts)} steps")
+        del sp_in
+
+    # The same steps captured into one hipGraph and replayed once: the step's
+    # two launches per step without the host's launch overhead. The position
+    # is a launch argument, so one graph covers one run of consecutive
+    # positions (the library's host position advances during the capture).
+    graph = None
+    n_graph = args.graph_steps if args.graph_steps is not None else (
+        512 if args.workload in ("toy", "gpt2_small") else 0)
+    if n_graph > 0:
+        g_in = [synth.step_inputs(w, args.seed, step_i + i, dev) for i in range(2 * n_graph)]
+        e_in = g_in[:n_graph]
+        torch.cuda.synchronize()
+        t_e = time.perf_counter()
+        for x in e_in:  # eager reference over the same number of steps
+            run_step(x)
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - t_e) * 1e3 / n_graph
+        step_i += n_graph
+        cg = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(cg, stream=cap):
+                for x in g_in[n_graph:]:
+                    run_step(x)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        step_i += n_graph
+        graph_ms = e0.elapsed_time(e1) / n_graph
+        if gpu.status() != confkv.OK:
+            log("device status after the graph replay is not OK")
+            sys.exit(1)
+        gpu.stats(reset=True)
+        graph = {"steps": n_graph, "graph_ms_per_step": graph_ms, "graph_steps_per_s": 1e3 / graph_ms,
+                 "eager_wall_ms_per_step": eager_ms}
+        log(f"hipGraph of {n_graph} steps: {graph_ms * 1e3:.1f} us/step ({1e3 / graph_ms:.0f} steps/s) against "
+            f"{eager_ms * 1e3:.1f} us/step issued one by one")
+        del g_in, e_in, cg
+
     achieved = alg_per_launch / (fused_avg_ms * 1e-3) / 1e9
     log(f"{steps_per_s:.1f} steps/s ({ms_per_step:.4f} ms/step), KV {kv_gbps:.0f} GB/s; fused kernel "
         f"{fused_avg_ms * 1e3:.1f} us avg -> {achieved:.0f} GB/s algorithmic"
@@ -393,6 +608,22 @@ def main():
         del pq, pk_, pv_, pp, pout, ws
         torch.cuda.empty_cache()
 
+    if args.run_to > 0:
+        target = w["prefill"] + args.run_to
+        log(f"decoding on to position {target} (from {gpu.position}) for the footprint")
+        while gpu.position < target:
+            run_step(synth.step_inputs(w, args.seed, step_i, dev))
+            step_i += 1
+            if step_i % 4096 == 0:
+                torch.cuda.synchronize()
+                log(f"... position {gpu.position}")
+        torch.cuda.synchronize()
+        if gpu.status() != confkv.OK:
+            log("device status after the run is not OK")
+            sys.exit(1)
+    footprint = kv_footprint(gpu, w)
+    log(f"retained K/V at position {footprint['position']}: {footprint['gb']:.3f} GB in {footprint['rows']} rows")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
@@ -409,7 +640,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 MFMA, fp32 accumulate; " + ("fp16 window + int8 K/V" if w["old_int8"] else "fp16 K/V"),
         "data": "synthetic",
         "config": {
             "workload": args.workload, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": d,
@@ -428,6 +659,10 @@ def main():
         "reducer_us": None if reduce_avg_ms is None else reduce_avg_ms * 1e3,
         "rows_evicted_per_step": st["rows_evicted"] / args.steps,
         "rows_moved_per_step": st["rows_moved"] / args.steps,
+        "step_time_spread": spread,
+        "hbm_ceiling": ceiling,
+        "kv_footprint": footprint,
+        "graph": graph,
         "roofline": {
             "bound": "hbm",
             "kernel": "fused_step_kernel",

@@ -328,6 +328,17 @@ int confkv_stats(confkv_handle* h, void* stream, uint64_t* totals, int32_t reset
  * and launch counts of the fused kernel and of the reducer, then (if reset)
  * clears them. confkv_profile_kernel does the same for one kernel: 0 fused
  * step, 1 logits reducer, 2 attend, 3 evict (EINVAL otherwise). */
+/* A measurement aid, not part of the decode step: a plain streaming kernel
+ * over `bytes` of device memory at `src`, enqueued on `stream`, giving the
+ * HBM bandwidth a simple read or copy attains on this part, the reference
+ * beside the published peak when the step's kernels are measured.
+ *   copy = 0: read only; `dst` is a scratch of at least 1 KiB (nothing is
+ *             normally written to it);
+ *   copy = 1: copy `bytes` from `src` to `dst` (buffers must not overlap).
+ * src and dst 16-byte aligned; bytes a positive multiple of 16; caller-owned
+ * device pointers. EINVAL on bad arguments, with nothing enqueued. */
+int confkv_bandwidth_probe(void* stream, const void* src, void* dst, size_t bytes, int32_t copy);
+
 #define CONFKV_PROFILE_STEP 1
 #define CONFKV_PROFILE_REDUCE 2
 #define CONFKV_PROFILE_ATTEND 4

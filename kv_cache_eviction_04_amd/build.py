@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libconfkv.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = [os.path.join(HERE, "csrc", n)
-           for n in ("kernels.hip", "split_attend.hip", "sample.hip", "kvpop_prefill.hip", "api.hip")]
+           for n in ("kernels.hip", "split_attend.hip", "sample.hip", "kvpop_prefill.hip", "probe.hip", "api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -68,6 +68,7 @@ def lib():
         "confkv_profile_read": (c_int, [P, POINTER(c_double), POINTER(c_int64), POINTER(c_double),
                                         POINTER(c_int64), c_int32]),
         "confkv_profile_kernel": (c_int, [P, c_int32, POINTER(c_double), POINTER(c_int64), c_int32]),
+        "confkv_bandwidth_probe": (c_int, [P, P, P, c_size_t, c_int32]),
         "confkv_position": (c_int64, [P]),
         "confkv_status": (c_int, [P]),
         "confkv_destroy": (c_int, [P]),
@@ -86,7 +87,18 @@ EXPORTED = ("confkv_validate", "confkv_state_bytes", "confkv_rows_max", "confkv_
             "confkv_kvpop_prefill_workspace", "confkv_kvpop_prefill", "confkv_kvpop_prefill_noalloc",
             "confkv_kvpop_future_target",
             "confkv_read_cache", "confkv_read_last_step", "confkv_stats", "confkv_profile", "confkv_profile_read",
-            "confkv_profile_kernel", "confkv_position", "confkv_status", "confkv_destroy", "confkv_strerror")
+            "confkv_profile_kernel", "confkv_bandwidth_probe", "confkv_position", "confkv_status", "confkv_destroy",
+            "confkv_strerror")
+
+
+def bandwidth_probe(src, dst, copy=False):
+    """Enqueue the library's plain streaming read (copy False; dst: a scratch
+    of at least 1 KiB) or copy of the whole of ``src`` on torch's current stream."""
+    if copy and dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ValueError("copy: dst is smaller than src")
+    stream = c_void_p(torch.cuda.current_stream(src.device).cuda_stream)
+    _check(lib().confkv_bandwidth_probe(stream, _ptr(src), _ptr(dst), src.numel() * src.element_size(), int(copy)),
+           "confkv_bandwidth_probe")
 
 
 class ConfKVError(RuntimeError):

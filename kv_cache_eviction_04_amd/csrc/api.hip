@@ -20,6 +20,10 @@
 
 using namespace confkv;
 
+namespace confkv {
+int launch_stream_probe(const void* src, void* dst, size_t bytes, int32_t copy, void* stream);  // probe.hip
+}
+
 // Workspace of confkv_kvpop_prefill_noalloc: a file-scope device array, one
 // copy per GPU, held until the process ends. Host code never passes its name
 // to a kernel or a copy (on the host it is only a stand-in for the symbol);
@@ -778,6 +782,12 @@ CONFKV_API int confkv_profile_kernel(confkv_handle* h, int32_t kernel, double* m
     p.n = 0;
   }
   return CONFKV_OK;
+}
+
+CONFKV_API int confkv_bandwidth_probe(void* stream, const void* src, void* dst, size_t bytes, int32_t copy) {
+  if (!src || !dst || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return CONFKV_EINVAL;
+  if (bytes < 16 || (bytes & 15) || (copy != 0 && copy != 1)) return CONFKV_EINVAL;
+  return launch_stream_probe(src, dst, bytes, copy, stream) == 0 ? CONFKV_OK : CONFKV_EHIP;
 }
 
 CONFKV_API int64_t confkv_position(const confkv_handle* h) { return live(h) ? h->t : -1; }

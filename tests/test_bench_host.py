@@ -50,3 +50,49 @@ def test_stored_traffic_is_tied_to_the_kernel_sources(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.stored_traffic("llama3_8b_32k") is None
     assert bench.stored_traffic("no_such_workload") is None
+
+
+def test_cpu_baseline_workers_reproduce_the_oracle_step():
+    # The baseline's pool runs the oracle's confidence per (row, step) and its
+    # per-segment step per segment; together they must equal OracleCache.step.
+    import copy
+
+    import numpy as np
+    import torch
+
+    from oracle import cache as OC
+
+    for name, over in (("toy", dict(prefill=100)), ("kvpop_qwen3_8b", dict(num_layers=1, batch=2, protect_last=8,
+                                                                          fp16_window=8, kvpop_k=20))):
+        w = synth.workload(name, **over)
+        cfg = OC.Config.from_dict(w)
+        S = w["num_layers"] * w["batch"] * w["num_kv_heads"]
+        rng = np.random.default_rng(0)
+        ref = OC.OracleCache(cfg)
+        P0 = w["prefill"]
+        rows_of = {s: (rng.standard_normal((P0, w["head_dim"])), rng.standard_normal((P0, w["head_dim"])))
+                   for s in range(S)}
+        ref.init(P0, lambda s: rows_of[s])
+        states = {s: copy.deepcopy(ref.segs[s]) for s in range(S)}
+        steps = []
+        for i in range(6):
+            x = {k: (None if v is None else v.numpy()) for k, v in
+                 synth.step_inputs(w, 1, i, torch.device("cpu")).items()}
+            steps.append(x)
+            ref.step(logits=x["logits"], q=x["q"], k_new=x["k"], v_new=x["v"], prio=x["prio"])
+        if cfg.policy == "conf":
+            tasks = [((b, i), x["logits"][b]) for i, x in enumerate(steps) for b in range(w["batch"])]
+            bases, _ = bench._oracle_rows_worker((cfg, tasks))
+            for i, x in enumerate(steps):
+                x["base"] = {b: bases[(b, i)] for b in range(w["batch"])}
+        bench._oracle_segments_worker((cfg, P0, states, steps))
+        for s in range(S):
+            assert states[s].pos.tolist() == ref.segs[s].pos.tolist()
+            assert np.array_equal(states[s].ema, ref.segs[s].ema)
+
+
+def test_host_cores_respects_the_thread_share(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.host_cores() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.setenv("OMP_NUM_THREADS", "")
+    assert bench.host_cores() == len(os.sched_getaffinity(0))
