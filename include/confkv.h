@@ -87,7 +87,10 @@ typedef struct confkv_config {
   int32_t vocab;           /* V >= 2 (CONF); ignored for KVPOP                     */
   int32_t capacity;        /* rows older than the FP16 window that one segment can
                               hold; >= max(prefill_len, largest budget + 1,
-                              num_sink + protect_last + 1)                        */
+                              num_sink + protect_last + 1). It counts the old
+                              (INT8, or FP16 under KVPOP) region only: the W + 1
+                              window slots are a fixed ring beside it, so the
+                              rows a segment can hold are capacity + W + 1     */
   int32_t policy;          /* CONFKV_POLICY_CONF | CONFKV_POLICY_KVPOP             */
   int32_t n_low, n_high;   /* the two base budgets (rows per segment)              */
   int32_t protect_last;    /* P: the last P positions are never evicted (KVPOP: w) */
@@ -289,7 +292,10 @@ int confkv_kvpop_future_target(confkv_handle* h, void* stream, int32_t seq_len, 
                                const float* lse, float* target);
 
 /* Gather the logical contents of segments [seg_first, seg_first+seg_count) in
- * ascending position order. Per segment i, rows 0..len[i]-1 of each
+ * ascending position order. The ranking score is not part of the cache (the
+ * step forms it from ema, position and the step's t, then ranks and evicts
+ * in the same kernel); a step's scores are read, with the rows it saw, by
+ * confkv_read_last_step under record_scores. Per segment i, rows 0..len[i]-1 of each
  * [seg_count][rows_max] / [seg_count][rows_max][d] output are written (rows_max
  * = confkv_rows_max); later rows are left untouched. Any output except len may
  * be NULL. FP16 rows appear in k16/v16 and have zero k8/v8/scales; INT8 rows
