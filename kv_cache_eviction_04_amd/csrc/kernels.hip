@@ -182,6 +182,49 @@ struct Stage {
   __device__ __forceinline__ int32_t* list(int plane) const { return reinterpret_cast<int32_t*>(p + plane * rs); }
 };
 
+// A PV tile buffer with the weights of the lane's 8 rows loaded beside it.
+template <class B>
+struct WithW {
+  B b;
+  float4 w0, w1;
+};
+
+// Walks over the staged keys. An HBM-staged key costs a memory round trip, so
+// that instance loads 8 keys of a thread before using them; one at a time, a
+// thread's walk over a 32K-row segment would be some 128 round trips in a
+// row. f(i, key) is called in ascending i within a thread.
+template <bool kLds>
+constexpr int kKeyBatch = kLds ? 1 : 8;
+// rows i = tid, tid + 256, ... below n
+template <bool kLds, class F>
+__device__ __forceinline__ void for_keys(const Stage<kLds>& st, int n, F&& f) {
+  constexpr int U = kKeyBatch<kLds>;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * U) {
+    uint64_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + kThreads * u;
+      k[u] = i < n ? st.key(i) : ~0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + kThreads * u < n) f(i0 + kThreads * u, k[u]);
+  }
+}
+// rows lo .. hi-1, in order
+template <bool kLds, class F>
+__device__ __forceinline__ void for_keys_range(const Stage<kLds>& st, int lo, int hi, F&& f) {
+  constexpr int U = kKeyBatch<kLds>;
+  for (int i0 = lo; i0 < hi; i0 += U) {
+    uint64_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) k[u] = i0 + u < hi ? st.key(i0 + u) : ~0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u < hi) f(i0 + u, k[u]);
+  }
+}
+
 // The e-th smallest key (e >= 1) over keys [0, rows): an 8-bit-digit radix
 // select from the most significant digit down. Keys are unique, so once the
 // selected digit's bin holds a single key, that key is the answer and one
@@ -194,10 +237,9 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
   for (int shift = 56; shift >= 0; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < rows; i += kThreads) {
-      const uint64_t k = st.key(i);
+    for_keys(st, rows, [&](int, uint64_t k) {
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-    }
+    });
     __syncthreads();
     const uint32_t cnt = hist[tid];
     uint32_t total;
@@ -216,10 +258,9 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
     __syncthreads();
     if (single && shift > 0) {
       uint64_t mk = ~0ull;
-      for (int i = tid; i < rows; i += kThreads) {
-        const uint64_t k = st.key(i);
+      for_keys(st, rows, [&](int, uint64_t k) {
         if ((k & mask) == prefix && k < mk) mk = k;
-      }
+      });
       return block_min_u64(mk, red64);
     }
   }
@@ -596,49 +637,71 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     floatx4 O[CBW];
 #pragma unroll
     for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto weights = [&](int srow, half8& ahi, half8& alo) {
+    // The weights of 8 consecutive rows of head lj (lanes lj < G; zero for the
+    // others), as fp16 hi and lo A operands.
+    auto wload = [&](int srow, float4& p0, float4& p1) {
       if (lj < G) {
-        const float4 p0 = st.at4(lj, srow), p1 = st.at4(lj, srow + 4);
-        const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
-                                __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
-                                __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
-                                __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
-        uint4 h, lw;
-        h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
-        h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
-        h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
-        h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
-        lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
-        lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
-        lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
-        lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
-        ahi = as_h8(h);
-        alo = as_h8(lw);
+        p0 = st.at4(lj, srow);
+        p1 = st.at4(lj, srow + 4);
       } else {
-        ahi = half8{};
-        alo = half8{};
+        p0 = p1 = float4{0.0f, 0.0f, 0.0f, 0.0f};
       }
+    };
+    auto wpack = [&](const float4& p0, const float4& p1, half8& ahi, half8& alo) {
+      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
+                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
+                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
+                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
+      uint4 h, lw;
+      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
+      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
+      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
+      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
+      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
+      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
+      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
+      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
+      ahi = as_h8(h);
+      alo = as_h8(lw);
     };
     // V tiles: a lane loads 8 consecutive rows (lane group lq); lanes whose
     // rows all lie past the region's nvalid rows read lane group 0's (same
-    // lines, no traffic), and their weights are 0
+    // lines, no traffic), and their weights are 0. LDS-staged weights are read
+    // when a tile is computed; HBM-staged ones are loaded with the tile.
     auto pv16 = [&](const uint16_t* vbase, int srow0, int ntiles, int nvalid) {
-      pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
-          0, ntiles,
-          [&](int tt, PV16Buf<CBW>& bf) {
-            const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * (32 * tt + 8 * lq < nvalid ? lane : lj);
+      auto vload = [&](int tt, PV16Buf<CBW>& bf) {
+        const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * (32 * tt + 8 * lq < nvalid ? lane : lj);
 #pragma unroll
-            for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
-          },
-          [&](int tt, const PV16Buf<CBW>& bf) {
-            half8 ahi, alo;
-            weights(srow0 + 32 * tt + 8 * lq, ahi, alo);
+        for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
+      };
+      auto mm = [&](const PV16Buf<CBW>& bf, const half8& ahi, const half8& alo) {
 #pragma unroll
-            for (int k = 0; k < CBW; ++k) {
-              O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
-              O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
-            }
-          });
+        for (int k = 0; k < CBW; ++k) {
+          O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
+          O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
+        }
+      };
+      if constexpr (kLds) {
+        pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(0, ntiles, vload, [&](int tt, const PV16Buf<CBW>& bf) {
+          float4 p0, p1;
+          half8 ahi, alo;
+          wload(srow0 + 32 * tt + 8 * lq, p0, p1);
+          wpack(p0, p1, ahi, alo);
+          mm(bf, ahi, alo);
+        });
+      } else {
+        pipelined<2, WithW<PV16Buf<CBW>>>(
+            0, ntiles,
+            [&](int tt, WithW<PV16Buf<CBW>>& bf) {
+              vload(tt, bf.b);
+              wload(srow0 + 32 * tt + 8 * lq, bf.w0, bf.w1);
+            },
+            [&](int tt, const WithW<PV16Buf<CBW>>& bf) {
+              half8 ahi, alo;
+              wpack(bf.w0, bf.w1, ahi, alo);
+              mm(bf.b, ahi, alo);
+            });
+      }
     };
     const int nv_old = n_old32 >> 5;
     auto load_pv8 = [&](int tt, PV8Buf& bf) {
@@ -651,9 +714,8 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       }
     };
     if (par.old_int8) {
-      auto pv8 = [&](int tt, const PV8Buf& bf) {
-        half8 ahi, alo, blo, bhi;
-        weights(32 * tt + 8 * lq, ahi, alo);
+      auto mm8 = [&](const PV8Buf& bf, const half8& ahi, const half8& alo) {
+        half8 blo, bhi;
         i8x16_to_h8(bf.v, blo, bhi);
         O[0] = mfma16(ahi, blo, O[0]);
         O[0] = mfma16(alo, blo, O[0]);
@@ -662,7 +724,27 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
           O[1] = mfma16(alo, bhi, O[1]);
         }
       };
-      pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, pv8);
+      if constexpr (kLds) {
+        pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, [&](int tt, const PV8Buf& bf) {
+          float4 p0, p1;
+          half8 ahi, alo;
+          wload(32 * tt + 8 * lq, p0, p1);
+          wpack(p0, p1, ahi, alo);
+          mm8(bf, ahi, alo);
+        });
+      } else {
+        pipelined<4, WithW<PV8Buf>>(
+            0, nv_old,
+            [&](int tt, WithW<PV8Buf>& bf) {
+              load_pv8(tt, bf.b);
+              wload(32 * tt + 8 * lq, bf.w0, bf.w1);
+            },
+            [&](int tt, const WithW<PV8Buf>& bf) {
+              half8 ahi, alo;
+              wpack(bf.w0, bf.w1, ahi, alo);
+              mm8(bf.b, ahi, alo);
+            });
+      }
     } else {
       pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old, n_old);
     }
@@ -854,10 +936,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   if (e > 1 && e <= 8) {
     for (uint32_t r = 1; r < e; ++r) {
       uint64_t mk = ~0ull;
-      for (int i = tid; i < rows; i += kThreads) {
-        const uint64_t k = st.key(i);
+      for_keys(st, rows, [&](int, uint64_t k) {
         if (k > T && k < mk) mk = k;
-      }
+      });
       T = block_min_u64(mk, red_k);
     }
   } else if (e > 8) {
@@ -878,12 +959,13 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       vmin = vmax = imin;
     }
   } else if (e > 1) {
-    for (int i = tid; i < n_old; i += kThreads)
-      if (st.key(i) <= T) {
+    for_keys(st, n_old, [&](int i, uint64_t k) {
+      if (k <= T) {
         ++ev_old;
         vmin = min(vmin, i);
         vmax = max(vmax, i);
       }
+    });
     for (int o = 32; o > 0; o >>= 1) {
       ev_old += __shfl_xor(ev_old, o, 64);
       vmin = min(vmin, __shfl_xor(vmin, o, 64));
@@ -934,25 +1016,28 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     }
   } else if (rem > 1) {
     // victim predicate for the hole fill: vmin is not a hole when it takes the aged-out row
-    auto hole = [&](int i) { return st.key(i) <= T && !(into_hole && i == vmin); };
+    auto hole = [&](int i, uint64_t k) { return k <= T && !(into_hole && i == vmin); };
     const int per = (n_old + kThreads - 1) / kThreads;
     const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
     uint32_t hv = 0, sv = 0;
-    for (int i = lo; i < hi; ++i) {
-      const bool v = hole(i);
+    for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
+      const bool v = hole(i, k);
       hv += (v && i < m) ? 1u : 0u;
       sv += (!v && i >= m) ? 1u : 0u;
-    }
+    });
     uint32_t nh, ns;
     uint32_t ho = block_excl_scan_u32(hv, red_u, &nh);
     uint32_t so = block_excl_scan_u32(sv, red_u, &ns);
     int32_t* holes = st.list(2);
     int32_t* srcs = st.list(3);
-    for (int i = lo; i < hi; ++i) {
-      const bool v = hole(i);
-      if (v && i < m) holes[ho++] = i;
-      if (!v && i >= m) srcs[so++] = i;
-    }
+    for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
+      const bool v = hole(i, k);
+      const bool to_hole = v && i < m, to_src = !v && i >= m;
+      if (to_hole) holes[ho] = i;
+      if (to_src) srcs[so] = i;
+      ho += to_hole ? 1u : 0u;
+      so += to_src ? 1u : 0u;
+    });
     __syncthreads();
     moved = nh;
     for (int r = rg; r < (int)nh; r += RPB) {
