@@ -275,11 +275,14 @@ int collect(EventPool& pool) {
 }
 
 // Staging of a launch: LDS planes sized for the most rows a segment can hold
-// at this step, or the HBM stage when they do not fit.
+// at this step, or the HBM stage when they do not fit. The HBM-staged
+// instance takes LDS for its selection (histogram, candidates and, when it
+// fits, the victim bitmask over every stage row).
 struct Staging {
   bool use_lds;
   int32_t lds_rows;
   int lds_bytes;
+  int32_t sel_bits_lds;
 };
 
 Staging staging(const confkv_handle* h, int planes) {
@@ -291,6 +294,12 @@ Staging staging(const confkv_handle* h, int planes) {
   st.use_lds = lds_bytes <= fused_max_dynamic_lds();
   st.lds_rows = st.use_lds ? (int32_t)lds_rows : 0;
   st.lds_bytes = st.use_lds ? (int)lds_bytes : 0;
+  st.sel_bits_lds = 0;
+  if (!st.use_lds) {
+    const int64_t bits_bytes = sel_bits_words(lay.rows_max) * 4;
+    st.sel_bits_lds = bits_bytes <= kSelBitsLdsMax ? 1 : 0;
+    st.lds_bytes = kSelLdsBytes + (st.sel_bits_lds ? (int)bits_bytes : 0);
+  }
   return st;
 }
 
@@ -424,6 +433,7 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
   }
   {
     StepArgs a;
+    memset(&a, 0, sizeof(a));
     a.t = (int32_t)h->t;
     a.seg0 = 0;
     a.q = q;
@@ -435,6 +445,7 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
     a.budget_out = budget_out;
     const Staging sg = staging(h, lay.planes);
     a.lds_rows = sg.lds_rows;
+    a.sel_bits_lds = sg.sel_bits_lds;
     if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;  // cannot happen: carve sized the staging
     if (record_event(h, h->pf, s, true)) goto hip_fail;
     if (launch_fused_step(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0) goto hip_fail;
@@ -527,6 +538,7 @@ CONFKV_API int confkv_evict(confkv_handle* h, void* stream, const float* logits,
   a.budget_out = budget_out;
   const Staging sg = staging(h, 4);  // keys (two planes) and the compaction lists
   a.lds_rows = sg.lds_rows;
+  a.sel_bits_lds = sg.sel_bits_lds;
   if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
   if (record_event(h, h->pe, s, true) || launch_evict(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0 ||
       record_event(h, h->pe, s, false)) {

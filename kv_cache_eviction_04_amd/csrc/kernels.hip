@@ -267,6 +267,25 @@ __device__ uint64_t radix_select(const Stage<kLds>& st, int rows, uint32_t e, ui
   return prefix;
 }
 
+// Count bin in the histogram h for the calling lanes: lanes whose bin equals
+// the first active lane's add together with one atomic (neighbouring rows
+// usually share a bin), the others one by one.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
+  const uint64_t same = __ballot(bin == b0);
+  if (bin == b0) {
+    if ((int)(threadIdx.x & 63) == __ffsll((unsigned long long)same) - 1)
+      atomicAdd(&h[b0], (uint32_t)__popcll(same));
+  } else {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
+// Bits [0, x) of a 32-bit word (x clamped to 0 .. 32).
+__device__ __forceinline__ uint32_t bits_below(int x) {
+  return x <= 0 ? 0u : (x >= 32 ? ~0u : (1u << x) - 1u);
+}
+
 // One workgroup per segment. Stage-row index space: old rows [0, n_old32)
 // (rows >= n_old are padding), ring slots [n_old32, n_old32 + Wr32).
 template <int D, int G, bool kLds, int MODE>
@@ -293,10 +312,11 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   __shared__ uint32_t hist[256];
   __shared__ int32_t sh[8];
   __shared__ int32_t sh_out_live, sh_base;
+  __shared__ uint32_t sh_cand;  // HBM-staged selection: candidates gathered
   __shared__ uint32_t sel_cnt[4][2];  // per wave: live rows, eligible rows
   __shared__ uint64_t sel_key[4];     // per wave: smallest key
   __shared__ int32_t sel_row[4];      // per wave: its stage row
-  extern __shared__ float dyn_lds[];
+  extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rg = tid / LPR;
@@ -340,6 +360,14 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     st.p = lay.stage + (size_t)seg * PL * lay.rows_max;
     st.rs = lay.rows_max;
   }
+  // HBM-staged selection: the key histogram (later the candidates) in LDS and
+  // the victim bitmask, in LDS after it or else in the upper half of stage
+  // plane 2 (the compaction's hole list, at most half the old rows, sits in
+  // the lower half).
+  uint32_t* const hsel = reinterpret_cast<uint32_t*>(dyn_lds);
+  uint32_t* vbits = nullptr;
+  if constexpr (!kLds && kEv)
+    vbits = a.sel_bits_lds ? hsel + kSelBins : reinterpret_cast<uint32_t*>(st.p + 2 * st.rs + st.rs / 2);
 
   // The new row (pos t) goes to ring slot t mod Wr; the row at t - W leaves
   // the FP16 window at the end of the step; under KVpop the row at t - w gets
@@ -800,8 +828,10 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   // this row's logits partials, merged by wave 0 after the key pass
   ConfPartial part0;
   if (kEv && !kvpop && wave == 0 && lane < lay.chunks) part0 = lay.partials[(size_t)b * lay.chunks + lane];
+  if constexpr (!kLds && kEv)
+    for (int j = tid; j < kSelBins; j += kThreads) hsel[j] = 0u;
   // every wave's PV has read the weights that the keys overwrite (evict: the
-  // flag sh_out_live is cleared)
+  // flag sh_out_live is cleared; HBM-staged: the histogram is cleared)
   if constexpr (kEv) __syncthreads();
   // ---- mass, EMA, score, key. [Conf-KV post] ema of the attention mass,
   // score = alpha*ema + (1-alpha)*recency; KVpop ranks by its priority.
@@ -870,6 +900,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
         }
         if constexpr (kEv) {
           st.set_key(i, key);
+          if constexpr (!kLds) hist_add(hsel, (uint32_t)(key >> (64 - kSelBinBits)));
           if (par.record) {
             lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
             lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
@@ -933,24 +964,139 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   uint32_t e = 0;
   if ((int)n_live > budget) e = min((uint32_t)((int)n_live - budget), n_elig);
   uint64_t T = e > 0 ? kmin : 0;  // victims: key <= T (no key is 0); the first is the smallest key
-  if (e > 1 && e <= 8) {
-    for (uint32_t r = 1; r < e; ++r) {
-      uint64_t mk = ~0ull;
-      for_keys(st, rows, [&](int, uint64_t k) {
-        if (k > T && k < mk) mk = k;
-      });
-      T = block_min_u64(mk, red_k);
+  if constexpr (kLds) {
+    if (e > 1 && e <= 8) {
+      for (uint32_t r = 1; r < e; ++r) {
+        uint64_t mk = ~0ull;
+        for_keys(st, rows, [&](int, uint64_t k) {
+          if (k > T && k < mk) mk = k;
+        });
+        T = block_min_u64(mk, red_k);
+      }
+    } else if (e > 8) {
+      T = radix_select(st, rows, e, hist, red_u, sh, red_k);
     }
-  } else if (e > 8) {
-    T = radix_select(st, rows, e, hist, red_u, sh, red_k);
+  } else if (e > 1) {
+    // Victims into the bitmask. The bin holding the e-th smallest key: each
+    // thread sums 32 consecutive bins, a block scan places them.
+    constexpr int BPT = kSelBins / kThreads;
+    {
+      uint32_t cnt = 0;
+#pragma unroll 8
+      for (int j = 0; j < BPT; ++j) cnt += hsel[BPT * tid + j];
+      uint32_t total;
+      const uint32_t excl = block_excl_scan_u32(cnt, red_u, &total);
+      if (excl < e && e <= excl + cnt) {
+        uint32_t acc = excl;
+        for (int j = 0; j < BPT; ++j) {
+          const uint32_t c = hsel[BPT * tid + j];
+          if (acc + c >= e) {
+            sh[0] = BPT * tid + j;
+            sh[1] = (int32_t)acc;
+            break;
+          }
+          acc += c;
+        }
+      }
+      if (tid == 0) sh_cand = 0u;
+      __syncthreads();
+    }
+    const uint32_t tb = (uint32_t)sh[0];
+    const uint32_t e2 = e - (uint32_t)sh[1];  // victims still to choose inside bin tb
+    uint64_t* ckey = reinterpret_cast<uint64_t*>(dyn_lds);
+    int32_t* crow = reinterpret_cast<int32_t*>(ckey + kSelCandCap);
+    // One pass over the keys' high words: rows of lower bins are victims
+    // (a wave stores the bitmask words of its 64 consecutive rows); the keys
+    // of bin tb are gathered as candidates while there is room.
+    {
+      constexpr int U = 8;
+      const int wrow0 = 64 * wave;
+      for (int i0 = 0; i0 < rows; i0 += kThreads * U) {
+        uint32_t hw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + kThreads * u + tid;
+          hw[u] = i < rows ? __builtin_bit_cast(uint32_t, st.at(1, i)) : ~0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int w0 = i0 + kThreads * u + wrow0;  // the wave's first row (a multiple of 64)
+          if (w0 >= rows) break;                     // wave-uniform
+          const int i = w0 + lane;
+          const uint32_t bn = hw[u] >> (32 - kSelBinBits);
+          const uint64_t below = __ballot(i < rows && bn < tb);
+          const uint64_t inbin = __ballot(i < rows && bn == tb);
+          if (lane == 0) vbits[w0 >> 5] = (uint32_t)below;
+          if (lane == 32 && w0 + 32 < rows) vbits[(w0 >> 5) + 1] = (uint32_t)(below >> 32);
+          if (inbin != 0ull) {
+            const int leader = __ffsll((unsigned long long)inbin) - 1;
+            uint32_t base = 0u;
+            if (lane == leader) base = atomicAdd(&sh_cand, (uint32_t)__popcll(inbin));
+            base = __shfl(base, leader, 64);
+            if ((inbin >> lane) & 1ull) {
+              const uint32_t idx = base + (uint32_t)__popcll(inbin & ((1ull << lane) - 1ull));
+              if (idx < (uint32_t)kSelCandCap) {
+                ckey[idx] = ((uint64_t)hw[u] << 32) | __builtin_bit_cast(uint32_t, st.at(0, i));
+                crow[idx] = i;
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nc = sh_cand;
+    if (nc <= (uint32_t)kSelCandCap) {
+      // the e2 smallest candidates (keys are unique): a candidate's rank is
+      // the number of smaller candidates. Candidates j = tid + 256 q are
+      // ranked four at a time against all of them.
+      for (uint32_t j0 = 0; j0 < nc; j0 += 4 * kThreads) {
+        uint64_t kj[4];
+        uint32_t rk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t j = j0 + tid + kThreads * q;
+          kj[q] = j < nc ? ckey[j] : 0ull;
+          rk[q] = 0u;
+        }
+        for (uint32_t k = 0; k < nc; ++k) {
+          const uint64_t kk = ckey[k];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rk[q] += kk < kj[q] ? 1u : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t j = j0 + tid + kThreads * q;
+          if (j < nc && rk[q] < e2) {
+            const int r = crow[j];
+            atomicOr(&vbits[r >> 5], 1u << (r & 31));
+          }
+        }
+      }
+    } else {
+      // too many keys share the bin: a radix select over the staged keys
+      // gives the e-th smallest key, and the bin's keys up to it are victims
+      T = radix_select(st, rows, e, hist, red_u, sh, red_k);
+      for_keys(st, rows, [&](int i, uint64_t k) {
+        if ((uint32_t)(k >> (64 - kSelBinBits)) == tb && k <= T) atomicOr(&vbits[i >> 5], 1u << (i & 31));
+      });
+    }
+    __syncthreads();
   }
+  // is stage row i a victim
+  auto victim = [&](int i) -> bool {
+    if constexpr (!kLds) {
+      if (e > 1) return (vbits[i >> 5] >> (i & 31)) & 1u;
+    }
+    return st.key(i) <= T;
+  };
 
   // ---- compaction of the old region. The row leaving the FP16 window (if it
   // survived) takes the lowest victim's slot; the other victims below the new
   // count m become holes, filled in ascending order by the survivors at or
   // above m. The steady state (one old victim, one aged-out row) moves nothing.
   const int slot_out = pos_out >= 0 ? pos_out % Wr : 0;
-  const bool age = pos_out >= 0 && sh_out_live && st.key(n_old32 + slot_out) > T;
+  const bool age = pos_out >= 0 && sh_out_live && !victim(n_old32 + slot_out);
   uint32_t ev_old = 0;
   int vmin = n_old, vmax = -1;
   if (e == 1) {
@@ -959,13 +1105,24 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       vmin = vmax = imin;
     }
   } else if (e > 1) {
-    for_keys(st, n_old, [&](int i, uint64_t k) {
-      if (k <= T) {
-        ++ev_old;
-        vmin = min(vmin, i);
-        vmax = max(vmax, i);
+    if constexpr (kLds) {
+      for_keys(st, n_old, [&](int i, uint64_t k) {
+        if (k <= T) {
+          ++ev_old;
+          vmin = min(vmin, i);
+          vmax = max(vmax, i);
+        }
+      });
+    } else {
+      for (int w = tid; w < ((n_old + 31) >> 5); w += kThreads) {
+        const uint32_t bw = vbits[w] & bits_below(n_old - 32 * w);
+        if (bw) {
+          ev_old += (uint32_t)__popc(bw);
+          vmin = min(vmin, 32 * w + __ffs(bw) - 1);
+          vmax = max(vmax, 32 * w + 31 - __clz(bw));
+        }
       }
-    });
+    }
     for (int o = 32; o > 0; o >>= 1) {
       ev_old += __shfl_xor(ev_old, o, 64);
       vmin = min(vmin, __shfl_xor(vmin, o, 64));
@@ -1015,29 +1172,60 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       }
     }
   } else if (rem > 1) {
-    // victim predicate for the hole fill: vmin is not a hole when it takes the aged-out row
-    auto hole = [&](int i, uint64_t k) { return k <= T && !(into_hole && i == vmin); };
-    const int per = (n_old + kThreads - 1) / kThreads;
-    const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
-    uint32_t hv = 0, sv = 0;
-    for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
-      const bool v = hole(i, k);
-      hv += (v && i < m) ? 1u : 0u;
-      sv += (!v && i >= m) ? 1u : 0u;
-    });
-    uint32_t nh, ns;
-    uint32_t ho = block_excl_scan_u32(hv, red_u, &nh);
-    uint32_t so = block_excl_scan_u32(sv, red_u, &ns);
     int32_t* holes = st.list(2);
     int32_t* srcs = st.list(3);
-    for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
-      const bool v = hole(i, k);
-      const bool to_hole = v && i < m, to_src = !v && i >= m;
-      if (to_hole) holes[ho] = i;
-      if (to_src) srcs[so] = i;
-      ho += to_hole ? 1u : 0u;
-      so += to_src ? 1u : 0u;
-    });
+    uint32_t nh;
+    if constexpr (kLds) {
+      // victim predicate for the hole fill: vmin is not a hole when it takes the aged-out row
+      auto hole = [&](int i, uint64_t k) { return k <= T && !(into_hole && i == vmin); };
+      const int per = (n_old + kThreads - 1) / kThreads;
+      const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
+      uint32_t hv = 0, sv = 0;
+      for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
+        const bool v = hole(i, k);
+        hv += (v && i < m) ? 1u : 0u;
+        sv += (!v && i >= m) ? 1u : 0u;
+      });
+      uint32_t ns;
+      uint32_t ho = block_excl_scan_u32(hv, red_u, &nh);
+      uint32_t so = block_excl_scan_u32(sv, red_u, &ns);
+      for_keys_range(st, lo, hi, [&](int i, uint64_t k) {
+        const bool v = hole(i, k);
+        const bool to_hole = v && i < m, to_src = !v && i >= m;
+        if (to_hole) holes[ho] = i;
+        if (to_src) srcs[so] = i;
+        ho += to_hole ? 1u : 0u;
+        so += to_src ? 1u : 0u;
+      });
+    } else {
+      // From the bitmask: a thread takes whole words of consecutive rows.
+      // Holes are the victims below m (vmin excepted when it takes the
+      // aged-out row), sources the survivors at or above m.
+      const int per = (((n_old + kThreads - 1) / kThreads) + 31) & ~31;
+      const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
+      auto hole_src = [&](int w, uint32_t& hw, uint32_t& sw) {
+        const uint32_t bw = vbits[w], in = bits_below(hi - 32 * w), lt_m = bits_below(m - 32 * w);
+        hw = bw & in & lt_m;
+        if (into_hole && (vmin >> 5) == w) hw &= ~(1u << (vmin & 31));
+        sw = ~bw & in & ~lt_m;
+      };
+      uint32_t hv = 0, sv = 0;
+      for (int w = lo >> 5; 32 * w < hi; ++w) {
+        uint32_t hw, sw;
+        hole_src(w, hw, sw);
+        hv += (uint32_t)__popc(hw);
+        sv += (uint32_t)__popc(sw);
+      }
+      uint32_t ns;
+      uint32_t ho = block_excl_scan_u32(hv, red_u, &nh);
+      uint32_t so = block_excl_scan_u32(sv, red_u, &ns);
+      for (int w = lo >> 5; 32 * w < hi; ++w) {
+        uint32_t hw, sw;
+        hole_src(w, hw, sw);
+        for (; hw; hw &= hw - 1u) holes[ho++] = 32 * w + __ffs(hw) - 1;
+        for (; sw; sw &= sw - 1u) srcs[so++] = 32 * w + __ffs(sw) - 1;
+      }
+    }
     __syncthreads();
     moved = nh;
     for (int r = rg; r < (int)nh; r += RPB) {
@@ -1068,7 +1256,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     if (tid == 0 && imin >= n_old32) rpos[imin - n_old32] = -1;
   } else if (e > 1) {
     for (int r = tid; r < Wr; r += kThreads)
-      if (st.key(n_old32 + r) <= T) rpos[r] = -1;
+      if (victim(n_old32 + r)) rpos[r] = -1;
   }
 
   // ---- age-out: the row at t - W leaves the FP16 window; if it survived it
@@ -1357,7 +1545,8 @@ static void launch_fused_dg(const Layout& lay, const Params& par, const StepArgs
   if (use_lds)
     hipLaunchKernelGGL((fused_step_kernel<D, G, true, MODE>), dim3(grid), dim3(kThreads), lds_bytes, s, lay, par, a);
   else
-    hipLaunchKernelGGL((fused_step_kernel<D, G, false, MODE>), dim3(grid), dim3(kThreads), 0, s, lay, par, a);
+    hipLaunchKernelGGL((fused_step_kernel<D, G, false, MODE>), dim3(grid), dim3(kThreads),
+                       MODE == kModeAttend ? 0 : lds_bytes, s, lay, par, a);
 }
 
 template <int D, int MODE>

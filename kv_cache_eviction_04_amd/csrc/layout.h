@@ -33,6 +33,20 @@ constexpr uint32_t kErrNonFinite = 1u, kErrCapacity = 2u, kErrInternal = 4u;
 // compaction and age-out for every segment after all layers have attended.
 enum { kModeStep = 0, kModeAttend = 1, kModeEvict = 2 };
 
+// Selection in the HBM-staged instance (segments whose rows do not fit LDS
+// staging): a histogram of the keys' top kSelBinBits bits in LDS, whose
+// space then holds up to kSelCandCap candidate keys (8 bytes) and rows (4
+// bytes); a victim bitmask of one bit per stage row follows it in LDS when
+// it fits kSelBitsLdsMax bytes, else it lives in the segment's HBM stage.
+constexpr int kSelBinBits = 13;
+constexpr int kSelBins = 1 << kSelBinBits;
+constexpr int kSelLdsBytes = kSelBins * 4;
+constexpr int kSelCandCap = 2560;
+constexpr int kSelBitsLdsMax = 32 * 1024;
+static_assert(kSelCandCap * 12 <= kSelLdsBytes, "the candidates reuse the histogram's LDS");
+// victim bitmask words for a stage-row count: whole 64-row groups
+inline constexpr int64_t sel_bits_words(int64_t rows) { return ((rows + 63) / 64) * 2; }
+
 struct ConfPartial {                   // one logits chunk: m = top1
   double S;                            // sum exp(z - m)
   double T;                            // sum exp(z - m) * (z - m)
@@ -107,6 +121,7 @@ struct StepArgs {
   int32_t seg0;              // attend: first segment of the layer (inputs are that layer's)
   int32_t ns;                // split-K attend: workgroups per segment
   int32_t lds_rows;          // staged-row capacity of the LDS planes (LDS variant)
+  int32_t sel_bits_lds;      // HBM-staged variant: 1 when the victim bitmask is in LDS
   const uint16_t* q;         // [L][B][Hq][D] (attend: [B][Hq][D])
   const uint16_t* k_new;     // [L][B][Hkv][D] (attend: [B][Hkv][D])
   const uint16_t* v_new;

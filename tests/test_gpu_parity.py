@@ -113,6 +113,40 @@ def test_every_selection_path_bit_exact():
     assert (e == 1).sum() > 0 and ((e >= 2) & (e <= 8)).sum() > 0 and (e > 8).sum() > 0, np.bincount(e)
 
 
+def test_hbm_staged_selection_paths():
+    # Segments too long for LDS staging (over 4096 rows with 4 planes) select
+    # through a 13-bit key histogram, an LDS victim bitmask and the threshold
+    # bin's candidates ranked among themselves.
+    # Steady steps at a budget above 4096 rows: one victim, 2..8 victims when
+    # the budget drops by 4, none when it rises; every step HBM-staged.
+    e = []
+    run(wl("toy", prefill=5200, n_low=4996, n_high=5000, protect_last=16, fp16_window=32), 24, seed=21,
+        check_every=1, victims=e)
+    e = np.array(e)
+    assert (e == 1).sum() > 0 and ((e >= 2) & (e <= 8)).sum() > 0, np.bincount(e)
+    # A capacity whose bitmask (one bit per stage row) exceeds 32 KiB keeps the
+    # bitmask in the HBM stage instead of LDS.
+    run(wl("toy", prefill=6000), 3, seed=22, capacity=280_000)
+
+
+def test_hbm_staged_selection_overflowing_candidates():
+    # All-zero prefill keys give every prefill row the same attention mass, so
+    # with alpha = 1 (EMA only) ~6000 keys share one score and one histogram
+    # bin: more candidates than the kernel keeps in LDS (2560), which sends
+    # the selection through its radix-select fallback over the staged keys.
+    w = wl("toy", prefill=6000, alpha=1.0)
+    pk, pv = synth.prefill(w, 23, DEV)
+    pk.zero_()
+    S = w["num_layers"] * w["batch"] * w["num_kv_heads"]
+    ls = Lockstep(w, 23, range(S), prefill=(pk, pv))
+    e = []
+    for i in range(3):
+        r = ls.step()
+        e.extend(len(sr.victims) for sr in r["orc"].seg.values())
+    assert max(e) > 5000, e
+    assert ls.gpu.status() == confkv.OK
+
+
 def test_kvpop_variant_closed_form():
     w = wl("kvpop_qwen3_8b", num_layers=1, batch=2, protect_last=32, fp16_window=32, kvpop_k=60)
     ls = run(w, 160, check_every=9)
