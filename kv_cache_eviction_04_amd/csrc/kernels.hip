@@ -182,13 +182,6 @@ struct Stage {
   __device__ __forceinline__ int32_t* list(int plane) const { return reinterpret_cast<int32_t*>(p + plane * rs); }
 };
 
-// A PV tile buffer with the weights of the lane's 8 rows loaded beside it.
-template <class B>
-struct WithW {
-  B b;
-  float4 w0, w1;
-};
-
 // Walks over the staged keys. An HBM-staged key costs a memory round trip, so
 // that instance loads 8 keys of a thread before using them; one at a time, a
 // thread's walk over a 32K-row segment would be some 128 round trips in a
@@ -313,6 +306,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   __shared__ int32_t sh[8];
   __shared__ int32_t sh_out_live, sh_base;
   __shared__ uint32_t sh_cand;  // HBM-staged selection: candidates gathered
+  __shared__ float sh_mrun[G], sh_lrun[G];  // HBM-staged attention: running maxima and sums
   __shared__ uint32_t sel_cnt[4][2];  // per wave: live rows, eligible rows
   __shared__ uint64_t sel_key[4];     // per wave: smallest key
   __shared__ int32_t sel_row[4];      // per wave: its stage row
@@ -396,7 +390,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       const int ix = r < 0 ? i : lay.cap32 + min(r, Wr32 - 1);
       kpos[u] = opos[ix];
       kev[u] = uev[ix];
-      ksv[u] = ovs[min(i, lay.cap32 - 1)];
+      if constexpr (kAtt && kLds) ksv[u] = ovs[min(i, lay.cap32 - 1)];  // V scales: LDS-staged weights only
     }
   };
   // the raw loaded state of stage row i, masked: position (-1: no row), EMA or
@@ -417,6 +411,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   };
   auto row_scale = [&](int i, float sv) { return (i < n_old && par.old_int8 && sv > 0.0f) ? sv : 1.0f; };
   float inv_l[G];  // 1 / sum of p per head (attention)
+  float Mf[G];     // HBM-staged: the final maximum score per head
   float finv = 1.0f;  // 1 / the power-of-two prescale of the PV weights
   if constexpr (!kAtt) {
     if (tid == 0) sh_out_live = 0;
@@ -427,26 +422,121 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     // take d in the order their 16-byte loads deliver it, FP16 tiles in theirs.
     const uint16_t* qrow = a.q + ((size_t)si * G + (lj < G ? lj : 0)) * D;
     half8 qa8[KS], qa16[KS];
+    auto load_q16 = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
-      qa16[kk] = lj < G ? as_h8(u16) : half8{};
-    }
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 u16 = *reinterpret_cast<const uint4*>(qrow + 8 * (lq + 4 * kk));
+        qa16[kk] = lj < G ? as_h8(u16) : half8{};
+      }
+    };
+    auto load_q8 = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
+        qa8[kk] = lj < G ? as_h8(u8) : half8{};
+      }
+    };
+    if constexpr (kLds) load_q16();
 
     // ---- the new row (pos t): its data is loaded now and appended to the ring
     // after the ring QK (below), so these loads do not hold up the first tiles.
+    // (The HBM-staged variant loads it when it appends the row.)
     const uint16_t* kn = a.k_new + (size_t)si * D;
     if (pos_prio >= 0) prio_now = a.prio_new[si];
-    const uint4 kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
-    const uint16_t vn1 = a.v_new[(size_t)si * D + tid % D];
+    uint4 kn4 = uint4{0u, 0u, 0u, 0u};
+    uint16_t vn1 = 0;
+    auto load_new_row = [&]() {
+      kn4 = reinterpret_cast<const uint4*>(kn)[tid % (D / 8)];
+      vn1 = a.v_new[(size_t)si * D + tid % D];
+    };
+    if constexpr (kLds) load_new_row();
     const int32_t pos_prio_slot = pos_prio >= 0 ? rpos[pos_prio % Wr] : -1;
 
+    // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
+    // previous row (pos t - Wr) left the window at the end of the last step.
+    // Nothing reads these stores back before a barrier: the ring QK takes the
+    // new row's K from k_new, and the row-state passes substitute its position,
+    // EMA and (KVpop) the delayed priority.
+    auto append_row = [&]() {
+      if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
+      if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
+      if (tid == 0) {
+        rpos[slot_new] = t;
+        rema[slot_new] = 0.0f;
+        rprio[slot_new] = 0.0f;
+        // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
+        // priority now, as it stops being protected.
+        if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
+        sh_out_live = 0;
+      }
+    };
+
+    // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
+    // with A = w as its fp16 hi and lo parts and B = V from the transposed
+    // tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj]. Waves split the
+    // columns: wave w owns column blocks CBW*w .. CBW*w+CBW-1 and streams every
+    // row, so no cross-wave reduction is needed.
+    // The weights of 8 consecutive rows of head lj (lanes lj < G; zero for the
+    // others), stored as fp16 (hi | lo << 16) pairs, into hi and lo A operands.
+    auto wpack = [&](const float4& p0, const float4& p1, half8& ahi, half8& alo) {
+      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
+                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
+                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
+                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
+      uint4 h, lw;
+      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
+      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
+      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
+      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
+      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
+      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
+      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
+      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
+      ahi = as_h8(h);
+      alo = as_h8(lw);
+    };
+    // V tiles: a lane loads 8 consecutive rows (lane group lq); lanes whose
+    // rows all lie past the region's nvalid rows read lane group 0's (same
+    // lines, no traffic), and their weights are 0.
+    auto vload16 = [&](const uint16_t* vbase, int nvalid, int tt, PV16Buf<CBW>& bf) {
+      const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * (32 * tt + 8 * lq < nvalid ? lane : lj);
+#pragma unroll
+      for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
+    };
+    auto load_pv8 = [&](int tt, PV8Buf& bf) {
+      const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * (32 * tt + 8 * lq < n_old ? lane : lj);
+      if constexpr (CBW == 2) {
+        bf.v = ldnt4(tb + 1024 * wave);
+      } else {
+        const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
+        bf.v = make_uint4(h.x, h.y, 0u, 0u);
+      }
+    };
+    auto mm16 = [&](floatx4(&acc)[CBW], const PV16Buf<CBW>& bf, const half8& ahi, const half8& alo) {
+#pragma unroll
+      for (int k = 0; k < CBW; ++k) {
+        acc[k] = mfma16(ahi, as_h8(bf.v[k]), acc[k]);
+        acc[k] = mfma16(alo, as_h8(bf.v[k]), acc[k]);
+      }
+    };
+    auto mm8 = [&](floatx4(&acc)[CBW], const PV8Buf& bf, const half8& ahi, const half8& alo) {
+      half8 blo, bhi;
+      i8x16_to_h8(bf.v, blo, bhi);
+      acc[0] = mfma16(ahi, blo, acc[0]);
+      acc[0] = mfma16(alo, blo, acc[0]);
+      if constexpr (CBW == 2) {
+        acc[1] = mfma16(ahi, bhi, acc[1]);
+        acc[1] = mfma16(alo, bhi, acc[1]);
+      }
+    };
+    const float sm = par.sm_scale;
+
+    if constexpr (kLds) {
     // ---- QK on MFMA: S[g][row] = sum_d q[g][d] K[row][d] for 16-row tiles;
     // lane (lq, lj) receives S[4*lq + r][row lj]. The ring goes first (its
     // tiles do not depend on the old-region count), then the old region. Each
     // wave takes a contiguous share of the tiles, stages s in LDS and keeps a
     // running max per head.
-    const float sm = par.sm_scale;
     float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float sv_max = 0.0f;
     {
@@ -483,22 +573,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
 #pragma unroll
         for (int g = 0; g < G; ++g) st.at(g, n_old32 + r) = -INFINITY;
     }
-    // ---- append the new row (pos t, ema 0) into ring slot t mod Wr. The slot's
-    // previous row (pos t - Wr) left the window at the end of the last step.
-    // Nothing reads these stores back before a barrier: the ring QK took the
-    // new row's K from k_new, and the row-state passes substitute its position,
-    // EMA and (KVpop) the delayed priority.
-    if (tid < D / 8) reinterpret_cast<uint4*>(rk + (size_t)slot_new * D)[tid] = kn4;
-    if (tid < D) rvt[vt16(slot_new, tid, D)] = vn1;
-    if (tid == 0) {
-      rpos[slot_new] = t;
-      rema[slot_new] = 0.0f;
-      rprio[slot_new] = 0.0f;
-      // [KVpop summary §2.3] delayed scoring: the row at t - w gets its
-      // priority now, as it stops being protected.
-      if (pos_prio >= 0 && pos_prio_slot == pos_prio) rprio[pos_prio % Wr] = prio_now;
-      sh_out_live = 0;
-    }
+    append_row();
 
     // 16-row tiles holding at least one old row; lanes past the last row read
     // the tile's first row, and a trailing tile without rows is not read
@@ -509,11 +584,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     {
       const int ta = (wave * nt_old) >> 2, tb = ((wave + 1) * nt_old) >> 2;
       if (par.old_int8) {
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const uint4 u8 = *reinterpret_cast<const uint4*>(qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1));
-          qa8[kk] = lj < G ? as_h8(u8) : half8{};
-        }
+        load_q8();
         pipelined<CONFKV_QK8_NPB, QK8Buf>(
             ta, tb,
             [&](int tt, QK8Buf& bf) {
@@ -657,122 +728,34 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       if (g < G) il4[r] = 1.0f / (red_l[0][g] + red_l[1][g] + red_l[2][g] + red_l[3][g]);
     }
 
-    // ---- PV on MFMA over 32-row tiles: O[g][col] += sum_row w[g][row] V[row][col]
-    // with A = w as its fp16 hi and lo parts and B = V from the transposed
-    // tiles; lane (lq, lj) receives O[4*lq + r][16*cb + lj]. Waves split the
-    // columns: wave w owns column blocks CBW*w .. CBW*w+CBW-1 and streams every
-    // row, so no cross-wave reduction is needed.
+    // ---- PV from the LDS weights
     floatx4 O[CBW];
 #pragma unroll
     for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    // The weights of 8 consecutive rows of head lj (lanes lj < G; zero for the
-    // others), as fp16 hi and lo A operands.
-    auto wload = [&](int srow, float4& p0, float4& p1) {
+    auto wfrag = [&](int srow, half8& ahi, half8& alo) {
+      float4 p0{0.0f, 0.0f, 0.0f, 0.0f}, p1{0.0f, 0.0f, 0.0f, 0.0f};
       if (lj < G) {
         p0 = st.at4(lj, srow);
         p1 = st.at4(lj, srow + 4);
-      } else {
-        p0 = p1 = float4{0.0f, 0.0f, 0.0f, 0.0f};
       }
+      wpack(p0, p1, ahi, alo);
     };
-    auto wpack = [&](const float4& p0, const float4& p1, half8& ahi, half8& alo) {
-      const uint32_t wd[8] = {__builtin_bit_cast(uint32_t, p0.x), __builtin_bit_cast(uint32_t, p0.y),
-                              __builtin_bit_cast(uint32_t, p0.z), __builtin_bit_cast(uint32_t, p0.w),
-                              __builtin_bit_cast(uint32_t, p1.x), __builtin_bit_cast(uint32_t, p1.y),
-                              __builtin_bit_cast(uint32_t, p1.z), __builtin_bit_cast(uint32_t, p1.w)};
-      uint4 h, lw;
-      h.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u);
-      h.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u);
-      h.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x05040100u);
-      h.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x05040100u);
-      lw.x = __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u);
-      lw.y = __builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u);
-      lw.z = __builtin_amdgcn_perm(wd[5], wd[4], 0x07060302u);
-      lw.w = __builtin_amdgcn_perm(wd[7], wd[6], 0x07060302u);
-      ahi = as_h8(h);
-      alo = as_h8(lw);
-    };
-    // V tiles: a lane loads 8 consecutive rows (lane group lq); lanes whose
-    // rows all lie past the region's nvalid rows read lane group 0's (same
-    // lines, no traffic), and their weights are 0. LDS-staged weights are read
-    // when a tile is computed; HBM-staged ones are loaded with the tile.
     auto pv16 = [&](const uint16_t* vbase, int srow0, int ntiles, int nvalid) {
-      auto vload = [&](int tt, PV16Buf<CBW>& bf) {
-        const uint16_t* tb = vbase + (size_t)tt * 32 * D + 8 * (32 * tt + 8 * lq < nvalid ? lane : lj);
-#pragma unroll
-        for (int k = 0; k < CBW; ++k) bf.v[k] = ldnt4(tb + 512 * (CBW * wave + k));
-      };
-      auto mm = [&](const PV16Buf<CBW>& bf, const half8& ahi, const half8& alo) {
-#pragma unroll
-        for (int k = 0; k < CBW; ++k) {
-          O[k] = mfma16(ahi, as_h8(bf.v[k]), O[k]);
-          O[k] = mfma16(alo, as_h8(bf.v[k]), O[k]);
-        }
-      };
-      if constexpr (kLds) {
-        pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(0, ntiles, vload, [&](int tt, const PV16Buf<CBW>& bf) {
-          float4 p0, p1;
-          half8 ahi, alo;
-          wload(srow0 + 32 * tt + 8 * lq, p0, p1);
-          wpack(p0, p1, ahi, alo);
-          mm(bf, ahi, alo);
-        });
-      } else {
-        pipelined<2, WithW<PV16Buf<CBW>>>(
-            0, ntiles,
-            [&](int tt, WithW<PV16Buf<CBW>>& bf) {
-              vload(tt, bf.b);
-              wload(srow0 + 32 * tt + 8 * lq, bf.w0, bf.w1);
-            },
-            [&](int tt, const WithW<PV16Buf<CBW>>& bf) {
-              half8 ahi, alo;
-              wpack(bf.w0, bf.w1, ahi, alo);
-              mm(bf.b, ahi, alo);
-            });
-      }
+      pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
+          0, ntiles, [&](int tt, PV16Buf<CBW>& bf) { vload16(vbase, nvalid, tt, bf); },
+          [&](int tt, const PV16Buf<CBW>& bf) {
+            half8 ahi, alo;
+            wfrag(srow0 + 32 * tt + 8 * lq, ahi, alo);
+            mm16(O, bf, ahi, alo);
+          });
     };
     const int nv_old = n_old32 >> 5;
-    auto load_pv8 = [&](int tt, PV8Buf& bf) {
-      const uint8_t* tb = ovt + (size_t)tt * 32 * D + 16 * (32 * tt + 8 * lq < n_old ? lane : lj);
-      if constexpr (CBW == 2) {
-        bf.v = ldnt4(tb + 1024 * wave);
-      } else {
-        const uint2 h = ldnt2(tb + 1024 * (wave >> 1) + 8 * (wave & 1));
-        bf.v = make_uint4(h.x, h.y, 0u, 0u);
-      }
-    };
     if (par.old_int8) {
-      auto mm8 = [&](const PV8Buf& bf, const half8& ahi, const half8& alo) {
-        half8 blo, bhi;
-        i8x16_to_h8(bf.v, blo, bhi);
-        O[0] = mfma16(ahi, blo, O[0]);
-        O[0] = mfma16(alo, blo, O[0]);
-        if constexpr (CBW == 2) {
-          O[1] = mfma16(ahi, bhi, O[1]);
-          O[1] = mfma16(alo, bhi, O[1]);
-        }
-      };
-      if constexpr (kLds) {
-        pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, [&](int tt, const PV8Buf& bf) {
-          float4 p0, p1;
-          half8 ahi, alo;
-          wload(32 * tt + 8 * lq, p0, p1);
-          wpack(p0, p1, ahi, alo);
-          mm8(bf, ahi, alo);
-        });
-      } else {
-        pipelined<4, WithW<PV8Buf>>(
-            0, nv_old,
-            [&](int tt, WithW<PV8Buf>& bf) {
-              load_pv8(tt, bf.b);
-              wload(32 * tt + 8 * lq, bf.w0, bf.w1);
-            },
-            [&](int tt, const WithW<PV8Buf>& bf) {
-              half8 ahi, alo;
-              wpack(bf.w0, bf.w1, ahi, alo);
-              mm8(bf.b, ahi, alo);
-            });
-      }
+      pipelined<CONFKV_PV8_NPB, PV8Buf>(0, nv_old, load_pv8, [&](int tt, const PV8Buf& bf) {
+        half8 ahi, alo;
+        wfrag(32 * tt + 8 * lq, ahi, alo);
+        mm8(O, bf, ahi, alo);
+      });
     } else {
       pv16(reinterpret_cast<const uint16_t*>(ovt), 0, nv_old, n_old);
     }
@@ -792,7 +775,273 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
 #pragma unroll
       for (int g = 0; g < G; ++g) lay.rec_lse[(size_t)seg * G + g] = M[g] + logf(Lsum[g]);
     }
-
+    } else {
+    // ---- Segments too long for LDS staging stream through LDS in chunks of
+    // CH rows: the old region's, then (after the new row is appended) the
+    // ring's. Per chunk: QK on MFMA (scores into the LDS chunk, and into the
+    // HBM stage for the key pass), the chunk's per-head maxima, the weights
+    // p = exp(s - M) against the running maxima M, with the row's V scale and
+    // a power-of-two prescale folded in, packed in place as fp16 hi/lo pairs,
+    // and PV on MFMA from them. Online softmax: a chunk that raises a head's
+    // maximum rescales that head's running sum and output rows by
+    // exp(M_old - M_new). The output accumulates in units of the current
+    // chunk's prescale: a new prescale rescales it by the ratio of the two
+    // (a power of two, exact). The running maxima and sums, the same in every
+    // thread, are kept in LDS (sh_mrun, sh_lrun).
+    constexpr int CH = hbm_chunk_rows(G);
+    float* const cs = dyn_lds;            // [G][CH] scores, then weights
+    float* const cvs = dyn_lds + G * CH;  // [CH] V scale of each INT8 row (1 for the others)
+    if (tid < G) {
+      sh_mrun[tid] = -INFINITY;
+      sh_lrun[tid] = 0.0f;
+    }
+    int fexp_run = 0;  // prescale exponent the output is held in
+    floatx4 O[CBW];
+#pragma unroll
+    for (int k = 0; k < CBW; ++k) O[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    // stage rows [c0, c1) (multiples of 32) of the ring (slot r = row - n_old32) or of the old region
+    auto run_chunk = [&](const bool ring, const int c0, const int c1) {
+      const bool int8 = !ring && par.old_int8;
+      // q in the order this region's K tiles deliver d, loaded per chunk (a
+      // cache hit) so that no operand set stays live through the PV
+      half8 qa[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint16_t* qp = int8 ? qrow + 16 * (lq + 4 * (kk >> 1)) + 8 * (kk & 1) : qrow + 8 * (lq + 4 * kk);
+        const uint4 u = *reinterpret_cast<const uint4*>(qp);
+        qa[kk] = lj < G ? as_h8(u) : half8{};
+      }
+      const int vend = ring ? min(c1, n_old32 + Wr) : min(c1, n_old);  // past the chunk's last row
+      // 16-row tiles holding a row; the chunk's rows past them score -inf
+      const int t0 = c0 >> 4, t1 = max(t0, (vend + 15) >> 4);
+      for (int i = 16 * t1 + tid; i < c1; i += kThreads) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) cs[g * CH + i - c0] = -INFINITY;
+        cvs[i - c0] = 1.0f;
+      }
+      float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      float sv_max = 0.0f;
+      auto put = [&](const floatx4& acc, int row, bool valid, float f) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int g = 4 * lq + r;
+          if (g < G) {
+            const float sc = valid ? acc[r] * f : -INFINITY;
+            cs[g * CH + row - c0] = sc;
+            st.at(g, row) = sc;
+            mrun[r] = fmaxf(mrun[r], sc);
+          }
+        }
+      };
+      const int nt = t1 - t0;
+      const int ta = t0 + ((wave * nt) >> 2), tb = t0 + (((wave + 1) * nt) >> 2);
+      if (ring) {
+        pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+            ta, tb,
+            [&](int tt, QK16Buf<KS>& bf) {
+              const int r = 16 * tt + lj - n_old32;
+              // lanes past the last slot read the tile's first slot (same lines, no traffic)
+              const uint16_t* kr = r == slot_new ? kn : rk + (size_t)(r < Wr ? r : 16 * tt - n_old32) * D;
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+              bf.pr = rpos[r];
+            },
+            [&](int tt, const QK16Buf<KS>& bf) {
+              floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[kk], as_h8(bf.kc[kk]), acc);
+              const int r = 16 * tt + lj - n_old32;
+              put(acc, 16 * tt + lj, r < Wr && (bf.pr >= 0 || r == slot_new), sm);
+            });
+      } else if (int8) {
+        pipelined<CONFKV_QK8_NPB, QK8Buf>(
+            ta, tb,
+            [&](int tt, QK8Buf& bf) {
+              const int row = 16 * tt + lj, rl = row < n_old ? row : 16 * tt;
+              const uint8_t* kr = okp + (size_t)rl * D;
+              bf.k0 = ldnt4(kr + 16 * lq);
+              if constexpr (D == 128) bf.k1 = ldnt4(kr + 16 * (lq + 4));
+              bf.sk = oks[rl];
+              bf.sv = ovs[rl];
+            },
+            [&](int tt, const QK8Buf& bf) {
+              half8 b0, b1;
+              floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+              i8x16_to_h8(bf.k0, b0, b1);
+              acc = mfma16(qa[0], b0, acc);
+              acc = mfma16(qa[1], b1, acc);
+              if constexpr (D == 128) {
+                half8 b2, b3;
+                i8x16_to_h8(bf.k1, b2, b3);
+                acc = mfma16(qa[2], b2, acc);
+                acc = mfma16(qa[3], b3, acc);
+              }
+              const int row = 16 * tt + lj;
+              const bool valid = row < n_old;
+              sv_max = fmaxf(sv_max, valid ? bf.sv : 0.0f);
+              if (lq == 0) cvs[row - c0] = (valid && bf.sv > 0.0f) ? bf.sv : 1.0f;
+              put(acc, row, valid, bf.sk * sm);
+            });
+      } else {
+        pipelined<CONFKV_QK16_NPB, QK16Buf<KS>>(
+            ta, tb,
+            [&](int tt, QK16Buf<KS>& bf) {
+              const int row = 16 * tt + lj, rl = row < n_old ? row : 16 * tt;
+              const uint16_t* kr = reinterpret_cast<const uint16_t*>(okp) + (size_t)rl * D;
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) bf.kc[kk] = ldnt4(kr + 8 * (lq + 4 * kk));
+            },
+            [&](int tt, const QK16Buf<KS>& bf) {
+              floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) acc = mfma16(qa[kk], as_h8(bf.kc[kk]), acc);
+              const int row = 16 * tt + lj;
+              put(acc, row, row < n_old, sm);
+            });
+      }
+      // the chunk's maxima, the new running maxima and the rescale factors
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = row16_reduce(mrun[r], [](float x, float y) { return fmaxf(x, y); });
+        const int g = 4 * lq + r;
+        if (lj == 0 && g < G) red_m[wave][g] = m;
+      }
+      sv_max = wave_max(sv_max);
+      if (lane == 0) red_u[wave] = __builtin_bit_cast(uint32_t, sv_max);
+      __syncthreads();
+      float Mn[G], corr[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mc = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
+        const float mo = sh_mrun[g];
+        Mn[g] = fmaxf(mo, mc);
+        corr[g] = Mn[g] == -INFINITY ? 1.0f : __expf(mo - Mn[g]);
+      }
+      float svm = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) svm = fmaxf(svm, __builtin_bit_cast(float, red_u[w]));
+      // prescale keeping p*sV*f below 2^14 (fp16 range) while lifting small
+      // weights out of the fp16 subnormals
+      int fexp = 10;
+      if (svm > 0.0f) {
+        int e2;
+        frexpf(svm, &e2);
+        fexp = min(10, max(-30, 14 - e2));
+      }
+      const float fsc = ldexpf(1.0f, fexp), fratio = ldexpf(1.0f, fexp - fexp_run);
+      fexp_run = fexp;
+      // weights of the chunk's rows, in place
+      float lpart[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
+      for (int i = c0 + tid; i < c1; i += kThreads) {
+        const int ii = i - c0;
+        const float scf = (int8 ? cvs[ii] : 1.0f) * fsc;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = Mn[g] == -INFINITY ? 0.0f : __expf(cs[g * CH + ii] - Mn[g]);
+          lpart[g] += p;
+          const float wv = p * scf;
+          const _Float16 hi = (_Float16)wv, lo = (_Float16)(wv - (float)hi);
+          cs[g * CH + ii] = __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                                                          ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16));
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float v = wave_sum(lpart[g]);
+        if (lane == 0) red_l[wave][g] = v;
+      }
+      __syncthreads();
+      if (tid < G) {
+        float c = 1.0f, m = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (g == tid) {
+            c = corr[g];
+            m = Mn[g];
+          }
+        sh_lrun[tid] = sh_lrun[tid] * c + ((red_l[0][tid] + red_l[1][tid]) + (red_l[2][tid] + red_l[3][tid]));
+        sh_mrun[tid] = m;
+      }
+      // the output rows 4*lq + r (a lane-dependent head) to the new maxima and prescale
+      float c4[4] = {fratio, fratio, fratio, fratio};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (g == 4 * lq + r) c4[r] = corr[g] * fratio;
+#pragma unroll
+      for (int k = 0; k < CBW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[k][r] *= c4[r];
+      auto wfrag = [&](int wl, half8& ahi, half8& alo) {  // chunk row wl
+        float4 p0{0.0f, 0.0f, 0.0f, 0.0f}, p1{0.0f, 0.0f, 0.0f, 0.0f};
+        if (lj < G) {
+          p0 = *reinterpret_cast<const float4*>(cs + lj * CH + wl);
+          p1 = *reinterpret_cast<const float4*>(cs + lj * CH + wl + 4);
+        }
+        wpack(p0, p1, ahi, alo);
+      };
+      if (ring) {
+        const int rt0 = (c0 - n_old32) >> 5, rt1 = min((c1 - n_old32) >> 5, (Wr + 31) >> 5);
+        pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
+            rt0, rt1, [&](int tt, PV16Buf<CBW>& bf) { vload16(rvt, Wr, tt, bf); },
+            [&](int tt, const PV16Buf<CBW>& bf) {
+              half8 ahi, alo;
+              wfrag(n_old32 + 32 * tt + 8 * lq - c0, ahi, alo);
+              mm16(O, bf, ahi, alo);
+            });
+      } else if (int8) {
+        pipelined<CONFKV_PV8_NPB, PV8Buf>(c0 >> 5, c1 >> 5, load_pv8, [&](int tt, const PV8Buf& bf) {
+          half8 ahi, alo;
+          wfrag(32 * tt + 8 * lq - c0, ahi, alo);
+          mm8(O, bf, ahi, alo);
+        });
+      } else {
+        const uint16_t* ov16 = reinterpret_cast<const uint16_t*>(ovt);
+        pipelined<CONFKV_PV16_NPB, PV16Buf<CBW>>(
+            c0 >> 5, c1 >> 5, [&](int tt, PV16Buf<CBW>& bf) { vload16(ov16, n_old, tt, bf); },
+            [&](int tt, const PV16Buf<CBW>& bf) {
+              half8 ahi, alo;
+              wfrag(32 * tt + 8 * lq - c0, ahi, alo);
+              mm16(O, bf, ahi, alo);
+            });
+      }
+      __syncthreads();  // every wave has read the chunk's LDS before the next chunk writes it
+    };
+    for (int c0 = 0; c0 < n_old32; c0 += CH) run_chunk(false, c0, min(c0 + CH, n_old32));
+    load_new_row();
+    append_row();
+    for (int c0 = n_old32; c0 < rows; c0 += CH) run_chunk(true, c0, min(c0 + CH, rows));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      Mf[g] = sh_mrun[g];
+      inv_l[g] = 1.0f / sh_lrun[g];
+    }
+    const float fiv = ldexpf(1.0f, -fexp_run);
+    float il4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (g == 4 * lq + r) il4[r] = inv_l[g];
+#pragma unroll
+    for (int k = 0; k < CBW; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * lq + r;
+        if (g < G) {
+          const int col = 16 * (CBW * wave + k) + lj;
+          a.out[((size_t)si * G + g) * D + col] = f2h(O[k][r] * fiv * il4[r]);
+        }
+      }
+    }
+    if (par.record && tid == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) lay.rec_lse[(size_t)seg * G + g] = Mf[g] + logf(sh_lrun[g]);
+    }
+    }
   }  // attention
 
   // An attend launch under KVpop has no per-row pass left: the priorities
@@ -803,8 +1052,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       return;
     }
   }
-  // the row pass starts from the first rows again (an evict launch loads them here first)
-  if (MODE == kModeEvict || rows > kThreads * KB) {
+  // the row pass starts from the first rows again (an evict launch, and the
+  // HBM-staged attention, which has no weight pass over them, load them here first)
+  if (MODE == kModeEvict || !kLds || rows > kThreads * KB) {
     int i0 = tid;
     asm volatile("" : "+v"(i0));  // recompute the addresses rather than keep them live
     load_rows(i0);
@@ -861,16 +1111,22 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
           if (!kvpop) {
             float e = ev_u;
             if constexpr (kAtt) {
-              const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
               float mass = 0.0f;
+              if constexpr (kLds) {
+                const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
 #pragma unroll
-              for (int g = 0; g < G; ++g) {
-                const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
-                const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
-                                 (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
-                mass = fmaf(wv, inv_l[g], mass);
+                for (int g = 0; g < G; ++g) {
+                  const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
+                  const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
+                                   (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+                  mass = fmaf(wv, inv_l[g], mass);
+                }
+                mass *= inv_scf * (1.0f / (float)G);
+              } else {  // from the raw scores in the HBM stage
+#pragma unroll
+                for (int g = 0; g < G; ++g) mass = fmaf(__expf(st.at(g, i) - Mf[g]), inv_l[g], mass);
+                mass *= 1.0f / (float)G;
               }
-              mass *= inv_scf * (1.0f / (float)G);
               e = par.beta * ev_u + (1.0f - par.beta) * mass;
               oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
             }
@@ -1546,7 +1802,7 @@ static void launch_fused_dg(const Layout& lay, const Params& par, const StepArgs
     hipLaunchKernelGGL((fused_step_kernel<D, G, true, MODE>), dim3(grid), dim3(kThreads), lds_bytes, s, lay, par, a);
   else
     hipLaunchKernelGGL((fused_step_kernel<D, G, false, MODE>), dim3(grid), dim3(kThreads),
-                       MODE == kModeAttend ? 0 : lds_bytes, s, lay, par, a);
+                       MODE == kModeAttend ? kSelLdsBytes : lds_bytes, s, lay, par, a);
 }
 
 template <int D, int MODE>

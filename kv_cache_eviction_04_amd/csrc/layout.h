@@ -46,6 +46,9 @@ constexpr int kSelBitsLdsMax = 32 * 1024;
 static_assert(kSelCandCap * 12 <= kSelLdsBytes, "the candidates reuse the histogram's LDS");
 // victim bitmask words for a stage-row count: whole 64-row groups
 inline constexpr int64_t sel_bits_words(int64_t rows) { return ((rows + 63) / 64) * 2; }
+// Attention of the HBM-staged instance: rows per LDS chunk (a multiple of 32)
+// for G score planes and one V-scale plane within kSelLdsBytes.
+inline constexpr int hbm_chunk_rows(int G) { return (kSelLdsBytes / (4 * (G + 1))) & ~31; }
 
 struct ConfPartial {                   // one logits chunk: m = top1
   double S;                            // sum exp(z - m)
