@@ -1430,7 +1430,9 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   } else if (rem > 1) {
     int32_t* holes = st.list(2);
     int32_t* srcs = st.list(3);
-    uint32_t nh;
+    uint32_t nh, kt = 0;        // rows and whole tiles to move
+    int32_t* tdst = nullptr;    // tiles of holes (HBM-staged variant)
+    int32_t* tsrc = nullptr;    // tiles of sources
     if constexpr (kLds) {
       // victim predicate for the hole fill: vmin is not a hole when it takes the aged-out row
       auto hole = [&](int i, uint64_t k) { return k <= T && !(into_hole && i == vmin); };
@@ -1454,58 +1456,203 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
         so += to_src ? 1u : 0u;
       });
     } else {
-      // From the bitmask: a thread takes whole words of consecutive rows.
-      // Holes are the victims below m (vmin excepted when it takes the
-      // aged-out row), sources the survivors at or above m.
+      // From the bitmask, whose words are the 32-row tiles: a thread takes
+      // whole words of consecutive rows. Holes are the victims below m (vmin
+      // excepted when it takes the aged-out row), sources the survivors at or
+      // above m. The old region keeps no row order, so any pairing of holes
+      // with sources will do: a tile of 32 holes is filled from a tile of 32
+      // sources as a whole (such tiles paired in ascending order; the copy is
+      // contiguous K rows, one V tile and the row state), and the remaining
+      // holes and sources pair row by row in ascending order.
       const int per = (((n_old + kThreads - 1) / kThreads) + 31) & ~31;
       const int lo = min(n_old, tid * per), hi = min(n_old, lo + per);
+      // this thread's words [w0, w1): none when its range is empty
+      const int w0 = lo >> 5, w1 = lo < hi ? (hi + 31) >> 5 : w0;
       auto hole_src = [&](int w, uint32_t& hw, uint32_t& sw) {
         const uint32_t bw = vbits[w], in = bits_below(hi - 32 * w), lt_m = bits_below(m - 32 * w);
         hw = bw & in & lt_m;
         if (into_hole && (vmin >> 5) == w) hw &= ~(1u << (vmin & 31));
         sw = ~bw & in & ~lt_m;
       };
-      uint32_t hv = 0, sv = 0;
-      for (int w = lo >> 5; 32 * w < hi; ++w) {
+      auto hole_tile = [&](uint32_t hw, int w) { return hw == ~0u && 32 * w + 32 <= m; };
+      auto src_tile = [&](uint32_t sw, int w) { return sw == ~0u && 32 * w >= m; };
+      uint32_t fh = 0, fs = 0;
+      for (int w = w0; w < w1; ++w) {
         uint32_t hw, sw;
         hole_src(w, hw, sw);
-        hv += (uint32_t)__popc(hw);
-        sv += (uint32_t)__popc(sw);
+        fh += hole_tile(hw, w) ? 1u : 0u;
+        fs += src_tile(sw, w) ? 1u : 0u;
+      }
+      uint32_t nfh, nfs;
+      const uint32_t fho = block_excl_scan_u32(fh, red_u, &nfh);
+      const uint32_t fso = block_excl_scan_u32(fs, red_u, &nfs);
+      kt = min(nfh, nfs);
+      // rows outside the paired tiles
+      uint32_t hv = 0, sv = 0;
+      {
+        uint32_t a = fho, b = fso;
+        for (int w = w0; w < w1; ++w) {
+          uint32_t hw, sw;
+          hole_src(w, hw, sw);
+          if (hole_tile(hw, w) && a++ < kt) hw = 0u;
+          if (src_tile(sw, w) && b++ < kt) sw = 0u;
+          hv += (uint32_t)__popc(hw);
+          sv += (uint32_t)__popc(sw);
+        }
       }
       uint32_t ns;
       uint32_t ho = block_excl_scan_u32(hv, red_u, &nh);
       uint32_t so = block_excl_scan_u32(sv, red_u, &ns);
-      for (int w = lo >> 5; 32 * w < hi; ++w) {
-        uint32_t hw, sw;
-        hole_src(w, hw, sw);
-        for (; hw; hw &= hw - 1u) holes[ho++] = 32 * w + __ffs(hw) - 1;
-        for (; sw; sw &= sw - 1u) srcs[so++] = 32 * w + __ffs(sw) - 1;
+      // row lists, then the tile lists, in the LDS the selection used when they fit
+      if (8 * (nh + kt) <= (uint32_t)kSelLdsBytes) {
+        holes = reinterpret_cast<int32_t*>(dyn_lds);
+        srcs = holes + nh;
+        tdst = srcs + nh;
+        tsrc = tdst + kt;
+      } else {
+        tdst = holes + nh;
+        tsrc = srcs + nh;
+      }
+      {
+        uint32_t a = fho, b = fso;
+        for (int w = w0; w < w1; ++w) {
+          uint32_t hw, sw;
+          hole_src(w, hw, sw);
+          if (hole_tile(hw, w)) {
+            if (a < kt) {
+              tdst[a] = w;
+              hw = 0u;
+            }
+            ++a;
+          }
+          if (src_tile(sw, w)) {
+            if (b < kt) {
+              tsrc[b] = w;
+              sw = 0u;
+            }
+            ++b;
+          }
+          for (; hw; hw &= hw - 1u) holes[ho++] = 32 * w + __ffs(hw) - 1;
+          for (; sw; sw &= sw - 1u) srcs[so++] = 32 * w + __ffs(sw) - 1;
+        }
       }
     }
     __syncthreads();
-    moved = nh;
-    for (int r = rg; r < (int)nh; r += RPB) {
-      const int src = srcs[r], dst = holes[r];
-      const size_t rb = (size_t)D * ob;
-      const int cbytes = 16 * ob;  // bytes per lane
-      for (int off = 0; off < cbytes; off += 16)
-        *reinterpret_cast<uint4*>(okp + dst * rb + c * cbytes + off) =
-            *reinterpret_cast<const uint4*>(okp + src * rb + c * cbytes + off);
+    moved = nh + 32 * kt;
+    // whole tiles: each thread copies 16-byte units of the K rows and of the
+    // V tile, and one row-state value; four tiles per iteration, every load
+    // before any store
+    if constexpr (!kLds) {
+      const int units = 2 * D * ob;  // 16-byte units in a tile's K rows (as in its V tile)
+      constexpr int TU = 4;
+      for (int i0 = 0; i0 < (int)kt; i0 += TU) {
+        uint4 kv[TU][4];
+        uint32_t sv4[TU];
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+          const int i = min(i0 + u, (int)kt - 1);  // past the list: the last pair again
+          const size_t sb = (size_t)tsrc[i] * units;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = tid + kThreads * h;
+            kv[u][2 * h] = kv[u][2 * h + 1] = uint4{0u, 0u, 0u, 0u};
+            if (j < units) {
+              kv[u][2 * h] = reinterpret_cast<const uint4*>(okp)[sb + j];
+              kv[u][2 * h + 1] = reinterpret_cast<const uint4*>(ovt)[sb + j];
+            }
+          }
+          const int r = 32 * tsrc[i] + (tid & 31), f = tid >> 5;  // row state: 5 arrays x 32 rows
+          sv4[u] = 0u;
+          if (f < 5) {
+            const uint32_t* arr = f == 0 ? reinterpret_cast<const uint32_t*>(opos)
+                                : f == 1 ? reinterpret_cast<const uint32_t*>(oema)
+                                : f == 2 ? reinterpret_cast<const uint32_t*>(oprio)
+                                : f == 3 ? reinterpret_cast<const uint32_t*>(oks)
+                                         : reinterpret_cast<const uint32_t*>(ovs);
+            sv4[u] = arr[r];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+          if (i0 + u < (int)kt) {
+            const size_t db = (size_t)tdst[i0 + u] * units;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int j = tid + kThreads * h;
+              if (j < units) {
+                reinterpret_cast<uint4*>(okp)[db + j] = kv[u][2 * h];
+                reinterpret_cast<uint4*>(ovt)[db + j] = kv[u][2 * h + 1];
+              }
+            }
+            const int r = 32 * tdst[i0 + u] + (tid & 31), f = tid >> 5;
+            if (f < 5) {
+              uint32_t* arr = f == 0 ? reinterpret_cast<uint32_t*>(opos)
+                            : f == 1 ? reinterpret_cast<uint32_t*>(oema)
+                            : f == 2 ? reinterpret_cast<uint32_t*>(oprio)
+                            : f == 3 ? reinterpret_cast<uint32_t*>(oks)
+                                     : reinterpret_cast<uint32_t*>(ovs);
+              arr[r] = sv4[u];
+            }
+          }
+        }
+      }
+    }
+    // A lane group moves two rows per iteration and issues every load of both
+    // before any store (a source is never a hole, so nothing overlaps).
+    const size_t rb = (size_t)D * ob;
+    const int cbytes = 16 * ob;  // bytes of a K row per lane
+    uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
+    struct MoveRow {
+      uint4 k0, k1;
+      uint32_t v[16];
+      int32_t p;
+      float f[4];
+    };
+    auto load_row = [&](int sr, MoveRow& m) __attribute__((always_inline)) {
+      m.k0 = *reinterpret_cast<const uint4*>(okp + sr * rb + c * cbytes);
+      m.k1 = uint4{0u, 0u, 0u, 0u};
+      if (ob == 2) m.k1 = *reinterpret_cast<const uint4*>(okp + sr * rb + c * cbytes + 16);
       if (ob == 1) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) ovt[vt8(dst, 16 * c + jj, D)] = ovt[vt8(src, 16 * c + jj, D)];
+        for (int jj = 0; jj < 16; ++jj) m.v[jj] = ovt[vt8(sr, 16 * c + jj, D)];
       } else {
-        uint16_t* v16 = reinterpret_cast<uint16_t*>(ovt);
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) v16[vt16(dst, 16 * c + jj, D)] = v16[vt16(src, 16 * c + jj, D)];
+        for (int jj = 0; jj < 16; ++jj) m.v[jj] = v16[vt16(sr, 16 * c + jj, D)];
+      }
+      m.p = opos[sr];
+      m.f[0] = oema[sr];
+      m.f[1] = oprio[sr];
+      m.f[2] = oks[sr];
+      m.f[3] = ovs[sr];
+    };
+    auto store_row = [&](int dr, const MoveRow& m) __attribute__((always_inline)) {
+      *reinterpret_cast<uint4*>(okp + dr * rb + c * cbytes) = m.k0;
+      if (ob == 2) *reinterpret_cast<uint4*>(okp + dr * rb + c * cbytes + 16) = m.k1;
+      if (ob == 1) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) ovt[vt8(dr, 16 * c + jj, D)] = (uint8_t)m.v[jj];
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) v16[vt16(dr, 16 * c + jj, D)] = (uint16_t)m.v[jj];
       }
       if (c == 0) {
-        opos[dst] = opos[src];
-        oema[dst] = oema[src];
-        oprio[dst] = oprio[src];
-        oks[dst] = oks[src];
-        ovs[dst] = ovs[src];
+        opos[dr] = m.p;
+        oema[dr] = m.f[0];
+        oprio[dr] = m.f[1];
+        oks[dr] = m.f[2];
+        ovs[dr] = m.f[3];
       }
+    };
+    for (int r0 = rg; r0 < (int)nh; r0 += 2 * RPB) {
+      const int r1 = r0 + RPB;
+      const bool two = r1 < (int)nh;
+      const int s0 = srcs[r0], d0 = holes[r0];
+      const int s1 = two ? srcs[r1] : s0, d1 = two ? holes[r1] : d0;  // no second row: reload the first
+      MoveRow m0, m1;
+      load_row(s0, m0);
+      load_row(s1, m1);
+      store_row(d0, m0);
+      store_row(d1, m1);  // without a second row: the first row's values again
     }
   }
   if (e == 1) {
