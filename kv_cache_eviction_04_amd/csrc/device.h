@@ -286,6 +286,9 @@ typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 #ifndef CONFKV_KB_WIDE
 #define CONFKV_KB_WIDE 6   // the same for larger groups, which have fewer registers left
 #endif
+#ifndef CONFKV_KB_HBM
+#define CONFKV_KB_HBM 6    // the same for HBM-staged segments, whose batches also hold the
+#endif                     // rows' scores and their results until the next batch is loaded
 #ifndef CONFKV_OCC
 #define CONFKV_OCC 4       // waves per SIMD the fused kernel is compiled for (G <= 5; a few
                            // spills at G = 5 cost less than a fourth of the occupancy)

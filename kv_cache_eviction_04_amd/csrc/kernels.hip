@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   constexpr int NP16 = 2;              // 16-row FP16 K tiles in flight per wave
   constexpr int NV8 = 8;               // 32-row INT8 V tiles in flight per wave
   constexpr int NV16 = 4;              // 32-row FP16 V tiles in flight per wave
-  constexpr int KB = G <= 4 ? CONFKV_KB : CONFKV_KB_WIDE;  // rows per thread in flight in the key phase
+  constexpr int KB = !kLds ? CONFKV_KB_HBM : (G <= 4 ? CONFKV_KB : CONFKV_KB_WIDE);  // rows per thread in flight in the key phase
   static_assert(LPR == 4 || LPR == 8, "head_dim 64 or 128");
   static_assert(G <= 16, "a GQA group fits one MFMA tile");
 
@@ -391,6 +391,20 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
       kpos[u] = opos[ix];
       kev[u] = uev[ix];
       if constexpr (kAtt && kLds) ksv[u] = ovs[min(i, lay.cap32 - 1)];  // V scales: LDS-staged weights only
+    }
+  };
+  // HBM-staged attention: the raw scores of the same rows, for their mass
+  float ksc[kLds ? 1 : KB][G];
+  auto load_scores = [&](int i0) {
+    if constexpr (!kLds && kAtt) {
+      const int wrow0 = i0 - tid + 64 * wave;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (wrow0 + kThreads * u >= rows) break;
+        const int i = min(i0 + kThreads * u, rows - 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) ksc[u][g] = st.at(g, i);
+      }
     }
   };
   // the raw loaded state of stage row i, masked: position (-1: no row), EMA or
@@ -1058,6 +1072,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     int i0 = tid;
     asm volatile("" : "+v"(i0));  // recompute the addresses rather than keep them live
     load_rows(i0);
+    load_scores(i0);
   }
   // prefetch of the row that may leave the FP16 window at the end of the step
   // (16 consecutive elements of K or V per lane for lanes 0 .. 2*LPR-1)
@@ -1095,73 +1110,115 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
   // random ranker: this step's and segment's generator state; a row's rank
   // is the top 24 bits of out(k2, pos + 1) times 2^-24
   const uint64_t rnd_k2 = splitmix64_out(splitmix64_out(par.seed, (uint64_t)t + 1), (uint64_t)seg + 1);
-  for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
-    if (i0 != tid) load_rows(i0);
+  // one row: its state, EMA (to store when est), score and key
+  auto key_row = [&](int i, int u, int32_t& pos, float& e_out, bool& est, float& score, uint64_t& key) {
+    key = ~0ull;
+    score = NAN;
+    est = false;
+    e_out = 0.0f;
+    float ev_u;
+    row_state(i, kpos[u], kev[u], pos, ev_u);
+    if (pos >= 0) {
+      ++n_live;
+      if (!kvpop) {
+        float e = ev_u;
+        if constexpr (kAtt) {
+          float mass = 0.0f;
+          if constexpr (kLds) {
+            const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int i = i0 + kThreads * u;
-      if (i < rows) {
-        uint64_t key = ~0ull;
-        float score = NAN;
-        int32_t pos;
-        float ev_u;
-        row_state(i, kpos[u], kev[u], pos, ev_u);
-        if (pos >= 0) {
-          ++n_live;
-          if (!kvpop) {
-            float e = ev_u;
-            if constexpr (kAtt) {
-              float mass = 0.0f;
-              if constexpr (kLds) {
-                const float inv_scf = __builtin_amdgcn_rcpf(row_scale(i, ksv[u])) * finv;
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                  const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
-                  const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
-                                   (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
-                  mass = fmaf(wv, inv_l[g], mass);
-                }
-                mass *= inv_scf * (1.0f / (float)G);
-              } else {  // from the raw scores in the HBM stage
-#pragma unroll
-                for (int g = 0; g < G; ++g) mass = fmaf(__expf(st.at(g, i) - Mf[g]), inv_l[g], mass);
-                mass *= 1.0f / (float)G;
-              }
-              e = par.beta * ev_u + (1.0f - par.beta) * mass;
-              oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
+            for (int g = 0; g < G; ++g) {
+              const uint32_t wd = __builtin_bit_cast(uint32_t, st.at(g, i));
+              const float wv = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu)) +
+                               (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+              mass = fmaf(wv, inv_l[g], mass);
             }
-            if (par.ranker == 0) {
-              const float rec = (float)(pos + 1) * inv_t1;
-              score = par.alpha * e + (1.0f - par.alpha) * rec;
-            } else {
-              score = (float)(uint32_t)(splitmix64_out(rnd_k2, (uint64_t)pos + 1) >> 40) * 0x1p-24f;
-            }
-          } else {
-            score = ev_u;
+            mass *= inv_scf * (1.0f / (float)G);
+          } else {  // from the raw scores in the HBM stage
+#pragma unroll
+            for (int g = 0; g < G; ++g) mass = fmaf(__expf(ksc[u][g] - Mf[g]), inv_l[g], mass);
+            mass *= 1.0f / (float)G;
           }
-          if constexpr (kEv) {
-            const bool elig = pos >= par.s && pos <= t - par.P;
-            if (!isfinite(score)) {
-              atomicOr(lay.err, kErrNonFinite);
-            } else if (elig) {
-              key = rank_key(score, pos);
-              ++n_elig;
-              if (key < kmin) {
-                kmin = key;
-                imin = i;
-              }
-            }
-            if (pos == pos_out && i >= n_old32) sh_out_live = 1;
+          e = par.beta * ev_u + (1.0f - par.beta) * mass;
+          e_out = e;
+          est = true;
+        }
+        if (par.ranker == 0) {
+          const float rec = (float)(pos + 1) * inv_t1;
+          score = par.alpha * e + (1.0f - par.alpha) * rec;
+        } else {
+          score = (float)(uint32_t)(splitmix64_out(rnd_k2, (uint64_t)pos + 1) >> 40) * 0x1p-24f;
+        }
+      } else {
+        score = ev_u;
+      }
+      if constexpr (kEv) {
+        const bool elig = pos >= par.s && pos <= t - par.P;
+        if (!isfinite(score)) {
+          atomicOr(lay.err, kErrNonFinite);
+        } else if (elig) {
+          key = rank_key(score, pos);
+          ++n_elig;
+          if (key < kmin) {
+            kmin = key;
+            imin = i;
           }
         }
-        if constexpr (kEv) {
-          st.set_key(i, key);
-          if constexpr (!kLds) hist_add(hsel, (uint32_t)(key >> (64 - kSelBinBits)));
-          if (par.record) {
-            lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
-            lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
-          }
+        if (pos == pos_out && i >= n_old32) sh_out_live = 1;
+      }
+    }
+  };
+  auto store_row = [&](int i, int32_t pos, float e, bool est, float score, uint64_t key) {
+    if constexpr (kAtt) {
+      if (est) oema[i < n_old32 ? i : lay.cap32 + (i - n_old32)] = e;  // unified row-state index
+    }
+    if constexpr (kEv) {
+      st.set_key(i, key);
+      if constexpr (!kLds) hist_add(hsel, (uint32_t)(key >> (64 - kSelBinBits)));
+      if (par.record) {
+        lay.rec_pos[(size_t)seg * lay.rows_max + i] = pos;
+        lay.rec_score[(size_t)seg * lay.rows_max + i] = pos >= 0 ? score : NAN;
+      }
+    }
+  };
+  if constexpr (kLds) {
+    for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
+      if (i0 != tid) load_rows(i0);
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + kThreads * u;
+        if (i < rows) {
+          int32_t pos;
+          float e, score;
+          bool est;
+          uint64_t key;
+          key_row(i, u, pos, e, est, score, key);
+          store_row(i, pos, e, est, score, key);
         }
+      }
+    }
+  } else {
+    // A batch's results wait in registers while the next batch's loads are
+    // issued, and are stored after them: loads and stores share one counter,
+    // so loads issued after the stores would wait for those stores too.
+    for (int i0 = tid; i0 < rows; i0 += kThreads * KB) {
+      int32_t pos[KB];
+      float e[KB], score[KB];
+      bool est[KB];
+      uint64_t key[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + kThreads * u;
+        if (i < rows) key_row(i, u, pos[u], e[u], est[u], score[u], key[u]);
+      }
+      if (i0 + kThreads * KB < rows) {
+        load_rows(i0 + kThreads * KB);
+        load_scores(i0 + kThreads * KB);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + kThreads * u;
+        if (i < rows) store_row(i, pos[u], e[u], est[u], score[u], key[u]);
       }
     }
   }
