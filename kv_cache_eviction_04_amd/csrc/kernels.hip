@@ -1320,9 +1320,10 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     int32_t* crow = reinterpret_cast<int32_t*>(ckey + kSelCandCap);
     // One pass over the keys' high words: rows of lower bins are victims
     // (a wave stores the bitmask words of its 64 consecutive rows); the keys
-    // of bin tb are gathered as candidates while there is room.
+    // of bin tb are gathered as candidates while there is room (their low
+    // words are loaded after the pass, all at once).
     {
-      constexpr int U = 8;
+      constexpr int U = 16;
       const int wrow0 = 64 * wave;
       for (int i0 = 0; i0 < rows; i0 += kThreads * U) {
         uint32_t hw[U];
@@ -1349,7 +1350,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
             if ((inbin >> lane) & 1ull) {
               const uint32_t idx = base + (uint32_t)__popcll(inbin & ((1ull << lane) - 1ull));
               if (idx < (uint32_t)kSelCandCap) {
-                ckey[idx] = ((uint64_t)hw[u] << 32) | __builtin_bit_cast(uint32_t, st.at(0, i));
+                ckey[idx] = (uint64_t)hw[u] << 32;
                 crow[idx] = i;
               }
             }
@@ -1360,29 +1361,63 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     __syncthreads();
     const uint32_t nc = sh_cand;
     if (nc <= (uint32_t)kSelCandCap) {
-      // the e2 smallest candidates (keys are unique): a candidate's rank is
-      // the number of smaller candidates. Candidates j = tid + 256 q are
-      // ranked four at a time against all of them.
-      for (uint32_t j0 = 0; j0 < nc; j0 += 4 * kThreads) {
-        uint64_t kj[4];
-        uint32_t rk[4];
+      // The e2 smallest candidates (keys are unique). A thread holds
+      // candidates j = tid + 256 q. Their low words first; then a histogram
+      // of the next 8 key bits (51..43 down) names the sub-bin holding the
+      // e2-th smallest, below which every candidate is a victim; inside it a
+      // candidate's rank is the number of smaller ones there.
+      constexpr int CPT = (kSelCandCap + kThreads - 1) / kThreads;
+      {
+        uint32_t lw[CPT];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t j = j0 + tid + kThreads * q;
-          kj[q] = j < nc ? ckey[j] : 0ull;
-          rk[q] = 0u;
-        }
-        for (uint32_t k = 0; k < nc; ++k) {
-          const uint64_t kk = ckey[k];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) rk[q] += kk < kj[q] ? 1u : 0u;
+        for (int q = 0; q < CPT; ++q) {
+          const uint32_t j = tid + kThreads * q;
+          lw[q] = j < nc ? __builtin_bit_cast(uint32_t, st.at(0, crow[j])) : 0u;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t j = j0 + tid + kThreads * q;
-          if (j < nc && rk[q] < e2) {
-            const int r = crow[j];
-            atomicOr(&vbits[r >> 5], 1u << (r & 31));
+        for (int q = 0; q < CPT; ++q) {
+          const uint32_t j = tid + kThreads * q;
+          if (j < nc) ckey[j] |= lw[q];
+        }
+      }
+      hist[tid] = 0u;
+      __syncthreads();
+      auto sub = [](uint64_t k) { return (uint32_t)(k >> (64 - kSelBinBits - 8)) & 0xFFu; };
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const uint32_t j = tid + kThreads * q;
+        if (j < nc) hist_add(hist, sub(ckey[j]));
+      }
+      __syncthreads();
+      {
+        const uint32_t cnt = hist[tid];
+        uint32_t total;
+        const uint32_t excl = block_excl_scan_u32(cnt, red_u, &total);
+        if (excl < e2 && e2 <= excl + cnt) {
+          sh[0] = tid;
+          sh[1] = (int32_t)excl;
+        }
+        __syncthreads();
+      }
+      const uint32_t tb2 = (uint32_t)sh[0], e3 = e2 - (uint32_t)sh[1];
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const uint32_t j = tid + kThreads * q;
+        if (j < nc) {
+          const uint64_t kj = ckey[j];
+          const uint32_t sj = sub(kj);
+          bool v = sj < tb2;
+          if (sj == tb2) {
+            uint32_t r = 0;
+            for (uint32_t k = 0; k < nc; ++k) {
+              const uint64_t kk = ckey[k];
+              r += (sub(kk) == tb2 && kk < kj) ? 1u : 0u;
+            }
+            v = r < e3;
+          }
+          if (v) {
+            const int rr = crow[j];
+            atomicOr(&vbits[rr >> 5], 1u << (rr & 31));
           }
         }
       }
