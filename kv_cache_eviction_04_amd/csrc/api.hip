@@ -67,6 +67,7 @@ struct confkv_handle {
   std::vector<uint8_t> attended;  // per layer: attended at position t by confkv_attend
   int32_t n_attended;             // layers attended at t (0: no split step under way)
   int32_t attend_splits;          // 0: automatic; 1: one workgroup per segment; >= 2: that many
+  int32_t step_split;             // the layers attended at t used the split-K attend
 };
 
 namespace {
@@ -166,13 +167,12 @@ size_t carve(const confkv_config* c, uint8_t* base, Layout* L) {
   lay.row_prio = (float*)take(S * (size_t)lay.rows_max * 4);
   lay.seg_nold = (int32_t*)take(S * 4);
   lay.seg_stats = (uint64_t*)take(S * kStatFields * 8);
-  const bool hbm_stage = (size_t)lay.planes * lay.rows_max * 4 > (size_t)fused_max_dynamic_lds();
-  lay.stage = hbm_stage ? (float*)take(S * lay.planes * (size_t)lay.rows_max * 4) : nullptr;
+  lay.stage = (float*)take(S * lay.planes * (size_t)lay.rows_max * 4);
   const size_t segs_l = (size_t)lay.B * lay.Hkv;
   lay.ns_max = kSplitMax;
   lay.sk_o = (float*)take(segs_l * kSplitMax * lay.G * D * 4);
   lay.sk_ml = (SplitML*)take(segs_l * kSplitMax * lay.G * sizeof(SplitML));
-  lay.sk_s = (float*)take(segs_l * lay.G * (size_t)lay.rows_max * 4);
+  lay.sk_lse = (float*)take(S * lay.G * 4);
   lay.partials = (ConfPartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(ConfPartial));
   lay.spart = (SamplePartial*)take((size_t)lay.B * std::max(lay.chunks, 1) * sizeof(SamplePartial));
   lay.err = (uint32_t*)take(4);
@@ -398,6 +398,7 @@ CONFKV_API int confkv_init(const confkv_config* cfg, void* state, size_t state_b
   h->attended.assign((size_t)cfg->num_layers, 0);
   h->n_attended = 0;
   h->attend_splits = 0;
+  h->step_split = 0;
   if (launch_init(h->lay, h->par, state, carve(cfg, nullptr, nullptr), prefill_k, prefill_v, prefill_len, stream) !=
       0) {
     h->magic = kDead;
@@ -446,7 +447,6 @@ CONFKV_API int confkv_step(confkv_handle* h, void* stream, const float* logits, 
     const Staging sg = staging(h, lay.planes);
     a.lds_rows = sg.lds_rows;
     a.sel_bits_lds = sg.sel_bits_lds;
-    if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;  // cannot happen: carve sized the staging
     if (record_event(h, h->pf, s, true)) goto hip_fail;
     if (launch_fused_step(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0) goto hip_fail;
     if (record_event(h, h->pf, s, false)) goto hip_fail;
@@ -490,11 +490,11 @@ CONFKV_API int confkv_attend(confkv_handle* h, void* stream, int32_t layer, cons
   } else {
     const Staging sg = staging(h, lay.planes);
     a.lds_rows = sg.lds_rows;
-    if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
     if (record_event(h, h->pa, s, true)) goto hip_fail;
     rc = launch_attend(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream);
   }
   if (rc != 0 || record_event(h, h->pa, s, false)) goto hip_fail;
+  h->step_split = ns >= 2 ? 1 : 0;  // the same for every layer of a step
   h->attended[(size_t)layer] = 1;
   h->n_attended += 1;
   return CONFKV_OK;
@@ -506,6 +506,7 @@ hip_fail:
 CONFKV_API int confkv_set_attend_splits(confkv_handle* h, int32_t splits) {
   if (!live(h)) return CONFKV_ESTATE;
   if (splits < 0 || splits > kSplitMax) return CONFKV_EINVAL;
+  if (h->n_attended) return CONFKV_EINVAL;  // not inside a split step: its layers share one mode
   h->attend_splits = splits;
   return CONFKV_OK;
 }
@@ -539,7 +540,7 @@ CONFKV_API int confkv_evict(confkv_handle* h, void* stream, const float* logits,
   const Staging sg = staging(h, 4);  // keys (two planes) and the compaction lists
   a.lds_rows = sg.lds_rows;
   a.sel_bits_lds = sg.sel_bits_lds;
-  if (!sg.use_lds && !lay.stage) return CONFKV_EINVAL;
+  a.ema_from_scores = h->step_split;
   if (record_event(h, h->pe, s, true) || launch_evict(lay, h->par, a, sg.use_lds, sg.lds_bytes, stream) != 0 ||
       record_event(h, h->pe, s, false)) {
     h->poisoned = 1;

@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     st.p = dyn_lds;
     st.rs = a.lds_rows;
   } else {
-    st.p = lay.stage + (size_t)seg * PL * lay.rows_max;
+    st.p = lay.stage + (size_t)seg * lay.planes * lay.rows_max;
     st.rs = lay.rows_max;
   }
   // HBM-staged selection: the key histogram (later the candidates) in LDS and
@@ -1064,6 +1064,47 @@ __global__ void __launch_bounds__(kThreads, (G <= 5 ? CONFKV_OCC : 3)) fused_ste
     if (kvpop) {
       if (tid == 0 && n_old != n_old_raw) atomicOr(lay.err, kErrInternal);
       return;
+    }
+  }
+  // ---- an evict launch after split-K attends (CONF): every live row's EMA
+  // from the scores the split attends stored and the heads' log-sum-exps
+  // [Conf-KV post: EMA of the attention mass], mass = mean over the G heads
+  // of exp(s - LSE). A thread updates the rows its key pass reads next.
+  if constexpr (MODE == kModeEvict) {
+    if (a.ema_from_scores && !kvpop) {
+      const float* sco = lay.stage + (size_t)seg * lay.planes * lay.rows_max;
+      float lse[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) lse[g] = lay.sk_lse[(size_t)seg * G + g];
+      constexpr int RB = 4;
+      for (int i0 = tid; i0 < rows; i0 += kThreads * RB) {
+        int32_t p[RB];
+        float ev[RB], sc[RB][G];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int i = min(i0 + kThreads * u, rows - 1);
+          const int r = i - n_old32;
+          const int ix = r < 0 ? i : lay.cap32 + min(r, Wr32 - 1);
+          p[u] = opos[ix];
+          ev[u] = oema[ix];
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc[u][g] = sco[(size_t)g * lay.rows_max + i];
+        }
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int i = i0 + kThreads * u;
+          if (i >= rows) continue;
+          const int r = i - n_old32;
+          const bool is_old = i < n_old, is_ring = r >= 0 && r < Wr;
+          const bool is_new = is_ring && r == slot_new;
+          if (!(is_old || (is_ring && (is_new || p[u] >= 0)))) continue;
+          float mass = 0.0f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) mass += __expf(sc[u][g] - lse[g]);
+          mass *= 1.0f / (float)G;
+          oema[is_old ? i : lay.cap32 + r] = par.beta * (is_new ? 0.0f : ev[u]) + (1.0f - par.beta) * mass;
+        }
+      }
     }
   }
   // the row pass starts from the first rows again (an evict launch, and the
@@ -2047,17 +2088,13 @@ static void launch_fused_dg(const Layout& lay, const Params& par, const StepArgs
 template <int D, int MODE>
 static int launch_fused_d(const Layout& lay, const Params& par, const StepArgs& a, int grid, bool use_lds,
                           int lds_bytes, hipStream_t s) {
-  if constexpr (MODE == kModeEvict) {  // no per-head work: one instance serves every group size
-    launch_fused_dg<D, 1, MODE>(lay, par, a, grid, use_lds, lds_bytes, s);
-  } else {
-    switch (lay.G) {
-      case 1: launch_fused_dg<D, 1, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
-      case 2: launch_fused_dg<D, 2, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
-      case 4: launch_fused_dg<D, 4, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
-      case 5: launch_fused_dg<D, 5, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
-      case 8: launch_fused_dg<D, 8, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
-      default: return -1;
-    }
+  switch (lay.G) {
+    case 1: launch_fused_dg<D, 1, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+    case 2: launch_fused_dg<D, 2, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+    case 4: launch_fused_dg<D, 4, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+    case 5: launch_fused_dg<D, 5, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+    case 8: launch_fused_dg<D, 8, MODE>(lay, par, a, grid, use_lds, lds_bytes, s); break;
+    default: return -1;
   }
   return ok_or_err();
 }

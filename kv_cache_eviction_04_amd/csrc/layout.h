@@ -94,12 +94,13 @@ struct Layout {
   float* row_prio;    // [S][rows_max]
   int32_t* seg_nold;  // [S]
   uint64_t* seg_stats;  // [S][kStatFields]
-  float* stage;       // [S][planes][rows_max] when staging does not fit LDS, else null
+  float* stage;       // [S][planes][rows_max]: the step's HBM staging where LDS does not hold a
+                      // segment's rows; the split attend's raw scores (planes 0..G-1)
   // split-K attend of one layer (reused by every layer)
   int32_t ns_max;     // most splits per segment
   float* sk_o;        // [B*Hkv][ns_max][G][D] unnormalised partial outputs
   SplitML* sk_ml;     // [B*Hkv][ns_max][G]
-  float* sk_s;        // [B*Hkv][G][rows_max] raw attention scores
+  float* sk_lse;      // [S][G] log-sum-exp of each head after the split attend's combine
   // confidence reducer
   ConfPartial* partials;  // [B][chunks]
   SamplePartial* spart;   // [B][chunks] (next-token draw)
@@ -125,6 +126,8 @@ struct StepArgs {
   int32_t ns;                // split-K attend: workgroups per segment
   int32_t lds_rows;          // staged-row capacity of the LDS planes (LDS variant)
   int32_t sel_bits_lds;      // HBM-staged variant: 1 when the victim bitmask is in LDS
+  int32_t ema_from_scores;   // evict: the layers attended split-K; update the EMA from the
+                             // stored scores and log-sum-exps first
   const uint16_t* q;         // [L][B][Hq][D] (attend: [B][Hq][D])
   const uint16_t* k_new;     // [L][B][Hkv][D] (attend: [B][Hkv][D])
   const uint16_t* v_new;

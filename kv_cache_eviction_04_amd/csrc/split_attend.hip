@@ -1,6 +1,6 @@
 // HIP kernels for gfx950 (MI355X): one layer's attention at the layer
-// boundary, split over several workgroups per segment (split-K), and the
-// log-sum-exp combine that also updates the rows' EMA.
+// boundary, split over several workgroups per segment (split-K), and its
+// log-sum-exp combine.
 //
 // Sources: CONF-KV abstract (chatpaper.ai); "Conf-KV" post (rcap.io), method
 // paragraph; "Resumen Técnico: KVpop" (gist.science) §2.3.
@@ -14,15 +14,17 @@ namespace confkv {
 // the run of 32-row stage tiles [c*T/ns, (c+1)*T/ns) (T tiles in all: the
 // old region, then the ring) and computes, per query head, its own maximum
 // m_c, sum l_c = sum exp(s - m_c) and unnormalised PV partial O_c, and
-// stores the raw scores s of its rows. The split holding the new row's slot
-// appends it. A second launch, one workgroup per segment, combines
-// [CONF-KV abstract: blockwise online-softmax attention]:
+// stores the raw scores s of its rows in the segment's HBM stage (planes
+// 0..G-1). The split holding the new row's slot appends it. A second launch,
+// one workgroup per segment, combines [CONF-KV abstract: blockwise
+// online-softmax attention]:
 //   M = max_c m_c, L = sum_c l_c e^(m_c - M), out = sum_c O_c e^(m_c - M) / L,
 //   LSE = M + log L,
-// and, under CONF, updates every live row's EMA from the stored scores with
-// mass = mean over the G heads of exp(s - LSE) [Conf-KV post: EMA of the
-// attention mass]. The launch boundary orders the two: a device-scope fence
-// per workgroup would write back and invalidate its XCD's whole L2.
+// and stores each head's LSE. Under CONF the evict launch after the last
+// layer updates every live row's EMA from the stored scores and LSEs (mass =
+// mean over the G heads of exp(s - LSE)), for all layers at once. The launch
+// boundary orders split and combine: a device-scope fence per workgroup
+// would write back and invalidate its XCD's whole L2.
 // Arithmetic per split is that of the whole-segment kernel.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_split_kernel(Layout lay, Params par,
@@ -272,11 +274,11 @@ __global__ void __launch_bounds__(kThreads, (G <= 4 ? CONFKV_OCC : 3)) attend_sp
   const float fscale = ldexpf(1.0f, fexp), finv = ldexpf(1.0f, -fexp);
 
   // ---- weights: p = exp(s - m_c) (0 for a run without a valid row), the
-  // raw scores kept for the combine's EMA pass
+  // raw scores kept for the evict launch's EMA pass
   float lpart[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) lpart[g] = 0.0f;
-  float* sco = lay.sk_s + (size_t)sl * G * lay.rows_max;
+  float* sco = lay.stage + (size_t)seg * lay.planes * lay.rows_max;  // planes 0..G-1 of the segment's stage
   for (int j = tid; j < r1 - r0; j += kThreads) {
     const int i = r0 + j;
     const float sv = (i < n_old && par.old_int8) ? svl[j] : 0.0f;
@@ -400,9 +402,19 @@ __global__ void __launch_bounds__(kThreads) attend_combine_kernel(Layout lay, Pa
   const int tid = threadIdx.x;
   const int ns = a.ns;
   const int sl = blockIdx.x, seg = a.seg0 + sl;
-  const int t = a.t, Wr = lay.Wr;
-  const bool kvpop = par.policy == 1;
   const size_t pbase = (size_t)sl * lay.ns_max;
+  // the first KPRE splits' partials of this thread's output elements are
+  // loaded before the statistics, so both round trips overlap
+  constexpr int EPT = (G * D + kThreads - 1) / kThreads;
+  constexpr int KPRE = 8;
+  const float* po = lay.sk_o + pbase * G * D;
+  float pre[EPT][KPRE];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + kThreads * j;
+#pragma unroll
+    for (int k = 0; k < KPRE; ++k) pre[j][k] = (e < G * D && k < ns) ? po[(size_t)k * G * D + e] : 0.0f;
+  }
   if (tid < G * ns) {
     const int k = tid / G, g = tid - k * G;
     const SplitML ml = lay.sk_ml[(pbase + k) * G + g];
@@ -421,63 +433,28 @@ __global__ void __launch_bounds__(kThreads) attend_combine_kernel(Layout lay, Pa
     sh_lse[tid] = M + logf(L);
   }
   __syncthreads();
-  // out = sum_k O_k * e^(m_k - M) / L, eight splits' loads at a time
-  const float* po = lay.sk_o + pbase * G * D;
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int g = e / D;
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < ns; k0 += 8) {
-      float v[8];
+  // out = sum_k O_k * e^(m_k - M) / L; splits past the first KPRE eight loads at a time
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = k0 + u < ns ? po[(size_t)(k0 + u) * G * D + e] : 0.0f;
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + kThreads * j;
+    if (e < G * D) {
+      const int g = e / D;
+      float acc = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += k0 + u < ns ? v[u] * sh_f[g][k0 + u] : 0.0f;
+      for (int k = 0; k < KPRE; ++k) acc += k < ns ? pre[j][k] * sh_f[g][k] : 0.0f;
+      for (int k0 = KPRE; k0 < ns; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < ns ? po[(size_t)(k0 + u) * G * D + e] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += k0 + u < ns ? v[u] * sh_f[g][k0 + u] : 0.0f;
+      }
+      a.out[(size_t)sl * G * D + e] = f2h(acc);
     }
-    a.out[(size_t)sl * G * D + e] = f2h(acc);
   }
-  if (par.record && tid < G) lay.rec_lse[(size_t)seg * G + tid] = sh_lse[tid];
-  if (kvpop) return;
-  // ---- EMA of every live row from the stored scores, four rows per thread
-  // per batch with every load of the batch issued first
-  const size_t sbase = (size_t)seg * lay.rows_max;
-  const int32_t* opos = lay.row_pos + sbase;
-  float* oema = lay.row_ema + sbase;
-  const int n_old = lay.seg_nold[seg];
-  const int n_old32 = (n_old + 31) & ~31;
-  const int rows = n_old32 + lay.Wr32;
-  const int slot_new = t % Wr;
-  const float* sco = lay.sk_s + (size_t)sl * G * lay.rows_max;
-  float lse[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) lse[g] = sh_lse[g];
-  constexpr int RB = 4;
-  for (int i0 = tid; i0 < rows; i0 += kThreads * RB) {
-    int32_t p[RB];
-    float ev[RB], sc[RB][G];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = min(i0 + kThreads * u, rows - 1);
-      const int r = i - n_old32;
-      const int ix = r < 0 ? i : lay.cap32 + min(r, lay.Wr32 - 1);
-      p[u] = opos[ix];
-      ev[u] = oema[ix];
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[u][g] = sco[(size_t)g * lay.rows_max + i];
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = i0 + kThreads * u;
-      if (i >= rows) continue;
-      const int r = i - n_old32;
-      const bool is_old = i < n_old, is_ring = r >= 0 && r < Wr;
-      const bool is_new = is_ring && r == slot_new;
-      if (!(is_old || (is_ring && (is_new || p[u] >= 0)))) continue;
-      float mass = 0.0f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) mass += __expf(sc[u][g] - lse[g]);
-      mass *= 1.0f / (float)G;
-      oema[is_old ? i : lay.cap32 + r] = par.beta * (is_new ? 0.0f : ev[u]) + (1.0f - par.beta) * mass;
-    }
+  if (tid < G) {
+    lay.sk_lse[(size_t)seg * G + tid] = sh_lse[tid];
+    if (par.record) lay.rec_lse[(size_t)seg * G + tid] = sh_lse[tid];
   }
 }
 
