@@ -205,7 +205,11 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   constexpr int QB = 16 * QT;                   // queries per workgroup
   constexpr int NR = HPW * QT;                  // 16-row blocks per wave
   constexpr int KSTR = D + 8;   // K tile row stride (halves)
-  constexpr int VSTR = 40;      // V^T tile row stride (halves): 32 keys + pad
+  // V^T tile row stride (halves): 32 keys + pad. Within row r the four
+  // 8-key groups are stored XOR-swizzled by ((r/8)/2) mod 4, so that the
+  // transposing stores of the 16 pieces of a key spread over the banks; the
+  // PV reads of group lq of rows 16cb.. take group lq ^ (cb mod 4).
+  constexpr int VSTR = 40;
   constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
   constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
   extern __shared__ __align__(16) uint16_t plds[];
@@ -319,9 +323,10 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
         const int key = e / (D / 8), piece = e - key * (D / 8);
         *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
         const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+        const int kcol = key ^ (8 * ((piece >> 1) & 3));  // 8-key groups swizzled by the piece
 #pragma unroll
         for (int x = 0; x < 8; ++x)
-          Vt[(8 * piece + x) * VSTR + key] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
+          Vt[(8 * piece + x) * VSTR + kcol] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
       }
     }
   };
@@ -392,7 +397,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
       m[rb] = mn;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * lq));
+        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * (lq ^ (cb & 3))));
         O[rb][cb] *= alpha;
         O[rb][cb] = mfma16(av, phi, O[rb][cb]);
         O[rb][cb] = mfma16(av, plo, O[rb][cb]);
