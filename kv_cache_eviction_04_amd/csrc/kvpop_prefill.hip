@@ -196,7 +196,8 @@ constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 // (transposed) go through LDS once for all the workgroup's queries; wave w
 // takes query heads w, w+4, ... for its 16-query blocks: S^T = K Q^T on
 // MFMA, the predicate per (key, query), online softmax per query in the
-// base-2 domain, and O^T = V^T P^T with the weights as fp16 hi and lo parts.
+// base-2 domain, and O^T = V^T P^T with the weights rounded once to fp16
+// (the sums l stay fp32, so the LSE is not affected).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
   constexpr int KS = D / 32, NCB = D / 16;
@@ -382,14 +383,12 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
       const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
       const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
       float ls = 0.0f;
-      half8 phi, plo;
+      half8 ph;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(sc[e] - ms);
         ls += pe;
-        const _Float16 hi = (_Float16)pe;
-        phi[e] = hi;
-        plo[e] = (_Float16)(pe - (float)hi);
+        ph[e] = (_Float16)pe;
       }
       ls += __shfl_xor(ls, 16, 64);
       ls += __shfl_xor(ls, 32, 64);
@@ -399,8 +398,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
       for (int cb = 0; cb < NCB; ++cb) {
         const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * (lq ^ (cb & 3))));
         O[rb][cb] *= alpha;
-        O[rb][cb] = mfma16(av, phi, O[rb][cb]);
-        O[rb][cb] = mfma16(av, plo, O[rb][cb]);
+        O[rb][cb] = mfma16(av, ph, O[rb][cb]);
       }
     }
     __syncthreads();
