@@ -185,6 +185,40 @@ __device__ __forceinline__ void xcd_tile_seg(int& tile, int& seg) {
   tile = work - seg * gridDim.x;
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes j, j+16, j+32,
+// j+48), in every lane, with gfx950's row-swap instructions: VALU work, no
+// LDS round trip. v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second, so with both set to x they end
+// up holding rows (0, 0, 2, 2) and (1, 1, 3, 3) of x; v_permlane32_swap does
+// the same for the two halves. Combining the pair gives every lane the same
+// value, in the same order as a shuffle-xor reduction. This compiler's
+// builtins for these instructions return the first operand for both
+// results, hence the asm; s_nop 1 gives the two wait states a swap needs
+// after a VALU write of its operands (and the same again before a VALU
+// reads its results).
+__device__ __forceinline__ void row_swap(float& a, float& b, int half) {
+  if (half)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float rows_max(float x) {
+  float a = x, b = x;
+  row_swap(a, b, 0);
+  a = fmaxf(a, b);
+  b = a;
+  row_swap(a, b, 1);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float a = x, b = x;
+  row_swap(a, b, 0);
+  a = a + b;
+  b = a;
+  row_swap(a, b, 1);
+  return a + b;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 
@@ -377,8 +411,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
         sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
         mt = fmaxf(mt, sc[e]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = rows_max(mt);
       const float mn = fmaxf(m[rb], mt);
       const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
       const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
@@ -390,8 +423,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
         ls += pe;
         ph[e] = (_Float16)pe;
       }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
+      ls = rows_sum(ls);
       l[rb] = l[rb] * alpha + ls;
       m[rb] = mn;
 #pragma unroll
