@@ -461,11 +461,18 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
 // Future-attention target [KVpop summary §2.2], the transposed pass: for key
 // t of a segment, log sum over the group's query heads g and the queries
 // d >= t + w of exp(s[d, g, t] - LSE[d, g]), with the queries' normalisers
-// handed in, so no attention map is formed. One workgroup per 128 keys; wave
-// w takes keys 32w .. 32w+31 of them as two 16-row MFMA A tiles. The later
+// handed in, so no attention map is formed. One workgroup per 64*kTgtTiles
+// keys; wave w takes kTgtTiles 16-row MFMA A tiles of them. The later
 // queries stream through LDS in stages of four (16-query tile, head) pairs,
 // double-buffered and shared by the four waves; the MFMA gives
-// S^T[key][query] and each lane accumulates the masked exponentials.
+// S^T[key][query] and each lane accumulates the masked exponentials. Every
+// workgroup streams the Q rows of all queries after its keys, so the keys
+// per workgroup set how often Q is read again.
+#ifndef CONFKV_TGT_TILES
+#define CONFKV_TGT_TILES 4
+#endif
+constexpr int kTgtTiles = CONFKV_TGT_TILES;   // 16-key A tiles per wave
+constexpr int kTgtKeys = 64 * kTgtTiles;      // keys per workgroup
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
                                                                 float* target) {
@@ -483,14 +490,14 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
   int tile, seg;
   xcd_tile_seg(tile, seg);
   const int b = seg / pa.Hkv, h = seg - b * pa.Hkv;
-  const int t0b = 128 * tile;                  // the workgroup's first key
-  const int t0 = t0b + 32 * wave;              // this wave's first key
+  const int t0b = kTgtKeys * tile;             // the workgroup's first key
+  const int t0 = t0b + 16 * kTgtTiles * wave;  // this wave's first key
   const uint16_t* kseg = pa.k + (size_t)seg * S * D;
   const float sl2 = pa.scale * kLog2e;
 
-  half8 ka[2][KS];
+  half8 ka[kTgtTiles][KS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kTgtTiles; ++kb) {
     const int t = t0 + 16 * kb + lj;
     const uint16_t* kr = kseg + (size_t)min(t, S - 1) * D;
 #pragma unroll
@@ -499,9 +506,9 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
       ka[kb][kk] = t < S ? as_h8(u) : half8{};
     }
   }
-  float acc[2][4];
+  float acc[kTgtTiles][4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < kTgtTiles; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[kb][r] = 0.0f;
 
@@ -561,9 +568,9 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
       // exp(s*scale - lse) = 2^(c*scale*log2(e) - lse*log2(e)): one FMA and one exp2
       const float nl2 = -ls[buf][pr][lj] * kLog2e;
       // every query of this tile counts for every key of this wave
-      const bool full = d0 >= t0 + 31 + w && d0 + 15 < S;
+      const bool full = d0 >= t0 + 16 * kTgtTiles - 1 + w && d0 + 15 < S;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kTgtTiles; ++kb) {
         floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], qb[kk], c);
@@ -584,7 +591,7 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
     __syncthreads();
   }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kTgtTiles; ++kb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float a = acc[kb][r];
@@ -629,7 +636,7 @@ int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
 
 template <int D>
 static int launch_target_d(const KvpopPrefillArgs& pa, const float* lse, float* target, hipStream_t s) {
-  const dim3 grid((pa.S + 127) / 128, pa.B * pa.Hkv);
+  const dim3 grid((pa.S + kTgtKeys - 1) / kTgtKeys, pa.B * pa.Hkv);
   switch (pa.G) {
     case 1: hipLaunchKernelGGL((kvpop_target_kernel<D, 1>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
     case 2: hipLaunchKernelGGL((kvpop_target_kernel<D, 2>), grid, dim3(kThreads), 0, s, pa, lse, target); break;
