@@ -474,7 +474,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
 constexpr int kTgtTiles = CONFKV_TGT_TILES;   // 16-key A tiles per wave
 constexpr int kTgtKeys = 64 * kTgtTiles;      // keys per workgroup
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
+__global__ void __launch_bounds__(kThreads, 2) kvpop_target_kernel(KvpopPrefillArgs pa, const float* lse_in,
                                                                 float* target) {
   constexpr int KS = D / 32;
   constexpr int QSTR = D + 8;                 // staged row stride (halves)
@@ -484,7 +484,8 @@ __global__ void __launch_bounds__(kThreads) kvpop_target_kernel(KvpopPrefillArgs
   static_assert(PPT * kThreads == NP * 16 * RP, "stage pieces divide the block");
   __shared__ __align__(16) uint16_t qs[2][NP][16][QSTR];
   __shared__ float ls[2][NP][16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the full-tile test is a scalar branch
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, w = pa.window;
   int tile, seg;
