@@ -580,6 +580,8 @@ PrefillSizes prefill_sizes(const confkv_handle* h, int64_t S) {
   z.N = N;
   z.sort_bytes = (int64_t)align256((size_t)(segs * N * 8));
   z.rank_bytes = (int64_t)align256((size_t)(segs * S * 4));
+  // the thresholds follow the ranks: the attend kernel's 16-byte reads may run
+  // up to 60 bytes past the last segment's ranks, into the thresholds
   z.total = z.sort_bytes + 2 * z.rank_bytes;
   return z;
 }

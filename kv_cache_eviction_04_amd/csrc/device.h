@@ -196,6 +196,7 @@ __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
   return r;
 }
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
+template <int NW = 4>
 __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* red, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = v;
@@ -205,9 +206,13 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* re
   }
   if (lane == 63) red[wave] = inc;
   __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += red[w];
-  *total = red[0] + red[1] + red[2] + red[3];
+  uint32_t off = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    off += w < wave ? red[w] : 0u;
+    all += red[w];
+  }
+  *total = all;
   __syncthreads();
   return off + inc - v;
 }

@@ -227,17 +227,22 @@ constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 // long-range keys that pass the first query's threshold (a superset for the
 // later queries, whose thresholds are no larger), and the contiguous run
 // [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
-// (transposed) go through LDS once for all the workgroup's queries; wave w
-// takes query heads w, w+4, ... for its 16-query blocks: S^T = K Q^T on
-// MFMA, the predicate per (key, query), online softmax per query in the
-// base-2 domain, and O^T = V^T P^T with the weights rounded once to fp16
-// (the sums l stay fp32, so the LSE is not affected).
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+// (transposed) go through LDS once for all the workgroup's queries. With 8
+// waves (groups of up to 4 query heads) wave w takes head w % 4 for the 16
+// queries of block w / 4; with 4 waves (larger groups) wave w takes heads w,
+// w+4, ... for 16 queries. Per row block: S^T = K Q^T on MFMA, the predicate
+// per (key, query), online softmax per query in the base-2 domain, and
+// O^T = V^T P^T with the weights rounded once to fp16 (the sums l stay
+// fp32, so the LSE is not affected).
+template <int D, int G, int NT>
+__global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
   constexpr int KS = D / 32, NCB = D / 16;
-  constexpr int HPW = (G + 3) / 4;              // query heads per wave
-  constexpr int QT = HPW == 1 ? 2 : 1;          // 16-query blocks per head
-  constexpr int QB = 16 * QT;                   // queries per workgroup
+  constexpr int NW = NT / 64;                   // waves
+  constexpr bool kWavePerBlock = NW == 8;       // 8 waves: one (head, 16-query block) per wave
+  static_assert(!kWavePerBlock || G <= 4, "8 waves serve groups of up to 4 heads");
+  constexpr int HPW = kWavePerBlock ? 1 : (G + 3) / 4;          // query heads per wave
+  constexpr int QT = kWavePerBlock ? 1 : (HPW == 1 ? 2 : 1);     // 16-query blocks per head and wave
+  constexpr int QB = kWavePerBlock ? 32 : 16 * QT;               // queries per workgroup
   constexpr int NR = HPW * QT;                  // 16-row blocks per wave
   constexpr int KSTR = D + 8;   // K tile row stride (halves)
   // V^T tile row stride (halves): 32 keys + pad. Within row r the four
@@ -246,15 +251,16 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   // PV reads of group lq of rows 16cb.. take group lq ^ (cb mod 4).
   constexpr int VSTR = 40;
   constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
-  constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
+  constexpr int PPT = (PIECES + NT - 1) / NT;
   extern __shared__ __align__(16) uint16_t plds[];
   uint16_t* Kt = plds;                        // [32][KSTR]
   uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
   int32_t* lpos = reinterpret_cast<int32_t*>(Vt + D * VSTR);
   int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, s = pa.sinks, w = pa.window;
   int tile, seg;
@@ -270,31 +276,59 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   const int n_sink = min(s, q1);
   const int g_end = max(s, q0 - w);            // long-range positions [s, g_end)
   const int thr0 = thr[q0];
-  const int glen = g_end - s;
-  const int per = (glen + kThreads - 1) / kThreads;
-  const int ga = s + min(glen, tid * per), gb = s + min(glen, tid * per + per);
+  // Each thread scans a run of ranks that starts 16-byte aligned in memory
+  // (at most 3 before s: the previous segment's, or for the first segment
+  // none before the array), 16 ranks per round as four 16-byte loads in
+  // flight. A round starts below g_end <= S and may read up to 15 ranks
+  // past the segment's end: the next segment's, or for the last segment the
+  // start of the thresholds, which follow the ranks in the workspace. Ranks
+  // before s and from g_end on are skipped. Count, scan, then write in
+  // ascending position order.
+  const int a0 = s - (int)(((size_t)seg * S + s) & 3);  // rank + a0 is 16-byte aligned
+  const int span = g_end - a0;
+  const int per = (((span + NT - 1) / NT) + 15) & ~15;
+  const int ga = a0 + min(span, tid * per), gb = a0 + min(span, tid * per + per);
+  auto load16 = [&](int j, int (&r)[16]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int4 v = *reinterpret_cast<const int4*>(rank + j + 4 * u);
+      r[4 * u] = v.x;
+      r[4 * u + 1] = v.y;
+      r[4 * u + 2] = v.z;
+      r[4 * u + 3] = v.w;
+    }
+  };
   uint32_t cnt = 0;
-  for (int j = ga; j < gb; ++j) cnt += rank[j] <= thr0 ? 1u : 0u;
+  for (int j = ga; j < gb; j += 16) {
+    int r[16];
+    load16(j, r);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cnt += (j + e >= s && j + e < gb && r[e] <= thr0) ? 1u : 0u;
+  }
   uint32_t ng;
-  uint32_t off = block_excl_scan_u32(cnt, red, &ng);
-  for (int j = ga; j < gb; ++j) {
-    const int r = rank[j];
-    if (r <= thr0) {
-      if (n_sink + (int)off < pa.list_cap) {
-        lpos[n_sink + off] = j;
-        lrank[n_sink + off] = r;
+  uint32_t off = block_excl_scan_u32<NW>(cnt, red, &ng);
+  for (int j = ga; j < gb; j += 16) {
+    int r[16];
+    load16(j, r);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (j + e >= s && j + e < gb && r[e] <= thr0) {
+        if (n_sink + (int)off < pa.list_cap) {
+          lpos[n_sink + off] = j + e;
+          lrank[n_sink + off] = r[e];
+        }
+        ++off;
       }
-      ++off;
     }
   }
   const int c0 = g_end;
   const int n_cont = max(0, q1 - c0);
   const int nk = n_sink + (int)ng + n_cont;
-  for (int i = tid; i < n_sink; i += kThreads) {
+  for (int i = tid; i < n_sink; i += NT) {
     lpos[i] = i;
     lrank[i] = -1;
   }
-  for (int i = tid; i < n_cont; i += kThreads) {
+  for (int i = tid; i < n_cont; i += NT) {
     if (n_sink + (int)ng + i < pa.list_cap) {
       lpos[n_sink + ng + i] = c0 + i;
       lrank[n_sink + ng + i] = rank[c0 + i];
@@ -304,20 +338,24 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   __syncthreads();
   const int nkc = min(nk, pa.list_cap);
 
-  // ---- row blocks of this wave: head slot rb / QT, query block rb % QT. The
+  // ---- row blocks of this wave: head rb_head(rb), query block rb_qblk(rb). The
   // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
   // that lane (lq, lj) receives query lj's scores against keys 8lq .. 8lq+7
   // of the chunk: the softmax of a query stays in one lane group, and its
   // eight weights are at once the lane's B operand of O^T = V^T P^T.
   // Scores and maxima are kept in base-2 units (scale * log2(e) folded in).
   const float sl2 = pa.scale * kLog2e;
+  auto rb_head = [&](int rb) { return kWavePerBlock ? (wave & 3) : wave + 4 * (rb / QT); };
+  auto rb_qblk = [&](int rb) { return kWavePerBlock ? (wave >> 2) : rb % QT; };
+  // row block rb serves a head (always so when G is a multiple of 4)
+  auto active = [&](int rb) { return G % 4 == 0 || rb_head(rb) < G; };
   half8 qb[NR][KS];
   float m[NR], l[NR];
   int thr_q[NR];
   floatx4 O[NR][NCB];
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
-    const int g = wave + 4 * (rb / QT), qt = rb % QT;
+    const int g = rb_head(rb), qt = rb_qblk(rb);
     const int hq = h * G + (g < G ? g : 0);
     const int qrow = q0 + 16 * qt + lj;
     const uint16_t* qp = pa.q + (((size_t)b * pa.Hq + hq) * S + min(qrow, S - 1)) * D;
@@ -340,8 +378,8 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   auto load_chunk = [&](int c) {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      if (e < PIECES) {
+      const int e = tid + NT * u;
+      if (PIECES % NT == 0 || e < PIECES) {
         const int key = e / (D / 8), piece = e - key * (D / 8);
         const int li = 32 * c + key;
         const int pos = li < nkc ? lpos[li] : 0;
@@ -353,8 +391,8 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   auto store_chunk = [&]() {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
-      const int e = tid + kThreads * u;
-      if (e < PIECES) {
+      const int e = tid + NT * u;
+      if (PIECES % NT == 0 || e < PIECES) {
         const int key = e / (D / 8), piece = e - key * (D / 8);
         *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
         const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
@@ -391,8 +429,8 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
     }
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb) {
-      if (wave + 4 * (rb / QT) >= G) continue;
-      const int qr = q0 + 16 * (rb % QT) + lj;
+      if (!active(rb)) continue;
+      const int qr = q0 + 16 * rb_qblk(rb) + lj;
       floatx4 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -439,7 +477,7 @@ __global__ void __launch_bounds__(kThreads, 3) kvpop_prefill_attend_kernel(Kvpop
   // holds O^T[column 16cb + 4lq + r][query lj].
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
-    const int g = wave + 4 * (rb / QT), qt = rb % QT;
+    const int g = rb_head(rb), qt = rb_qblk(rb);
     if (g >= G) continue;
     const int hq = h * G + g;
     const int qr = q0 + 16 * qt + lj;
@@ -607,12 +645,12 @@ template <int D>
 static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipStream_t s) {
   const int qb = pa.G <= 4 ? 32 : 16;  // queries per workgroup (see the kernel)
   const dim3 grid((pa.S + qb - 1) / qb, pa.B * pa.Hkv);
-  switch (pa.G) {
-    case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 4: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 4>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 5: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 5>), grid, dim3(kThreads), lds_bytes, s, pa); break;
-    case 8: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 8>), grid, dim3(kThreads), lds_bytes, s, pa); break;
+  switch (pa.G) {  // 8 waves for groups of up to 4 heads, 4 for larger ones
+    case 1: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 1, 512>), grid, dim3(512), lds_bytes, s, pa); break;
+    case 2: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 2, 512>), grid, dim3(512), lds_bytes, s, pa); break;
+    case 4: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 4, 512>), grid, dim3(512), lds_bytes, s, pa); break;
+    case 5: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 5, 256>), grid, dim3(256), lds_bytes, s, pa); break;
+    case 8: hipLaunchKernelGGL((kvpop_prefill_attend_kernel<D, 8, 256>), grid, dim3(256), lds_bytes, s, pa); break;
     default: return -1;
   }
   return ok_or_err();
