@@ -121,21 +121,19 @@ def test_kvpop_thresholds_at_batch_edges(S, s, w, k, ties):
         assert np.array_equal(t_or, kth_smallest_prefix(r_or, S, s, w, k))
 
 
-def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
-    # the Qwen3-8B shape at the pages' 16384-token training length, budget
-    # s + w + k = 4 + 256 + 1788; rows checked one by one against top-k per row
-    B, Hq, Hkv, d, S = 1, 32, 8, 128, 16384
-    w_ = synth.workload("kvpop_qwen3_8b", num_layers=1, batch=B)
+def check_sampled_rows(w_, S, rows, seed):
+    """Prefill at w_'s shape over S positions; the given query rows checked
+    one by one against top-k per row (ranks and all thresholds in full)."""
+    B, Hq, Hkv, d = w_["batch"], w_["num_q_heads"], w_["num_kv_heads"], w_["head_dim"]
     s, w, k = w_["num_sink"], w_["protect_last"], w_["kvpop_k"]
     gpu = confkv.Cache(w_)
-    q, kk, v, p = inputs(B, Hq, Hkv, S, d, seed=7)
+    q, kk, v, p = inputs(B, Hq, Hkv, S, d, seed=seed)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
     out, lse, ws = gpu.kvpop_prefill(q, kk, v, p, lse=lse)
     ranks, thr = gpu.kvpop_prefill_ranks(ws, S)
     assert gpu.status() == confkv.OK
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(d)
-    rows = [0, 3, 4, 259, 260, 261, 2047, 2048, 2049, 5000, 9999, S - 17, S - 1]
     worst = 0.0
     for h in range(Hkv):
         pn = p[0, h].cpu().numpy()
@@ -164,7 +162,30 @@ def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
                 assert err <= TOL_OUT, f"h{h} g{g} q{qr}: {err}"
                 l_or = m + np.log(e.sum())
                 assert abs(float(lse[0, h * G + g, qr]) - l_or) <= TOL_LSE_REL * max(1.0, abs(l_or))
-    log(f"kvpop prefill Qwen3-8B 16K: {len(rows)} rows x 2 heads x {G}, worst out err {worst:.2e}")
+    return worst
+
+
+def test_kvpop_prefill_qwen3_8b_16k_sampled_rows():
+    # the Qwen3-8B shape at the pages' 16384-token training length, budget
+    # s + w + k = 4 + 256 + 1788; rows checked one by one against top-k per row
+    S = 16384
+    w_ = synth.workload("kvpop_qwen3_8b", num_layers=1, batch=1)
+    rows = [0, 3, 4, 259, 260, 261, 2047, 2048, 2049, 5000, 9999, S - 17, S - 1]
+    worst = check_sampled_rows(w_, S, rows, seed=7)
+    log(f"kvpop prefill Qwen3-8B 16K: {len(rows)} rows x 8 heads x 4, worst out err {worst:.2e}")
+
+
+def test_kvpop_prefill_long_key_list():
+    # k = 3500 at d = 128: a query tile's key list of s + k + w + 40 = 3608
+    # entries (28.9 KB of LDS beside the 18.9 KB chunk buffer), most of the
+    # rows' keys long-range, and queries on both sides of the fill-up at
+    # q = s + w + k
+    S = 6000
+    w_ = synth.workload("kvpop_qwen3_8b", num_layers=1, batch=1, num_q_heads=8, num_kv_heads=2, num_sink=4,
+                        protect_last=64, fp16_window=64, kvpop_k=3500)
+    rows = [0, 5, 67, 68, 69, 3567, 3568, 3569, 3570, 4000, 5000, S - 1]
+    worst = check_sampled_rows(w_, S, rows, seed=11)
+    log(f"kvpop prefill k 3500: worst out err {worst:.2e}")
 
 
 TOL_TARGET = 1e-4  # on the log: fp32 sums of exponentials, relative error well below 1e-4 at these lengths
