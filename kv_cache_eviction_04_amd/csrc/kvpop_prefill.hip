@@ -403,6 +403,12 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       }
     }
   };
+  // Thresholds do not increase with the query, so thr(q1 - 1) is the
+  // tile's smallest: a key at or before q0 and below g_end (a sink, or a
+  // long-range key) whose rank passes it is allowed for every query of the
+  // tile, and a chunk of such keys needs no per-pair predicate.
+  const int thr_min = thr[q1 - 1];
+  const int easy_end = min(q0 + 1, g_end);
   const int nchunks = (nkc + 31) >> 5;
   if (nchunks > 0) load_chunk(0);
   for (int c = 0; c < nchunks; ++c) {
@@ -427,6 +433,10 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
         krank[e] = rr[e];
       }
     }
+    bool easy = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) easy = easy && kpos[e] < easy_end && krank[e] <= thr_min;
+    const bool chunk_easy = __all(easy);
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb) {
       if (!active(rb)) continue;
@@ -442,12 +452,20 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       }
       float sc[8];
       float mt = -INFINITY;
+      if (chunk_easy) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = kpos[e];
-        const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
-        sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
-        mt = fmaxf(mt, sc[e]);
+        for (int e = 0; e < 8; ++e) {
+          sc[e] = qr < q1 ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+          mt = fmaxf(mt, sc[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = kpos[e];
+          const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
+          sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+          mt = fmaxf(mt, sc[e]);
+        }
       }
       mt = rows_max(mt);
       const float mn = fmaxf(m[rb], mt);
@@ -464,10 +482,15 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       ls = rows_sum(ls);
       l[rb] = l[rb] * alpha + ls;
       m[rb] = mn;
+      // the output is rescaled only when some query's maximum moved (alpha 1
+      // elsewhere: skipping leaves every bit as it is)
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) O[rb][cb] *= alpha;
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * (lq ^ (cb & 3))));
-        O[rb][cb] *= alpha;
         O[rb][cb] = mfma16(av, ph, O[rb][cb]);
       }
     }
