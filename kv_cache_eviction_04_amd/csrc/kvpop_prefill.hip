@@ -222,12 +222,28 @@ __device__ __forceinline__ float rows_sum(float x) {
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2)
 
+// 16-byte piece swizzle of row r of the LDS V tile (rows of D halves). The PV
+// operand of a lane group is read by gfx950's transposing LDS read: each lane
+// of a 16-lane group names 8 bytes (4 columns) of one of 4 rows, and lane j
+// receives column j of the 4 rows. A half-wave so reads 32 bytes of each of 8
+// rows that differ in bits 0, 1 and 3 (D = 128: rows are 256 bytes, one bank
+// line each) or in bits 1 and 3 within each parity (D = 64: 128-byte rows,
+// odd rows on the upper half of the banks). XOR-ing the piece index with an
+// even value taken from those bits puts the 8 rows on distinct banks.
+template <int D>
+__device__ __forceinline__ int vtile_swizzle(int r) {
+  return D == 128 ? 2 * ((r & 3) | (((r >> 3) & 1) << 2)) : 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+
 // Masked prefill attention: one workgroup per 32 queries of a segment (16
 // when a wave serves two query heads). The key list holds the sinks, the
 // long-range keys that pass the first query's threshold (a superset for the
 // later queries, whose thresholds are no larger), and the contiguous run
-// [q0 - w, q1). Per 32-key chunk the K rows (row-major) and V rows
-// (transposed) go through LDS once for all the workgroup's queries. With 8
+// [q0 - w, q1). Per 32-key chunk the K rows and V rows (both row-major, V's
+// pieces swizzled) go through LDS once for all the workgroup's queries. With 8
 // waves (groups of up to 4 query heads) wave w takes head w % 4 for the 16
 // queries of block w / 4; with 4 waves (larger groups) wave w takes heads w,
 // w+4, ... for 16 queries. Per row block: S^T = K Q^T on MFMA, the predicate
@@ -245,17 +261,13 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
   constexpr int QB = kWavePerBlock ? 32 : 16 * QT;               // queries per workgroup
   constexpr int NR = HPW * QT;                  // 16-row blocks per wave
   constexpr int KSTR = D + 8;   // K tile row stride (halves)
-  // V^T tile row stride (halves): 32 keys + pad. Within row r the four
-  // 8-key groups are stored XOR-swizzled by ((r/8)/2) mod 4, so that the
-  // transposing stores of the 16 pieces of a key spread over the banks; the
-  // PV reads of group lq of rows 16cb.. take group lq ^ (cb mod 4).
-  constexpr int VSTR = 40;
+  static_assert(D == 64 || D == 128, "V tile swizzle");
   constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
   constexpr int PPT = (PIECES + NT - 1) / NT;
   extern __shared__ __align__(16) uint16_t plds[];
   uint16_t* Kt = plds;                        // [32][KSTR]
-  uint16_t* Vt = Kt + 32 * KSTR;              // [D][VSTR]
-  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + D * VSTR);
+  uint16_t* Vt = Kt + 32 * KSTR;              // [32][D], pieces swizzled
+  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + 32 * D);
   int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
   __shared__ uint32_t red[NW];
 
@@ -372,6 +384,12 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
   }
   // row lj of permuted block kb holds key 8*(lj/4) + 4*kb + lj%4 of the chunk
   const int kperm0 = 8 * (lj >> 2) + (lj & 3);
+  // PV operand of column block cb: keys 8lq .. 8lq+7 of column 16cb + lj, as
+  // two transposing reads of rows 8lq + lj/4 and 8lq + 4 + lj/4 (same
+  // swizzle), columns 16cb + 4(lj%4) .. +3
+  const int vrow = 8 * lq + (lj >> 2);
+  const int vsw = vtile_swizzle<D>(vrow);
+  const uint16_t* vbase = Vt + vrow * D + 4 * (lj & 1);
 
   // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
   uint4 rk[PPT], rv[PPT];
@@ -395,11 +413,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       if (PIECES % NT == 0 || e < PIECES) {
         const int key = e / (D / 8), piece = e - key * (D / 8);
         *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
-        const uint32_t wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
-        const int kcol = key ^ (8 * ((piece >> 1) & 3));  // 8-key groups swizzled by the piece
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          Vt[(8 * piece + x) * VSTR + kcol] = (uint16_t)(wv[x >> 1] >> (16 * (x & 1)));
+        *reinterpret_cast<uint4*>(Vt + key * D + 8 * (piece ^ vtile_swizzle<D>(key))) = rv[u];
       }
     }
   };
@@ -490,7 +504,11 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const half8 av = as_h8(*reinterpret_cast<const uint4*>(Vt + (16 * cb + lj) * VSTR + 8 * (lq ^ (cb & 3))));
+        const uint16_t* vp = vbase + 8 * ((2 * cb + ((lj & 3) >> 1)) ^ vsw);
+        typedef __attribute__((address_space(3))) short4v lds_s4;
+        const half4v a0 = __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)vp));
+        const half4v a1 = __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 4 * D)));
+        const half8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         O[rb][cb] = mfma16(av, ph, O[rb][cb]);
       }
     }
@@ -680,7 +698,7 @@ static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipS
 }
 
 int kvpop_prefill_attend_lds(int D, int list_cap) {
-  return (32 * (D + 8) + D * 40) * 2 + ((list_cap + 31) & ~31) * 8;
+  return (32 * (D + 8) + 32 * D) * 2 + ((list_cap + 31) & ~31) * 8;
 }
 
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
