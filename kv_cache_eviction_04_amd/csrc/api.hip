@@ -615,7 +615,7 @@ int kvpop_prefill_enqueue(confkv_handle* h, void* stream, int32_t seq_len, const
                           const uint16_t* v, const float* prio, uint16_t* out, float* lse, void* workspace) {
   const PrefillSizes z = prefill_sizes(h, seq_len);
   const int cap = prefill_list_cap(h, seq_len);
-  if (kvpop_prefill_attend_lds(h->lay.D, cap) > fused_max_dynamic_lds()) return CONFKV_EINVAL;
+  if (kvpop_prefill_attend_lds(h->lay.D, cap, true) > fused_max_dynamic_lds()) return CONFKV_EINVAL;
   KvpopPrefillArgs pa;
   memset(&pa, 0, sizeof(pa));
   pa.B = h->lay.B;

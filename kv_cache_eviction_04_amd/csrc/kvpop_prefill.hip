@@ -235,6 +235,21 @@ __device__ __forceinline__ int vtile_swizzle(int r) {
   return D == 128 ? 2 * ((r & 3) | (((r >> 3) & 1) << 2)) : 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
 }
 
+// 16-byte piece swizzle of row r of the LDS K tile (rows of D halves, no
+// padding). QK reads one piece of 16 rows per 16-lane group: rows
+// 8(j/4) + j%4 (+4) for lane j, which differ in bits 0, 1, 3 and 4; XOR-ing
+// the piece index with those bits puts the 16 reads on distinct banks (D =
+// 128; at D = 64, two rows per bank line, bits 1, 3 and 4).
+template <int D>
+__device__ __forceinline__ int ktile_swizzle(int r) {
+  return D == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+}
+
+// LDS of one chunk buffer of the prefill attention: K then V, 32 rows of D
+// halves each.
+template <int D>
+constexpr int kChunkHalves = 2 * 32 * D;
+
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 
@@ -242,8 +257,10 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 // when a wave serves two query heads). The key list holds the sinks, the
 // long-range keys that pass the first query's threshold (a superset for the
 // later queries, whose thresholds are no larger), and the contiguous run
-// [q0 - w, q1). Per 32-key chunk the K rows and V rows (both row-major, V's
-// pieces swizzled) go through LDS once for all the workgroup's queries. With 8
+// [q0 - w, q1). Per 32-key chunk the K rows and V rows (row-major, 16-byte
+// pieces swizzled per row) go through LDS once for all the workgroup's
+// queries, loaded straight from global memory into one of two buffers
+// while the other is computed. With 8
 // waves (groups of up to 4 query heads) wave w takes head w % 4 for the 16
 // queries of block w / 4; with 4 waves (larger groups) wave w takes heads w,
 // w+4, ... for 16 queries. Per row block: S^T = K Q^T on MFMA, the predicate
@@ -251,7 +268,7 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 // O^T = V^T P^T with the weights rounded once to fp16 (the sums l stay
 // fp32, so the LSE is not affected).
 template <int D, int G, int NT>
-__global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
+__global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
   constexpr int KS = D / 32, NCB = D / 16;
   constexpr int NW = NT / 64;                   // waves
   constexpr bool kWavePerBlock = NW == 8;       // 8 waves: one (head, 16-query block) per wave
@@ -260,14 +277,14 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
   constexpr int QT = kWavePerBlock ? 1 : (HPW == 1 ? 2 : 1);     // 16-query blocks per head and wave
   constexpr int QB = kWavePerBlock ? 32 : 16 * QT;               // queries per workgroup
   constexpr int NR = HPW * QT;                  // 16-row blocks per wave
-  constexpr int KSTR = D + 8;   // K tile row stride (halves)
-  static_assert(D == 64 || D == 128, "V tile swizzle");
-  constexpr int PIECES = 32 * D / 8;               // 16-byte pieces of a 32-row tile
+  static_assert(D == 64 || D == 128, "tile swizzles");
+  constexpr int PIECES = kChunkHalves<D> / 8;      // 16-byte pieces of a chunk: K then V
   constexpr int PPT = (PIECES + NT - 1) / NT;
-  extern __shared__ __align__(16) uint16_t plds[];
-  uint16_t* Kt = plds;                        // [32][KSTR]
-  uint16_t* Vt = Kt + 32 * KSTR;              // [32][D], pieces swizzled
-  int32_t* lpos = reinterpret_cast<int32_t*>(Vt + 32 * D);
+  // two chunk buffers, distinct objects: the compiler then sees that the
+  // reads of one never wait for the loads in flight into the other
+  __shared__ __align__(16) uint16_t cbuf0[kChunkHalves<D>], cbuf1[kChunkHalves<D>];
+  extern __shared__ __align__(16) int32_t plds[];
+  int32_t* lpos = plds;
   int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
   __shared__ uint32_t red[NW];
 
@@ -389,31 +406,35 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
   // swizzle), columns 16cb + 4(lj%4) .. +3
   const int vrow = 8 * lq + (lj >> 2);
   const int vsw = vtile_swizzle<D>(vrow);
-  const uint16_t* vbase = Vt + vrow * D + 4 * (lj & 1);
+  const int voff = 32 * D + vrow * D + 4 * (lj & 1);  // halves into a chunk buffer
 
-  // ---- 32-key chunks: rows of the next chunk are loaded while this one is computed
-  uint4 rk[PPT], rv[PPT];
-  auto load_chunk = [&](int c) {
+  // ---- 32-key chunks, loaded global -> LDS (gfx950): lane l of a wave
+  // writes the 16 bytes at the wave's LDS base + 16 l, so piece e of the
+  // buffer (K pieces, then V pieces, row by row) is loaded by the thread
+  // NT u + e and holds the global piece that the row's swizzle maps there.
+  // Keys past the list's end repeat its last entry (masked).
+  // The list reads that give the addresses come first, the loads after: an
+  // LDS read issued behind a load into LDS waits for it unless the compiler
+  // can tell the two apart, which it cannot for the (dynamic) lists.
+  auto issue_chunk = [&](int c, uint16_t* buf) {
+    const uint16_t* src[PPT];
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int e = tid + NT * u;
-      if (PIECES % NT == 0 || e < PIECES) {
-        const int key = e / (D / 8), piece = e - key * (D / 8);
-        const int li = 32 * c + key;
-        const int pos = li < nkc ? lpos[li] : 0;
-        rk[u] = *reinterpret_cast<const uint4*>(kseg + (size_t)pos * D + 8 * piece);
-        rv[u] = *reinterpret_cast<const uint4*>(vseg + (size_t)pos * D + 8 * piece);
-      }
+      const bool isv = e >= PIECES / 2;
+      const int pe = isv ? e - PIECES / 2 : e;
+      const int row = pe / (D / 8), slot = pe - row * (D / 8);
+      const int pos = lpos[min(32 * c + row, nkc - 1)];
+      const int piece = slot ^ (isv ? vtile_swizzle<D>(row) : ktile_swizzle<D>(row));
+      src[u] = (isv ? vseg : kseg) + (size_t)pos * D + 8 * piece;
     }
-  };
-  auto store_chunk = [&]() {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int e = tid + NT * u;
       if (PIECES % NT == 0 || e < PIECES) {
-        const int key = e / (D / 8), piece = e - key * (D / 8);
-        *reinterpret_cast<uint4*>(Kt + key * KSTR + 8 * piece) = rk[u];
-        *reinterpret_cast<uint4*>(Vt + key * D + 8 * (piece ^ vtile_swizzle<D>(key))) = rv[u];
+        const int wbase = __builtin_amdgcn_readfirstlane(8 * (tid - lane + NT * u));  // halves, wave-uniform
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src[u],
+                                         (__attribute__((address_space(3))) void*)(buf + wbase), 16, 0, 0);
       }
     }
   };
@@ -424,11 +445,12 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
   const int thr_min = thr[q1 - 1];
   const int easy_end = min(q0 + 1, g_end);
   const int nchunks = (nkc + 31) >> 5;
-  if (nchunks > 0) load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    store_chunk();
+  // one chunk: wait for this wave's loads of it, barrier (every wave's loads
+  // landed; every wave is done with the other buffer), start the next
+  // chunk's loads into the other buffer, compute this one
+  auto step = [&](const int c, const uint16_t* buf, uint16_t* nbuf) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
     // this lane's eight keys of the chunk: list entries 32c + 8lq .. +7
     int kpos[8], krank[8];
     {
@@ -447,6 +469,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
         krank[e] = rr[e];
       }
     }
+    if (c + 1 < nchunks) issue_chunk(c + 1, nbuf);
     bool easy = true;
 #pragma unroll
     for (int e = 0; e < 8; ++e) easy = easy && kpos[e] < easy_end && krank[e] <= thr_min;
@@ -459,10 +482,12 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         acc[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t* kr = Kt + (kperm0 + 4 * kb) * KSTR;
+        const int krow = kperm0 + 4 * kb;
+        const uint16_t* kr = buf + krow * D;
+        const int ksw = ktile_swizzle<D>(krow);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-          acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * (lq + 4 * kk))), qb[rb][kk], acc[kb]);
+          acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * ((lq + 4 * kk) ^ ksw))), qb[rb][kk], acc[kb]);
       }
       float sc[8];
       float mt = -INFINITY;
@@ -504,7 +529,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
       }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* vp = vbase + 8 * ((2 * cb + ((lj & 3) >> 1)) ^ vsw);
+        const uint16_t* vp = buf + voff + 8 * ((2 * cb + ((lj & 3) >> 1)) ^ vsw);
         typedef __attribute__((address_space(3))) short4v lds_s4;
         const half4v a0 = __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)vp));
         const half4v a1 = __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 4 * D)));
@@ -512,7 +537,11 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 2 : 3) kvpop_prefill_attend_ke
         O[rb][cb] = mfma16(av, ph, O[rb][cb]);
       }
     }
-    __syncthreads();
+  };
+  if (nchunks > 0) issue_chunk(0, cbuf0);
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, cbuf0, cbuf1);
+    if (c + 1 < nchunks) step(c + 1, cbuf1, cbuf0);
   }
   // ---- output rows and LSE (natural log: m * ln 2 + ln l). Lane (lq, lj)
   // holds O^T[column 16cb + 4lq + r][query lj].
@@ -697,8 +726,10 @@ static int launch_kvpop_attend_d(const KvpopPrefillArgs& pa, int lds_bytes, hipS
   return ok_or_err();
 }
 
-int kvpop_prefill_attend_lds(int D, int list_cap) {
-  return (32 * (D + 8) + 32 * D) * 2 + ((list_cap + 31) & ~31) * 8;
+// LDS of the attention kernel: the key lists (dynamic) and, with
+// with_buffers, the two chunk buffers (static).
+int kvpop_prefill_attend_lds(int D, int list_cap, bool with_buffers) {
+  return ((list_cap + 31) & ~31) * 8 + (with_buffers ? 2 * 2 * 32 * D * 2 : 0);
 }
 
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
@@ -708,7 +739,7 @@ int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
   if (hipGetLastError() != hipSuccess) return -3;
   hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
-  const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap);
+  const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap, false);
   if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
   if (pa.D == 128) return launch_kvpop_attend_d<128>(pa, lds, s);
   return -1;

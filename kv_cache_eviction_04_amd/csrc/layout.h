@@ -174,7 +174,7 @@ int launch_read_cache(const Layout& lay, int32_t seg_first, int32_t seg_count, i
 int launch_stats_total(const Layout& lay, int32_t reset, void* stream);
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream);
 int launch_kvpop_target(const KvpopPrefillArgs& pa, const float* lse, float* target, void* stream);
-int kvpop_prefill_attend_lds(int D, int list_cap);
+int kvpop_prefill_attend_lds(int D, int list_cap, bool with_buffers);
 int fused_max_dynamic_lds();
 
 }  // namespace confkv
