@@ -8,6 +8,7 @@
 namespace confkv {
 
 constexpr int kRankBlock = 8192;  // keys per LDS block of the rank sort (64 KB)
+constexpr int kMaxChunks = 1024;  // 32-key chunks of one query tile's key list, at most
 
 // ==================================================== KVpop prefill mask
 // [KVpop summary §2.4] The k long-range slots follow a running threshold over
@@ -318,6 +319,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   int32_t* lpos = plds;
   int32_t* lrank = lpos + ((pa.list_cap + 31) & ~31);  // 16-byte aligned for vector reads
   __shared__ uint32_t red[NW];
+  __shared__ uint32_t easy_bits[kMaxChunks / 32];  // chunk c: bit c % 32 of word c / 32
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -397,6 +399,31 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   if (tid == 0 && nk > pa.list_cap) atomicOr(pa.err, kErrInternal);  // cannot happen: host bound
   __syncthreads();
   const int nkc = min(nk, pa.list_cap);
+  const int nchunks = (nkc + 31) >> 5;
+
+  // Thresholds do not increase with the query, so thr(q1 - 1) is the
+  // tile's smallest: a key at or before q0 and below g_end (a sink, or a
+  // long-range key) whose rank passes it is allowed for every query of the
+  // tile, and a chunk of such keys needs no per-pair predicate. Thread c
+  // decides chunk c; the flags go to an LDS bitmask.
+  const int thr_min = thr[q1 - 1];
+  const int easy_end = min(q0 + 1, g_end);
+  for (int c0 = 0; c0 < nchunks; c0 += NT) {
+    const int c = c0 + tid;
+    bool easy = c < nchunks;
+    if (easy) {
+      for (int e = 0; e < 32 && easy; ++e) {
+        const int li = 32 * c + e;
+        easy = li < nkc && lpos[li] < easy_end && lrank[li] <= thr_min;
+      }
+    }
+    const uint64_t bal = __ballot(easy);
+    if (lane == 0) {
+      easy_bits[(c0 >> 5) + 2 * wave] = (uint32_t)bal;
+      easy_bits[(c0 >> 5) + 2 * wave + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();
 
   // ---- row blocks of this wave: head rb_head(rb), query block rb_qblk(rb). The
   // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
@@ -469,22 +496,18 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       }
     }
   };
-  // Thresholds do not increase with the query, so thr(q1 - 1) is the
-  // tile's smallest: a key at or before q0 and below g_end (a sink, or a
-  // long-range key) whose rank passes it is allowed for every query of the
-  // tile, and a chunk of such keys needs no per-pair predicate.
-  const int thr_min = thr[q1 - 1];
-  const int easy_end = min(q0 + 1, g_end);
-  const int nchunks = (nkc + 31) >> 5;
   // one chunk: wait for this wave's loads of it, barrier (every wave's loads
   // landed; every wave is done with the other buffer), start the next
   // chunk's loads into the other buffer, compute this one
   auto step = [&](const int c, const uint16_t* buf, uint16_t* nbuf) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    // this lane's eight keys of the chunk: list entries 32c + 8lq .. +7
+    const bool chunk_easy = (__builtin_amdgcn_readfirstlane(easy_bits[c >> 5]) >> (c & 31)) & 1u;
+    // this lane's eight keys of the chunk (list entries 32c + 8lq .. +7), for
+    // the per-pair predicate of a chunk that needs it. List reads come
+    // before the loads into LDS are issued (see issue_chunk).
     int kpos[8], krank[8];
-    {
+    if (!chunk_easy) {
       const int li0 = 32 * c + 8 * lq;
       const uint4 p0 = *reinterpret_cast<const uint4*>(lpos + li0);
       const uint4 p1 = *reinterpret_cast<const uint4*>(lpos + li0 + 4);
@@ -501,10 +524,6 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       }
     }
     if (c + 1 < nchunks) issue_chunk(c + 1, nbuf);
-    bool easy = true;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) easy = easy && kpos[e] < easy_end && krank[e] <= thr_min;
-    const bool chunk_easy = __all(easy);
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb) {
       if (!active(rb)) continue;
@@ -520,12 +539,16 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
         for (int kk = 0; kk < KS; ++kk)
           acc[kb] = mfma16(as_h8(*reinterpret_cast<const uint4*>(kr + 8 * ((lq + 4 * kk) ^ ksw))), qb[rb][kk], acc[kb]);
       }
+      // raw scores (masked pairs -inf); the scale goes into the maximum
+      // (rounding is monotone, so the scaled maximum is the maximum of the
+      // scaled scores) and into one FMA per weight
       float sc[8];
       float mt = -INFINITY;
       if (chunk_easy) {
+        const bool rows_in = q0 + 16 * (rb_qblk(rb) + 1) <= q1;  // every query of the block exists
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          sc[e] = qr < q1 ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+          sc[e] = rows_in || qr < q1 ? acc[e >> 2][e & 3] : -INFINITY;
           mt = fmaxf(mt, sc[e]);
         }
       } else {
@@ -533,11 +556,11 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
         for (int e = 0; e < 8; ++e) {
           const int j = kpos[e];
           const bool ok = qr < q1 && j <= qr && (j < s || j >= qr - w || krank[e] <= thr_q[rb]);
-          sc[e] = ok ? acc[e >> 2][e & 3] * sl2 : -INFINITY;
+          sc[e] = ok ? acc[e >> 2][e & 3] : -INFINITY;
           mt = fmaxf(mt, sc[e]);
         }
       }
-      mt = rows_max(mt);
+      mt = rows_max(mt) * sl2;
       const float mn = fmaxf(m[rb], mt);
       const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
       const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
@@ -545,7 +568,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       half8 ph;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sc[e] - ms);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -ms));
         ls += pe;
         ph[e] = (_Float16)pe;
       }
