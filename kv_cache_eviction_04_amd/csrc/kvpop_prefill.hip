@@ -9,6 +9,8 @@ namespace confkv {
 
 constexpr int kRankBlock = 8192;  // keys per LDS block of the rank sort (64 KB)
 constexpr int kMaxChunks = 1024;  // 32-key chunks of one query tile's key list, at most
+constexpr int kThrChunk = 1024;   // queries per workgroup of the threshold pass (a multiple of 256)
+constexpr int kThrThreads = 256;
 
 // ==================================================== KVpop prefill mask
 // [KVpop summary §2.4] The k long-range slots follow a running threshold over
@@ -94,7 +96,16 @@ __global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
 // n >= k a rank above thr is never the threshold again (thr only moves
 // down, and the search for the next rank runs below it), so it is not
 // entered in the bitmap.
-// One wave per segment walks the queries in batches of 64: lane i loads the
+// The state before any query a follows from its definition, not only from
+// the walk: the candidates are then the M = a - 1 - w - s positions
+// [s, a-2-w] (position a-1-w joins at query a), thr is their k-th smallest
+// rank (S while M < k), and a bitmap holding all their ranks serves as well
+// as the walk's (the ranks above thr that it also holds are never visited).
+// So each workgroup takes one chunk of 1024 queries of a segment: its 256
+// threads enter the ranks that precede the chunk's first query into the
+// bitmap and find thr there by a scan over the words' popcounts, and then
+// one wave walks the chunk.
+// The wave walks the chunk's queries in batches of 64: lane i loads the
 // rank that joins at query q0 + i (four batches at a time, loaded a group
 // ahead), and lane i keeps the threshold of query q0 + i until the batch is
 // stored. A batch that leaves n below k only enters its ranks; the batch in
@@ -108,17 +119,61 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
   return v;
 }
-__global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
+__global__ void __launch_bounds__(kThrThreads) kvpop_threshold_kernel(KvpopPrefillArgs pa) {
   extern __shared__ uint32_t kbits[];  // ceil(N/32) words
-  const int lane = threadIdx.x, seg = blockIdx.x;
+  __shared__ uint32_t red[kThrThreads / 64];
+  __shared__ int sh_t, sh_max;
+  const int tid = threadIdx.x, lane = tid & 63, seg = blockIdx.y;
   const int S = pa.S, s = pa.sinks, w = pa.window, k = pa.topk, nw = (pa.N + 31) >> 5;
+  const int a = blockIdx.x * kThrChunk, b_end = min(a + kThrChunk, S);  // this chunk's queries
   const int32_t* rank = pa.rank + (size_t)seg * S;
   int32_t* thr = pa.thr + (size_t)seg * S;
-  for (int i = lane; i < nw; i += 64) kbits[i] = 0u;
+  for (int i = tid; i < nw; i += kThrThreads) kbits[i] = 0u;
+  if (tid == 0) sh_max = -1;
   __syncthreads();
-  int n = 0, t = k > 0 ? S : -1, maxr = -1;
+  // ---- the state before query a: the ranks of positions [s, s + M)
+  const int M = max(0, a - 1 - w - s);
+  int mx = -1;
+  for (int i = tid; i < M; i += kThrThreads) {
+    const int r = rank[s + i];
+    atomicOr(&kbits[r >> 5], 1u << (r & 31));
+    mx = max(mx, r);
+  }
+  mx = wave_max_i32(mx);
+  if (lane == 0) atomicMax(&sh_max, mx);
+  __syncthreads();
+  if (k > 0 && M >= k) {
+    // thr(a): the k-th smallest entered rank. Each thread counts a run of
+    // words; the one whose run holds the k-th set bit finds it.
+    const int wpt = (nw + kThrThreads - 1) / kThrThreads;
+    const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
+    uint32_t cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __popc(kbits[i]);
+    uint32_t total;
+    const uint32_t excl = block_excl_scan_u32<kThrThreads / 64>(cnt, red, &total);
+    if (excl < (uint32_t)k && (uint32_t)k <= excl + cnt) {
+      uint32_t acc = excl;
+      for (int i = w0; i < w1; ++i) {
+        uint32_t word = kbits[i];
+        const uint32_t pc = __popc(word);
+        if (acc + pc >= (uint32_t)k) {
+          for (uint32_t j = acc + 1; j < (uint32_t)k; ++j) word &= word - 1;  // drop the lower set bits
+          sh_t = (i << 5) + __builtin_ctz(word);
+          break;
+        }
+        acc += pc;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid >= 64) return;  // one wave walks the chunk
+  int n = M, t = k > 0 ? (M >= k ? sh_t : S) : -1, maxr = sh_max;
   int wt = 0;        // the bitmap word holding thr once n >= k,
   uint32_t ct = 0u;  // and a copy of it kept up to date
+  if (k > 0 && M >= k) {
+    wt = t >> 5;
+    ct = kbits[wt];
+  }
   // insert rank r below thr and move thr to the next candidate rank below it
   auto move = [&](int r) {
     const uint32_t bit = 1u << (r & 31);
@@ -136,20 +191,20 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
   };
   auto rank_at = [&](int q0) {
     const int q = q0 + lane, p = q - 1 - w;
-    return (q < S && p >= s) ? rank[p] : -2;
+    return (q < b_end && p >= s) ? rank[p] : -2;
   };
   constexpr int NB = 4;  // batches whose ranks are loaded together
   int rv[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) rv[j] = rank_at(64 * j);
-  for (int g0 = 0; g0 < S; g0 += 64 * NB) {
+  for (int j = 0; j < NB; ++j) rv[j] = rank_at(a + 64 * j);
+  for (int g0 = a; g0 < b_end; g0 += 64 * NB) {
     int rn[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) rn[j] = g0 + 64 * (NB + j) < S ? rank_at(g0 + 64 * (NB + j)) : -2;
+    for (int j = 0; j < NB; ++j) rn[j] = g0 + 64 * (NB + j) < b_end ? rank_at(g0 + 64 * (NB + j)) : -2;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int q0 = g0 + 64 * j, q = q0 + lane;
-      if (q0 >= S) break;
+      if (q0 >= b_end) break;
       const int r_l = rv[j];
       int tv = t;
       const uint64_t valid = __ballot(r_l >= 0);
@@ -174,7 +229,7 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
         maxr = max(maxr, wave_max_i32(r_l));
         n += nv;
       } else {
-        const int cnt = min(64, S - q0);
+        const int cnt = min(64, b_end - q0);
         for (int i = 0; i < cnt; ++i) {
           const int r = __builtin_amdgcn_readlane(r_l, i);
           if (r >= 0 && k > 0) {
@@ -194,7 +249,7 @@ __global__ void __launch_bounds__(64) kvpop_threshold_kernel(KvpopPrefillArgs pa
           tv = lane == i ? t : tv;
         }
       }
-      if (q < S) thr[q] = tv;
+      if (q < b_end) thr[q] = tv;
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) rv[j] = rn[j];
@@ -791,7 +846,8 @@ int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
   const int segs = pa.B * pa.Hkv;
   hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), (size_t)std::min(pa.N, kRankBlock) * 8, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3(segs), dim3(64), ((pa.N + 31) / 32) * 4, s, pa);
+  hipLaunchKernelGGL(kvpop_threshold_kernel, dim3((pa.S + kThrChunk - 1) / kThrChunk, segs), dim3(kThrThreads),
+                     ((pa.N + 31) / 32) * 4, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
   const int lds = kvpop_prefill_attend_lds(pa.D, pa.list_cap, false);
   if (pa.D == 64) return launch_kvpop_attend_d<64>(pa, lds, s);
