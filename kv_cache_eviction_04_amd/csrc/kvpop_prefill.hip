@@ -28,62 +28,71 @@ constexpr int kThrThreads = 256;
 // bitonic network over the segment's N (a power of two) keys in the
 // workspace, then rank[position] = sorted index (-1 for sinks). A pass
 // (k, jj) compares i with i ^ jj, so every pass with jj below the block size
-// B (up to 8192 keys, 64 KB) pairs keys of one block: those run in LDS, a
-// block at a time (the whole sort of each block first, then for each larger
-// k the passes below B), and only the passes with jj >= B go through global
-// memory. Direction: descending where i & k is 0.
+// B (up to 8192 keys, 64 KB) pairs keys of one block: those run in LDS, and
+// only the passes with jj >= B go through global memory. Direction:
+// descending where i & k is 0. Two launches: the first sorts every block
+// (k = 2 .. B) with one workgroup per (block, segment); the second, one
+// workgroup per segment, runs each larger k (its global passes, then its
+// passes below B block by block in LDS) and scatters the ranks.
+__device__ __forceinline__ void rank_cmpx(uint64_t* X, int i, int ixj, int gi, int k) {
+  const uint64_t a = X[i], b = X[ixj];
+  const bool desc = (gi & k) == 0;
+  if (desc ? (a < b) : (a > b)) {
+    X[i] = b;
+    X[ixj] = a;
+  }
+}
+// passes (k, jj) for jj from min(k, B)/2 down to 1 on block b in LDS, for k
+// from 2 to B (k0 = 0: the block's own sort, loading the keys from the
+// priorities) or for k = k0 alone (the keys from the workspace)
+__device__ void rank_block_passes(const KvpopPrefillArgs& pa, uint64_t* sblk, int seg, int b, int k0) {
+  const int tid = threadIdx.x;
+  const int S = pa.S, s = pa.sinks, N = pa.N, B = min(N, kRankBlock);
+  const float* pr = pa.prio + (size_t)seg * S;
+  uint64_t* A = pa.sort + (size_t)seg * N;
+  const int base = b * B;
+  for (int i = tid; i < B; i += 1024) {
+    const int j = s + base + i;
+    if (k0 == 0) {
+      sblk[i] = j < S ? rank_key(pr[j], j) : 0ull;  // padding sorts last
+      if (j < S && !isfinite(pr[j])) atomicOr(pa.err, kErrNonFinite);
+    } else {
+      sblk[i] = A[base + i];
+    }
+  }
+  __syncthreads();
+  for (int k = k0 ? k0 : 2; k <= (k0 ? k0 : B); k <<= 1) {
+    for (int jj = min(k, B) >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < B; i += 1024) {
+        const int ixj = i ^ jj;
+        if (ixj > i) rank_cmpx(sblk, i, ixj, base + i, k);
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < B; i += 1024) A[base + i] = sblk[i];
+  __syncthreads();
+}
+__global__ void __launch_bounds__(1024) kvpop_rank_blocks_kernel(KvpopPrefillArgs pa) {
+  extern __shared__ uint64_t sblk[];  // [B]
+  rank_block_passes(pa, sblk, blockIdx.y, blockIdx.x, 0);
+}
 __global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
   extern __shared__ uint64_t sblk[];  // [B]
   const int tid = threadIdx.x, seg = blockIdx.x;
   const int S = pa.S, s = pa.sinks, N = pa.N, B = min(N, kRankBlock);
-  const float* pr = pa.prio + (size_t)seg * S;
   uint64_t* A = pa.sort + (size_t)seg * N;
   int32_t* rank = pa.rank + (size_t)seg * S;
   for (int j = tid; j < min(s, S); j += 1024) rank[j] = -1;
-  auto cmpx = [](uint64_t* X, int i, int ixj, int gi, int k) {
-    const uint64_t a = X[i], b = X[ixj];
-    const bool desc = (gi & k) == 0;
-    if (desc ? (a < b) : (a > b)) {
-      X[i] = b;
-      X[ixj] = a;
-    }
-  };
-  // passes (k, jj) for jj from jj0 down to 1 on block b in LDS; k0 = 0 runs
-  // the block's whole sort (k = 2 .. B)
-  auto block_passes = [&](int b, int k0, bool fill) {
-    const int base = b * B;
-    for (int i = tid; i < B; i += 1024) {
-      const int j = s + base + i;
-      if (fill) {
-        sblk[i] = j < S ? rank_key(pr[j], j) : 0ull;  // padding sorts last
-        if (j < S && !isfinite(pr[j])) atomicOr(pa.err, kErrNonFinite);
-      } else {
-        sblk[i] = A[base + i];
-      }
-    }
-    __syncthreads();
-    for (int k = k0 ? k0 : 2; k <= (k0 ? k0 : B); k <<= 1) {
-      for (int jj = min(k, B) >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < B; i += 1024) {
-          const int ixj = i ^ jj;
-          if (ixj > i) cmpx(sblk, i, ixj, base + i, k);
-        }
-        __syncthreads();
-      }
-    }
-    for (int i = tid; i < B; i += 1024) A[base + i] = sblk[i];
-    __syncthreads();
-  };
-  for (int b = 0; b < N / B; ++b) block_passes(b, 0, true);
   for (int k = 2 * B; k <= N; k <<= 1) {
     for (int jj = k >> 1; jj >= B; jj >>= 1) {
       for (int i = tid; i < N; i += 1024) {
         const int ixj = i ^ jj;
-        if (ixj > i) cmpx(A, i, ixj, i, k);
+        if (ixj > i) rank_cmpx(A, i, ixj, i, k);
       }
       __syncthreads();
     }
-    for (int b = 0; b < N / B; ++b) block_passes(b, k, false);
+    for (int b = 0; b < N / B; ++b) rank_block_passes(pa, sblk, seg, b, k);
   }
   for (int i = tid; i < S - s; i += 1024) rank[0xFFFFFFFFu - (uint32_t)A[i]] = i;
 }
@@ -844,7 +853,10 @@ int kvpop_prefill_attend_lds(int D, int list_cap, bool with_buffers) {
 int launch_kvpop_prefill(const KvpopPrefillArgs& pa, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int segs = pa.B * pa.Hkv;
-  hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), (size_t)std::min(pa.N, kRankBlock) * 8, s, pa);
+  const int rb = std::min(pa.N, kRankBlock);
+  hipLaunchKernelGGL(kvpop_rank_blocks_kernel, dim3(pa.N / rb, segs), dim3(1024), (size_t)rb * 8, s, pa);
+  if (hipGetLastError() != hipSuccess) return -3;
+  hipLaunchKernelGGL(kvpop_rank_kernel, dim3(segs), dim3(1024), (size_t)rb * 8, s, pa);
   if (hipGetLastError() != hipSuccess) return -3;
   hipLaunchKernelGGL(kvpop_threshold_kernel, dim3((pa.S + kThrChunk - 1) / kThrChunk, segs), dim3(kThrThreads),
                      ((pa.N + 31) / 32) * 4, s, pa);
