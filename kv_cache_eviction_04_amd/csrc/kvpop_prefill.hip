@@ -402,48 +402,95 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   const int n_sink = min(s, q1);
   const int g_end = max(s, q0 - w);            // long-range positions [s, g_end)
   const int thr0 = thr[q0];
-  // Each thread scans a run of ranks that starts 16-byte aligned in memory
-  // (at most 3 before s: the previous segment's, or for the first segment
-  // none before the array), 16 ranks per round as four 16-byte loads in
-  // flight. A round starts below g_end <= S and may read up to 15 ranks
-  // past the segment's end: the next segment's, or for the last segment the
-  // start of the thresholds, which follow the ranks in the workspace. Ranks
-  // before s and from g_end on are skipped. Count, scan, then write in
-  // ascending position order.
-  const int a0 = s - (int)(((size_t)seg * S + s) & 3);  // rank + a0 is 16-byte aligned
-  const int span = g_end - a0;
-  const int per = (((span + NT - 1) / NT) + 15) & ~15;
-  const int ga = a0 + min(span, tid * per), gb = a0 + min(span, tid * per + per);
-  auto load16 = [&](int j, int (&r)[16]) {
+  // The long-range keys are the positions in [s, g_end) whose rank is at
+  // most thr0. Two ways to find them, whichever reads fewer bytes: the
+  // ranks of [s, g_end) (4 bytes each), or the sorted keys of ranks
+  // 0 .. thr0 (8 bytes each; the rank sort leaves rank i's key at entry i),
+  // keeping those below g_end. Late tiles take the second: their top-k set
+  // is a small share of the positions before them.
+  const int nr = max(0, min(thr0 + 1, S - s));
+  const bool by_rank = 2 * nr < g_end - s && pa.N >= 2;
+  uint32_t cnt = 0, ng, off;
+  if (by_rank) {
+    // Each thread takes a run of 8 sorted entries per round (four 16-byte
+    // loads; entry 0 is 16-byte aligned as N >= 2); a round may read up to
+    // 7 entries past nr, inside the segment's N entries or the workspace's
+    // next part (the ranks). Count, scan, then write in rank order.
+    const uint64_t* A = pa.sort + (size_t)seg * pa.N;
+    const int per = (((nr + NT - 1) / NT) + 7) & ~7;
+    const int ia = min(nr, tid * per), ib = min(nr, tid * per + per);
+    auto load8 = [&](int i, uint64_t (&kv)[8]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int4 v = *reinterpret_cast<const int4*>(rank + j + 4 * u);
-      r[4 * u] = v.x;
-      r[4 * u + 1] = v.y;
-      r[4 * u + 2] = v.z;
-      r[4 * u + 3] = v.w;
+      for (int u = 0; u < 4; ++u) {
+        const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(A + i + 2 * u);
+        kv[2 * u] = v.x;
+        kv[2 * u + 1] = v.y;
+      }
+    };
+    for (int i = ia; i < ib; i += 8) {
+      uint64_t kv[8];
+      load8(i, kv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cnt += (i + e < ib && (int)(0xFFFFFFFFu - (uint32_t)kv[e]) < g_end) ? 1u : 0u;
     }
-  };
-  uint32_t cnt = 0;
-  for (int j = ga; j < gb; j += 16) {
-    int r[16];
-    load16(j, r);
+    off = block_excl_scan_u32<NW>(cnt, red, &ng);
+    for (int i = ia; i < ib; i += 8) {
+      uint64_t kv[8];
+      load8(i, kv);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) cnt += (j + e >= s && j + e < gb && r[e] <= thr0) ? 1u : 0u;
-  }
-  uint32_t ng;
-  uint32_t off = block_excl_scan_u32<NW>(cnt, red, &ng);
-  for (int j = ga; j < gb; j += 16) {
-    int r[16];
-    load16(j, r);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (j + e >= s && j + e < gb && r[e] <= thr0) {
-        if (n_sink + (int)off < pa.list_cap) {
-          lpos[n_sink + off] = j + e;
-          lrank[n_sink + off] = r[e];
+      for (int e = 0; e < 8; ++e) {
+        const int pos = (int)(0xFFFFFFFFu - (uint32_t)kv[e]);
+        if (i + e < ib && pos < g_end) {
+          if (n_sink + (int)off < pa.list_cap) {
+            lpos[n_sink + off] = pos;
+            lrank[n_sink + off] = i + e;
+          }
+          ++off;
         }
-        ++off;
+      }
+    }
+  } else {
+    // Each thread scans a run of ranks that starts 16-byte aligned in memory
+    // (at most 3 before s: the previous segment's, or for the first segment
+    // none before the array), 16 ranks per round as four 16-byte loads in
+    // flight. A round starts below g_end <= S and may read up to 15 ranks
+    // past the segment's end: the next segment's, or for the last segment
+    // the start of the thresholds, which follow the ranks in the workspace.
+    // Ranks before s and from g_end on are skipped. Count, scan, then write
+    // in ascending position order.
+    const int a0 = s - (int)(((size_t)seg * S + s) & 3);  // rank + a0 is 16-byte aligned
+    const int span = g_end - a0;
+    const int per = (((span + NT - 1) / NT) + 15) & ~15;
+    const int ga = a0 + min(span, tid * per), gb = a0 + min(span, tid * per + per);
+    auto load16 = [&](int j, int (&r)[16]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int4 v = *reinterpret_cast<const int4*>(rank + j + 4 * u);
+        r[4 * u] = v.x;
+        r[4 * u + 1] = v.y;
+        r[4 * u + 2] = v.z;
+        r[4 * u + 3] = v.w;
+      }
+    };
+    for (int j = ga; j < gb; j += 16) {
+      int r[16];
+      load16(j, r);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cnt += (j + e >= s && j + e < gb && r[e] <= thr0) ? 1u : 0u;
+    }
+    off = block_excl_scan_u32<NW>(cnt, red, &ng);
+    for (int j = ga; j < gb; j += 16) {
+      int r[16];
+      load16(j, r);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (j + e >= s && j + e < gb && r[e] <= thr0) {
+          if (n_sink + (int)off < pa.list_cap) {
+            lpos[n_sink + off] = j + e;
+            lrank[n_sink + off] = r[e];
+          }
+          ++off;
+        }
       }
     }
   }
