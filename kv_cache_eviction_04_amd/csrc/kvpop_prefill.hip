@@ -9,7 +9,7 @@ namespace confkv {
 
 constexpr int kRankBlock = 8192;  // keys per LDS block of the rank sort (64 KB)
 constexpr int kMaxChunks = 1024;  // 32-key chunks of one query tile's key list, at most
-constexpr int kThrChunk = 1024;   // queries per workgroup of the threshold pass (a multiple of 256)
+constexpr int kThrChunk = 256;    // queries per workgroup of the threshold pass (a multiple of 256)
 constexpr int kThrThreads = 256;
 
 // ==================================================== KVpop prefill mask
@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(1024) kvpop_rank_kernel(KvpopPrefillArgs pa) {
 // [s, a-2-w] (position a-1-w joins at query a), thr is their k-th smallest
 // rank (S while M < k), and a bitmap holding all their ranks serves as well
 // as the walk's (the ranks above thr that it also holds are never visited).
-// So each workgroup takes one chunk of 1024 queries of a segment: its 256
+// So each workgroup takes one chunk of 256 queries of a segment: its 256
 // threads enter the ranks that precede the chunk's first query into the
 // bitmap and find thr there by a scan over the words' popcounts, and then
 // one wave walks the chunk.

@@ -101,16 +101,17 @@ def kth_smallest_prefix(rank, S, s, w, k):
 @pytest.mark.parametrize("S,s,w,k,ties", [
     (64, 0, 0, 1, False), (65, 1, 3, 61, True), (257, 2, 5, 63, False), (300, 0, 40, 200, True),
     (513, 3, 0, 129, False), (256, 0, 0, 256, False), (700, 0, 2, 5, True),
-    # several 1024-query chunks, each starting from the state its first query defines
-    (3000, 0, 0, 1024, True), (2500, 3, 5, 1100, False), (2100, 2, 7, 0, False), (2100, 0, 0, 1, True),
-    (4097, 4, 300, 1800, False),
+    # several 256-query chunks, each starting from the state before its first query
+    (3000, 0, 0, 1024, True), (3000, 0, 0, 1279, False), (2500, 3, 5, 1100, False), (2100, 2, 7, 0, False),
+    (2100, 0, 0, 1, True), (4097, 4, 300, 1800, False),
 ])
 def test_kvpop_thresholds_at_batch_edges(S, s, w, k, ties):
     # the threshold pass walks queries in batches of 64 (groups of 256): the
     # fill-up ends (n reaches k) at different offsets inside a batch, and S
-    # ends partial batches and groups. Chunks of 1024 queries start from the
-    # state their first query defines: before the fill-up (M < k), exactly
-    # at it (M = k at query 1024) and after it
+    # ends partial batches and groups. Chunks of 256 queries start from the
+    # state before their first query: before the fill-up (M < k), with the
+    # fill-up at the chunk's first query (k = 1024), exactly at it (M = k
+    # before query 1280) and after it
     B, Hq, Hkv, d = 1, 2, 2, 64
     w_ = kvpop_cfg(Hq, Hkv, d, s, w, k, B)
     gpu = confkv.Cache(w_)
