@@ -42,6 +42,69 @@ __device__ __forceinline__ void rank_cmpx(uint64_t* X, int i, int ixj, int gi, i
     X[ixj] = a;
   }
 }
+// Passes (k, jj) for k = k_lo .. k_hi (powers of two) and jj from
+// min(k, 8192)/2 down to 1 (larger strides pair keys of different blocks and
+// are done before, in global memory) over an 8192-key block in LDS (in LDS
+// on entry and on return), 1024 threads: thread t keeps keys 8t .. 8t+7 in registers for
+// the passes with jj < 512, whose partners are in the same wave: jj < 8 in
+// the thread, 8 <= jj < 512 in lane t ^ (jj/8), exchanged by shuffles. Only
+// the passes with jj >= 512 pair keys of different waves and go through
+// LDS, with a barrier each. gbase: the block's first index in the segment.
+__device__ void rank_block_regs(uint64_t* sblk, int gbase, int k_lo, int k_hi) {
+  const int t = threadIdx.x;
+  uint64_t x[8];
+  bool in_regs = false;
+  for (int k = k_lo; k <= k_hi; k <<= 1) {
+    int jj = min(k, kRankBlock) >> 1;  // larger strides pair keys of different blocks: done before
+    for (; jj >= 512; jj >>= 1) {
+      if (in_regs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sblk[8 * t + e] = x[e];
+        __syncthreads();
+        in_regs = false;
+      }
+      for (int i = t; i < kRankBlock; i += 1024) {
+        const int ixj = i ^ jj;
+        if (ixj > i) rank_cmpx(sblk, i, ixj, gbase + i, k);
+      }
+      __syncthreads();
+    }
+    if (!in_regs) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = sblk[8 * t + e];
+      in_regs = true;
+    }
+    for (; jj >= 8; jj >>= 1) {
+      const int d = jj >> 3;
+      const bool lower = (t & d) == 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint64_t y = __shfl_xor(x[e], d, 64);
+        const bool desc = ((gbase + 8 * t + e) & k) == 0;
+        x[e] = (lower == desc) ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
+      }
+    }
+    for (; jj >= 1; jj >>= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((e & jj) == 0) {
+          const int f = e | jj;
+          const bool desc = ((gbase + 8 * t + e) & k) == 0;
+          const uint64_t a = x[e], b = x[f];
+          if (desc ? (a < b) : (a > b)) {
+            x[e] = b;
+            x[f] = a;
+          }
+        }
+      }
+    }
+  }
+  if (in_regs) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sblk[8 * t + e] = x[e];
+    __syncthreads();
+  }
+}
 // passes (k, jj) for jj from min(k, B)/2 down to 1 on block b in LDS, for k
 // from 2 to B (k0 = 0: the block's own sort, loading the keys from the
 // priorities) or for k = k0 alone (the keys from the workspace)
@@ -61,13 +124,17 @@ __device__ void rank_block_passes(const KvpopPrefillArgs& pa, uint64_t* sblk, in
     }
   }
   __syncthreads();
-  for (int k = k0 ? k0 : 2; k <= (k0 ? k0 : B); k <<= 1) {
-    for (int jj = min(k, B) >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < B; i += 1024) {
-        const int ixj = i ^ jj;
-        if (ixj > i) rank_cmpx(sblk, i, ixj, base + i, k);
+  if (B == kRankBlock) {
+    rank_block_regs(sblk, base, k0 ? k0 : 2, k0 ? k0 : B);
+  } else {
+    for (int k = k0 ? k0 : 2; k <= (k0 ? k0 : B); k <<= 1) {
+      for (int jj = min(k, B) >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < B; i += 1024) {
+          const int ixj = i ^ jj;
+          if (ixj > i) rank_cmpx(sblk, i, ixj, base + i, k);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   for (int i = tid; i < B; i += 1024) A[base + i] = sblk[i];
