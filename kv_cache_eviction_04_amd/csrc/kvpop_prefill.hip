@@ -456,6 +456,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane >> 4, lj = lane & 15;
   const int S = pa.S, s = pa.sinks, w = pa.window;
+  if (tid < kMaxChunks / 32) easy_bits[tid] = 0u;  // cleared before the list's barrier
   int tile, seg;
   xcd_tile_seg(tile, seg);
   const int b = seg / pa.Hkv, h = seg - b * pa.Hkv;
@@ -582,26 +583,54 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   // Thresholds do not increase with the query, so thr(q1 - 1) is the
   // tile's smallest: a key at or before q0 and below g_end (a sink, or a
   // long-range key) whose rank passes it is allowed for every query of the
-  // tile, and a chunk of such keys needs no per-pair predicate. Thread c
-  // decides chunk c; the flags go to an LDS bitmask.
+  // tile, and a chunk of such keys needs no per-pair predicate. Thread i
+  // checks list entry i; a wave's 64 entries are two chunks, whose flags are
+  // the halves of its ballot, ORed into an LDS bitmask.
   const int thr_min = thr[q1 - 1];
   const int easy_end = min(q0 + 1, g_end);
-  for (int c0 = 0; c0 < nchunks; c0 += NT) {
-    const int c = c0 + tid;
-    bool easy = c < nchunks;
-    if (easy) {
-      for (int e = 0; e < 32 && easy; ++e) {
-        const int li = 32 * c + e;
-        easy = li < nkc && lpos[li] < easy_end && lrank[li] <= thr_min;
-      }
-    }
-    const uint64_t bal = __ballot(easy);
+  for (int b0 = 0; b0 < 32 * nchunks; b0 += NT) {
+    const int li = b0 + tid;
+    const bool ok = li < nkc && lpos[li] < easy_end && lrank[li] <= thr_min;
+    const uint64_t bal = __ballot(ok);
     if (lane == 0) {
-      easy_bits[(c0 >> 5) + 2 * wave] = (uint32_t)bal;
-      easy_bits[(c0 >> 5) + 2 * wave + 1] = (uint32_t)(bal >> 32);
+      const int c = (b0 + 64 * wave) >> 5;  // even
+      const uint32_t bits = ((uint32_t)bal == 0xFFFFFFFFu ? 1u : 0u) | ((uint32_t)(bal >> 32) == 0xFFFFFFFFu ? 2u : 0u);
+      if (bits) atomicOr(&easy_bits[c >> 5], bits << (c & 31));
     }
   }
   __syncthreads();
+  // ---- 32-key chunks, loaded global -> LDS (gfx950): lane l of a wave
+  // writes the 16 bytes at the wave's LDS base + 16 l, so piece e of the
+  // buffer (K pieces, then V pieces, row by row) is loaded by the thread
+  // NT u + e and holds the global piece that the row's swizzle maps there.
+  // Keys past the list's end repeat its last entry (masked).
+  // The list reads that give the addresses come first, the loads after: an
+  // LDS read issued behind a load into LDS waits for it unless the compiler
+  // can tell the two apart, which it cannot for the (dynamic) lists.
+  auto issue_chunk = [&](int c, uint16_t* buf) {
+    const uint16_t* src[PPT];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + NT * u;
+      const bool isv = e >= PIECES / 2;
+      const int pe = isv ? e - PIECES / 2 : e;
+      const int row = pe / (D / 8), slot = pe - row * (D / 8);
+      const int pos = lpos[min(32 * c + row, nkc - 1)];
+      const int piece = slot ^ (isv ? vtile_swizzle<D>(row) : ktile_swizzle<D>(row));
+      src[u] = (isv ? vseg : kseg) + (size_t)pos * D + 8 * piece;
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + NT * u;
+      if (PIECES % NT == 0 || e < PIECES) {
+        const int wbase = __builtin_amdgcn_readfirstlane(8 * (tid - lane + NT * u));  // halves, wave-uniform
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src[u],
+                                         (__attribute__((address_space(3))) void*)(buf + wbase), 16, 0, 0);
+      }
+    }
+  };
+  // the first chunk's loads go out now, ahead of the queries' loads below
+  if (nchunks > 0) issue_chunk(0, cbuf0);
 
   // ---- row blocks of this wave: head rb_head(rb), query block rb_qblk(rb). The
   // MFMA computes S^T = K Q^T with the chunk's K rows in a permuted order, so
@@ -644,36 +673,6 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
   const int vsw = vtile_swizzle<D>(vrow);
   const int voff = 32 * D + vrow * D + 4 * (lj & 1);  // halves into a chunk buffer
 
-  // ---- 32-key chunks, loaded global -> LDS (gfx950): lane l of a wave
-  // writes the 16 bytes at the wave's LDS base + 16 l, so piece e of the
-  // buffer (K pieces, then V pieces, row by row) is loaded by the thread
-  // NT u + e and holds the global piece that the row's swizzle maps there.
-  // Keys past the list's end repeat its last entry (masked).
-  // The list reads that give the addresses come first, the loads after: an
-  // LDS read issued behind a load into LDS waits for it unless the compiler
-  // can tell the two apart, which it cannot for the (dynamic) lists.
-  auto issue_chunk = [&](int c, uint16_t* buf) {
-    const uint16_t* src[PPT];
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + NT * u;
-      const bool isv = e >= PIECES / 2;
-      const int pe = isv ? e - PIECES / 2 : e;
-      const int row = pe / (D / 8), slot = pe - row * (D / 8);
-      const int pos = lpos[min(32 * c + row, nkc - 1)];
-      const int piece = slot ^ (isv ? vtile_swizzle<D>(row) : ktile_swizzle<D>(row));
-      src[u] = (isv ? vseg : kseg) + (size_t)pos * D + 8 * piece;
-    }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int e = tid + NT * u;
-      if (PIECES % NT == 0 || e < PIECES) {
-        const int wbase = __builtin_amdgcn_readfirstlane(8 * (tid - lane + NT * u));  // halves, wave-uniform
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src[u],
-                                         (__attribute__((address_space(3))) void*)(buf + wbase), 16, 0, 0);
-      }
-    }
-  };
   // one chunk: wait for this wave's loads of it, barrier (every wave's loads
   // landed; every wave is done with the other buffer), start the next
   // chunk's loads into the other buffer, compute this one
@@ -770,7 +769,6 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       }
     }
   };
-  if (nchunks > 0) issue_chunk(0, cbuf0);
   for (int c = 0; c < nchunks; c += 2) {
     step(c, cbuf0, cbuf1);
     if (c + 1 < nchunks) step(c + 1, cbuf1, cbuf0);
