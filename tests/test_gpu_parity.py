@@ -69,6 +69,18 @@ def test_group_sizes_2_and_8():
                protect_last=8, fp16_window=20), 12, seed=hq + d)
 
 
+def test_hbm_staged_group_sizes_and_fp16_storage():
+    # The HBM-staged instances of the other compiled group sizes (their chunk
+    # rows depend on G) and of FP16-only storage: a 5000-row prefill evicted
+    # to the budget on the first step, then steady steps at a budget above
+    # what LDS staging holds, so every step is HBM-staged.
+    for hq, hkv, d in ((16, 8, 128), (10, 2, 128), (16, 2, 64)):  # G = 2, 5, 8
+        run(wl("toy", num_q_heads=hq, num_kv_heads=hkv, head_dim=d, prefill=5000, n_low=4400, n_high=4600,
+               protect_last=16, fp16_window=32), 4, seed=hq + d + 1)
+    run(wl("toy", prefill=5000, n_low=4400, n_high=4600, protect_last=16, fp16_window=32, old_int8=False), 4,
+        seed=31)
+
+
 def test_degenerate_cases():
     # window 0 (every row INT8 right after its step), budget below the
     # protected count, sinks, the pseudocode's literal gate, FP16-only storage.
