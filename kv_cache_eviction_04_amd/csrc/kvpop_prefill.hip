@@ -419,17 +419,18 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 // Masked prefill attention: one workgroup per 32 queries of a segment (16
 // when a wave serves two query heads). The key list holds the sinks, the
 // long-range keys that pass the first query's threshold (a superset for the
-// later queries, whose thresholds are no larger), and the contiguous run
-// [q0 - w, q1). Per 32-key chunk the K rows and V rows (row-major, 16-byte
-// pieces swizzled per row) go through LDS once for all the workgroup's
-// queries, loaded straight from global memory into one of two buffers
-// while the other is computed. With 8
-// waves (groups of up to 4 query heads) wave w takes head w % 4 for the 16
-// queries of block w / 4; with 4 waves (larger groups) wave w takes heads w,
-// w+4, ... for 16 queries. Per row block: S^T = K Q^T on MFMA, the predicate
-// per (key, query), online softmax per query in the base-2 domain, and
-// O^T = V^T P^T with the weights rounded once to fp16 (the sums l stay
-// fp32, so the LSE is not affected).
+// later queries, whose thresholds are no larger), found from the earlier
+// positions' ranks or from the rank-sorted keys, whichever reads less, and
+// the contiguous run [q0 - w, q1). Per 32-key chunk the K rows and V rows
+// (row-major, 16-byte pieces swizzled per row) go through LDS once for all
+// the workgroup's queries, loaded straight from global memory into one of
+// two buffers while the other is computed. With 8 waves (groups of up to 4
+// query heads) wave w takes head w % 4 for the 16 queries of block w / 4;
+// with 4 waves (larger groups) wave w takes heads w, w+4, ... for 16
+// queries. Per row block: S^T = K Q^T on MFMA, the predicate per (key,
+// query), online softmax per query in the base-2 domain, and O^T = V^T P^T
+// with the weights rounded once to fp16 (the sums l stay fp32, so the LSE
+// is not affected).
 template <int D, int G, int NT>
 __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_kernel(KvpopPrefillArgs pa) {
   constexpr int KS = D / 32, NCB = D / 16;

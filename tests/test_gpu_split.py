@@ -161,7 +161,8 @@ def test_split_k_attend_lockstep_toy(split):
 
 def test_split_k_attend_lockstep_shapes():
     # GQA 32/8 d 128 with an HBM-sized first step (5000-row prefill) cut into
-    # splits, pyramid layers, G = 5, G = 8, W = 0, FP16-only storage, KVpop
+    # splits, pyramid layers, G = 5, G = 8, G = 2, W = 0, FP16-only storage,
+    # KVpop
     ls = lockstep_split(wl("llama3_8b_32k", num_layers=2, batch=2, prefill=5000), 4, 0, seed=30)
     assert max(ls.splits_used) >= 2
     lockstep_split(wl("gpt2_small", num_layers=3, prefill=400, n_low=64, n_high=128, protect_last=16,
@@ -169,6 +170,8 @@ def test_split_k_attend_lockstep_shapes():
     lockstep_split(wl("qwen32b", num_layers=2, batch=2, prefill=300), 6, 5, seed=32)
     lockstep_split(wl("toy", num_q_heads=16, num_kv_heads=2, head_dim=128, prefill=200, n_low=40, n_high=90,
                       protect_last=8, fp16_window=20), 8, 4, seed=33)
+    lockstep_split(wl("toy", num_q_heads=16, num_kv_heads=8, head_dim=64, prefill=200, n_low=40, n_high=90,
+                      protect_last=8, fp16_window=20), 8, 3, seed=37)
     lockstep_split(wl("toy", fp16_window=0, prefill=70), 10, 3, seed=34)
     lockstep_split(wl("toy", old_int8=False, prefill=100), 10, 2, seed=35)
     lockstep_split(wl("kvpop_qwen3_8b", num_layers=2, batch=2, protect_last=32, fp16_window=32, kvpop_k=60),
