@@ -365,13 +365,22 @@ __device__ __forceinline__ void row_swap(float& a, float& b, int half) {
   else
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+// The maximum is taken in the same asm block as the swaps: written as
+// fmaxf on the swaps' results, each operand would first be canonicalised
+// (the compiler cannot see that a swap only moves values), two VALU
+// instructions more per step. The operands are scores or -inf, never NaN.
 __device__ __forceinline__ float rows_max(float x) {
-  float a = x, b = x;
-  row_swap(a, b, 0);
-  a = fmaxf(a, b);
-  b = a;
-  row_swap(a, b, 1);
-  return fmaxf(a, b);
+  float a = x, b;
+  asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+      : "+v"(a), "=&v"(b));
+  return a;
+}
+// max(a, b) of two non-NaN values without the canonicalising moves
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 __device__ __forceinline__ float rows_sum(float x) {
   float a = x, b = x;
@@ -739,7 +748,7 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
         }
       }
       mt = rows_max(mt) * sl2;
-      const float mn = fmaxf(m[rb], mt);
+      const float mn = max_raw(m[rb], mt);
       const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
       const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
       float ls = 0.0f;
