@@ -916,17 +916,30 @@ __global__ void __launch_bounds__(kThreads, 2) kvpop_target_kernel(KvpopPrefillA
       for (int kk = 0; kk < KS; ++kk) qb[kk] = as_h8(*reinterpret_cast<const uint4*>(&qs[buf][pr][lj][8 * (lq + 4 * kk)]));
       // exp(s*scale - lse) = 2^(c*scale*log2(e) - lse*log2(e)): one FMA and one exp2
       const float nl2 = -ls[buf][pr][lj] * kLog2e;
-      // every query of this tile counts for every key of this wave
-      const bool full = d0 >= t0 + 16 * kTgtTiles - 1 + w && d0 + 15 < S;
-#pragma unroll
-      for (int kb = 0; kb < kTgtTiles; ++kb) {
+      auto qk = [&](int kb) {
         floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) c = mfma16(ka[kb][kk], qb[kk], c);
-        if (full) {
+        return c;
+      };
+      // every query of this tile counts for every key of this wave (a branch
+      // uniform over the wave)
+      if (d0 >= t0 + 16 * kTgtTiles - 1 + w && d0 + 15 < S) {
+        // the products of key tile kb + 1 are issued before the
+        // exponentials of tile kb, so the matrix unit works while they run
+        floatx4 c = qk(0);
+#pragma unroll
+        for (int kb = 0; kb < kTgtTiles; ++kb) {
+          floatx4 cn = c;
+          if (kb + 1 < kTgtTiles) cn = qk(kb + 1);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[kb][r] += __builtin_amdgcn_exp2f(fmaf(c[r], sl2, nl2));
-        } else {
+          c = cn;
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < kTgtTiles; ++kb) {
+          const floatx4 c = qk(kb);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = t0 + 16 * kb + 4 * lq + r;
