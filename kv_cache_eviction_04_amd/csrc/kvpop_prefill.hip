@@ -732,10 +732,11 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       float sc[8];
       float mt = -INFINITY;
       if (chunk_easy) {
-        const bool rows_in = q0 + 16 * (rb_qblk(rb) + 1) <= q1;  // every query of the block exists
+        // No mask: a query row past the tile's end has zero Q, so finite
+        // scores of its own, and its output and LSE are never stored.
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          sc[e] = rows_in || qr < q1 ? acc[e >> 2][e & 3] : -INFINITY;
+          sc[e] = acc[e >> 2][e & 3];
           mt = fmaxf(mt, sc[e]);
         }
       } else {
