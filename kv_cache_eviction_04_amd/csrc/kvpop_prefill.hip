@@ -3,6 +3,8 @@
 // scorer's future-attention training target.
 //
 // Source: "Resumen Técnico: KVpop" (gist.science) §2.1, §2.2, §2.4.
+#include <float.h>
+
 #include "device.h"
 
 namespace confkv {
@@ -750,14 +752,16 @@ __global__ void __launch_bounds__(NT, NT == 512 ? 4 : 3) kvpop_prefill_attend_ke
       }
       mt = rows_max(mt) * sl2;
       const float mn = max_raw(m[rb], mt);
-      const float ms = mn == -INFINITY ? 0.0f : mn;  // all masked so far: exp2(-inf - 0) = 0
+      // all masked so far (mn = -inf): every score of the row is -inf too, and
+      // a finite reference gives exp2(-inf) = 0 for the weights and alpha
+      const float ms = max_raw(mn, -FLT_MAX);
       const float alpha = __builtin_amdgcn_exp2f(m[rb] - ms);
       float ls = 0.0f;
       half8 ph;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -ms));
-        ls += pe;
+        ls = e == 0 ? pe : ls + pe;
         ph[e] = (_Float16)pe;
       }
       ls = rows_sum(ls);
