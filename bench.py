@@ -278,6 +278,70 @@ def kv_footprint(gpu, w):
     return {"bytes": total, "gb": total / 1e9, "rows": rows, "position": gpu.position}
 
 
+def kvpop_prefill_leg(gpu, w, S, seed, dev):
+    """KVpop masked prefill at sequence length S on the cache `gpu` (a KVpop
+    configuration), then its future-attention target pass, five timed calls
+    each. Algorithmic FLOPs count 4*d per allowed (query head, key) pair for
+    the prefill (QK and PV multiply-adds) and 2*d per counted pair for the
+    target."""
+    import torch
+
+    from kv_cache_eviction_04_amd import confkv
+
+    B, Hq, H, d = w["batch"], w["num_q_heads"], w["num_kv_heads"], w["head_dim"]
+    gq = torch.Generator(device=dev).manual_seed(seed + 1)
+    pq = torch.randn((B, Hq, S, d), generator=gq, device=dev).half()
+    pk_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
+    pv_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
+    pp = torch.rand((B, H, S), generator=gq, device=dev)
+    pout = torch.empty_like(pq)
+    s_, wnd, kk = w["num_sink"], w["protect_last"], w["kvpop_k"]
+    pairs = 0
+    for qq in range(S):
+        pairs += min(s_, qq + 1) + max(0, qq - max(s_, qq - wnd) + 1) + min(kk, max(0, qq - wnd - s_))
+    flops = 4.0 * d * pairs * B * Hq
+    _, _, ws = gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record()
+    for _ in range(n):
+        gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    if gpu.status() != confkv.OK:
+        log("device status after the prefill is not OK")
+        sys.exit(1)
+    prefill = {"seq_len": S, "batch": B, "ms_per_layer": ms, "allowed_pairs_per_head": pairs,
+               "tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
+               "frac": flops / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
+    log(f"kvpop prefill S={S} B={B}: {ms:.3f} ms per layer, {prefill['tflops']:.0f} TFLOP/s "
+        f"({100 * prefill['frac']:.1f}% of fp16 MFMA peak)")
+    # the transposed pass: 2*d FLOPs per counted (query head, key) pair
+    plse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, lse=plse, workspace=ws)
+    tgt = gpu.kvpop_future_target(pq, pk_, plse)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        gpu.kvpop_future_target(pq, pk_, plse, out=tgt)
+    e1.record()
+    torch.cuda.synchronize()
+    tms = e0.elapsed_time(e1) / n
+    tpairs = sum(max(0, S - t - wnd) for t in range(S))
+    tflops = 2.0 * d * tpairs * B * Hq
+    prefill["future_target"] = {"ms_per_layer": tms, "counted_pairs_per_head": tpairs,
+                                "tflops": tflops / (tms * 1e-3) / 1e12,
+                                "frac": tflops / (tms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
+    log(f"kvpop future target S={S} B={B}: {tms:.3f} ms per layer, "
+        f"{prefill['future_target']['tflops']:.0f} TFLOP/s")
+    del plse, tgt
+    del pq, pk_, pv_, pp, pout, ws
+    torch.cuda.empty_cache()
+    return prefill
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,7 +352,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-len", type=int, default=16384,
-                    help="KVpop workloads: sequence length of the masked-prefill measurement (0 skips it)")
+                    help="sequence length of the KVpop masked-prefill measurement (0 skips it)")
+    ap.add_argument("--no-kvpop-leg", action="store_true",
+                    help="other workloads: skip the KVpop prefill measurement on a cache of the KVpop shape")
     ap.add_argument("--split-steps", type=int, default=50,
                     help="steps of the per-layer call sequence (attend per layer, then evict) timed after the "
                          "fused steps; 0 skips it")
@@ -552,61 +618,21 @@ def main():
             f"({sampling['logits_bytes'] / 1e6:.1f} MB of logits)")
 
     # KVpop prefill with the multi-query mask at the pages' 16384-token
-    # training length, one layer per call: algorithmic FLOPs count 4*d per
-    # allowed (query head, key) pair (QK and PV multiply-adds).
+    # training length, one layer per call. A KVpop workload measures it on its
+    # own cache; any other workload on a cache of the KVpop Qwen3-8B shape made
+    # for it (its state is a few GB), so the default run reports it too.
     prefill = None
-    if w["policy"] == "kvpop" and args.prefill_len > 0:
-        S = args.prefill_len
-        gq = torch.Generator(device=dev).manual_seed(args.seed + 1)
-        pq = torch.randn((B, Hq, S, d), generator=gq, device=dev).half()
-        pk_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
-        pv_ = torch.randn((B, H, S, d), generator=gq, device=dev).half()
-        pp = torch.rand((B, H, S), generator=gq, device=dev)
-        pout = torch.empty_like(pq)
-        s_, wnd, kk = w["num_sink"], w["protect_last"], w["kvpop_k"]
-        pairs = 0
-        for qq in range(S):
-            pairs += min(s_, qq + 1) + max(0, qq - max(s_, qq - wnd) + 1) + min(kk, max(0, qq - wnd - s_))
-        flops = 4.0 * d * pairs * B * Hq
-        _, _, ws = gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 5
-        e0.record()
-        for _ in range(n):
-            gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
-        if gpu.status() != confkv.OK:
-            log("device status after the prefill is not OK")
-            sys.exit(1)
-        prefill = {"seq_len": S, "batch": B, "ms_per_layer": ms, "allowed_pairs_per_head": pairs,
-                   "tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
-                   "frac": flops / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
-        log(f"kvpop prefill S={S} B={B}: {ms:.3f} ms per layer, {prefill['tflops']:.0f} TFLOP/s "
-            f"({100 * prefill['frac']:.1f}% of fp16 MFMA peak)")
-        # the transposed pass: 2*d FLOPs per counted (query head, key) pair
-        plse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-        gpu.kvpop_prefill(pq, pk_, pv_, pp, out=pout, lse=plse, workspace=ws)
-        tgt = gpu.kvpop_future_target(pq, pk_, plse)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(n):
-            gpu.kvpop_future_target(pq, pk_, plse, out=tgt)
-        e1.record()
-        torch.cuda.synchronize()
-        tms = e0.elapsed_time(e1) / n
-        tpairs = sum(max(0, S - t - wnd) for t in range(S))
-        tflops = 2.0 * d * tpairs * B * Hq
-        prefill["future_target"] = {"ms_per_layer": tms, "counted_pairs_per_head": tpairs,
-                                    "tflops": tflops / (tms * 1e-3) / 1e12,
-                                    "frac": tflops / (tms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS}
-        log(f"kvpop future target S={S} B={B}: {tms:.3f} ms per layer, "
-            f"{prefill['future_target']['tflops']:.0f} TFLOP/s")
-        del plse, tgt
-        del pq, pk_, pv_, pp, pout, ws
-        torch.cuda.empty_cache()
+    if args.prefill_len > 0 and (w["policy"] == "kvpop" or not args.no_kvpop_leg):
+        if w["policy"] == "kvpop":
+            prefill = kvpop_prefill_leg(gpu, w, args.prefill_len, args.seed, dev)
+        else:
+            kw = synth.workload("kvpop_qwen3_8b")
+            kpk, kpv = synth.prefill(kw, args.seed, dev)
+            kgpu = confkv.Cache(kw, kpk, kpv, device=dev)
+            prefill = kvpop_prefill_leg(kgpu, kw, args.prefill_len, args.seed, dev)
+            prefill["workload"] = "kvpop_qwen3_8b"
+            del kgpu, kpk, kpv
+            torch.cuda.empty_cache()
 
     if args.run_to > 0:
         target = w["prefill"] + args.run_to
