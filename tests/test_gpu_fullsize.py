@@ -100,3 +100,40 @@ def test_llama3_8b_32k_full_size_per_layer_calls():
     worst = drive(ls, 6, {0, 1, 5})
     assert max(ls.splits_used) >= 2
     log(f"llama3_8b_32k per-layer calls: splits used {sorted(ls.splits_used)}, worst out err {worst:.2e}")
+
+
+def test_kvpop_qwen3_8b_whole_stream_closed_form():
+    """The KVpop stream at its stated length (131072 decode steps), on the GPU
+    alone: at checkpoints along the stream the kept set of each sampled
+    segment equals the history-free closed form, which static priorities make
+    exact ("Resumen Técnico: KVpop" §2.3 and §2.4). The priorities the step
+    consumes are gathered on the device as the stream runs."""
+    w = synth.workload("kvpop_qwen3_8b")
+    L, B, Hq, H, d = w["num_layers"], w["batch"], w["num_q_heads"], w["num_kv_heads"], w["head_dim"]
+    s_, wnd, k = w["num_sink"], w["protect_last"], w["kvpop_k"]
+    picks = [(0, 0, 0), (L // 2, 3, 4), (L - 1, B - 1, H - 1)]
+    seed = 7
+    total = w["steps"]
+    checks = {s_ + wnd + k + 1000, total // 4 - 1, total // 2 - 1, total - 1}
+    gpu = confkv.Cache(w, None, None)
+    li = torch.tensor([p[0] for p in picks], device=DEV)
+    bi = torch.tensor([p[1] for p in picks], device=DEV)
+    hi = torch.tensor([p[2] for p in picks], device=DEV)
+    pbuf = torch.empty((total, len(picks)), dtype=torch.float32, device=DEV)
+    out = torch.empty((L, B, Hq, d), dtype=torch.float16, device=DEV)
+    for step in range(total):
+        x = synth.step_inputs(w, seed, step, DEV)
+        gpu.step(None, x["q"], x["k"], x["v"], x["prio"], out=out)
+        pbuf[step] = x["prio"][li, bi, hi]
+        if step in checks:
+            t = gpu.position - 1
+            # the priority of position p arrives with the inputs of step p + w
+            pr = pbuf[: t + 1].cpu().numpy()
+            for j, (l, b, h) in enumerate(picks):
+                seg = (l * B + b) * H + h
+                want = KP.kept_closed_form(t, lambda p: pr[p + wnd, j], s_, wnd, k)
+                ro = gpu.read_cache(seg, 1)
+                n = int(ro["len"][0])
+                assert ro["pos"][0, :n].tolist() == want, f"t {t} segment {seg}"
+            log(f"kvpop whole stream: closed form holds at t {t} for {len(picks)} segments")
+    assert gpu.status() == confkv.OK
