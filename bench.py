@@ -653,7 +653,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gpu, args.seed, step_i, args.cpu_seconds)
-        log(f"cpu oracle: {cpu['value']:.4g} steps/s ({cpu['seconds']:.1f}s of CPU work)")
+        log(f"cpu oracle: {cpu['value']:.4g} steps/s ({cpu['seconds']:.1f} s wall on {cpu['cores']} processes, "
+            f"about {cpu['seconds'] * cpu['cores']:.0f} s of CPU work)")
 
     res = {
         "metric": METRIC,
